@@ -1,0 +1,251 @@
+"""Plain, slow, obviously correct fp64 CPU oracle of the GEMM-epilogue hot path.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py``; never by the product path. It shares no code,
+header, table or constant generator with the HIP library.
+
+Sources (the paper is "CODA: Rewriting Transformer Blocks as GEMM-Epilogue Programs",
+arXiv 2605.19269; two web pages about it are used):
+  [notes]  papernotes.org notes page, section "方法详解" (method), "关键设计" 1-4
+           (key designs 1-4) and their displayed equations;
+  [pith]   pith.science page: Figure 4 and Figure 5 captions (two-level reduction and
+           the formula for r), Figure 7 caption (pairwise activations), and the
+           fragments of Appendix A.1 / Listing 2 (the epilogue visitor list
+           EVTResidual, EVTColBlockReductionStore, EVTRowVecMulPostAct).
+
+Conventions
+  * Every input is taken as bf16 bit patterns (``uint16``) and decoded *exactly* to
+    fp64 by :func:`decode_bf16`. fp32 inputs (RoPE tables are never used here) stay
+    fp32 -> fp64. Nothing is rounded afterwards: all arithmetic is fp64.
+  * Every operation on the path is independent across rows (tokens), so every
+    function takes an optional ``rows`` index array and then computes exactly those
+    rows of the full result (row sampling for large workloads).
+  * Matrix products use ``numpy.matmul`` in float64, a library primitive; nothing is
+    blocked, fused or reordered beyond the definitions below.
+
+Readings where the pages are silent, garbled or inconsistent (each is also listed in
+the design notes of the repository):
+  R1  eps sits inside the square root: r = 1 / sqrt(mean(h1^2) + eps) ([pith] Fig. 5
+      caption prints the formula with the radical sign lost; the standard RMSNorm).
+  R2  The tile partial is a *sum* of squares over a 256-column tile; the reduction
+      divides by the full width d. (The listing stores a block mean with
+      inv_block_size = 1/tile_N; both agree when the tile divides d, and the sum is
+      right for a ragged last tile.)
+  R3  The square is taken of h1 = x W0 + z before gamma and before any rounding
+      ([notes] key design 1: r = 1/rms(x W0 + z); Listing 2: the partial is taken on
+      the unscaled D, the main output D stays unscaled).
+  R4  GEMM2 consumes h2 = h1 * gamma (not normalised) and r multiplies its
+      accumulator: y[i, j] = r[i] * h3[i, j], h3 = h2 W1 ([notes] key design 1).
+  R5  RoPE: theta_p = theta^(-2p/head_dim) for the pair p of adjacent columns
+      (2p, 2p+1) inside a head; the pair is rotated by [[cos a, -sin a],
+      [sin a, cos a]] with a = pos * theta_p, pos = (row + pos_offset) mod seq_len;
+      the output is [Q | K | V] in contiguous blocks, V unrotated.
+  R6  SwiGLU: even accumulator column = gate G, odd = up U, out = silu(G) * U with
+      silu(g) = g / (1 + exp(-g)); the output width is half the accumulator width.
+  R7  Backward statistic: h2 is the GEMM2 input and y = h2 W1 ([notes] key design 3);
+      s = (1/d) sum_cols(dY W1^T * h2), also computed as (1/d) sum(dY * y).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "PARTIAL_TILE_N",
+    "decode_bf16",
+    "matmul",
+    "tile_row_sums",
+    "rowstat_reduce",
+    "gemm_rmsnorm_fwd",
+    "rmsnorm_rows",
+    "rope_rotate",
+    "gemm_rope",
+    "silu",
+    "gemm_swiglu",
+    "gemm_rmsnorm_bwd_stats",
+    "flops_gemm_rmsnorm_fwd",
+]
+
+# Width of one column tile of the partial-statistic workspace [M, nb]: tile t covers
+# columns [t*256, (t+1)*256) (the last tile may be ragged). This is the layout
+# contract of the workspace, stated by the library's interface documentation.
+PARTIAL_TILE_N = 256
+
+
+def decode_bf16(bits) -> np.ndarray:
+    """bf16 bit patterns -> exact fp64 values.
+
+    bf16 is the upper half of an IEEE-754 binary32: placing the 16 bits in the high
+    half of a 32-bit word gives the fp32 number exactly, which widens exactly to fp64.
+    """
+    b = np.asarray(bits)
+    if b.dtype != np.uint16:
+        raise TypeError("decode_bf16 expects uint16 bit patterns")
+    u32 = b.astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def _as_f64(a) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return decode_bf16(a)
+    return a.astype(np.float64)
+
+
+def _take_rows(a: np.ndarray, rows):
+    return a if rows is None else a[np.asarray(rows)]
+
+
+def matmul(a, b) -> np.ndarray:
+    """fp64 matrix product a @ b (a: [M, K], b: [K, N])."""
+    a = _as_f64(a)
+    b = _as_f64(b)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError(f"matmul shape mismatch {a.shape} @ {b.shape}")
+    return np.matmul(a, b)
+
+
+def tile_row_sums(v: np.ndarray, tile_n: int = PARTIAL_TILE_N) -> np.ndarray:
+    """Per-row sums of ``v`` over consecutive column tiles of width ``tile_n``.
+
+    Returns P[m, t] = sum_{n in [t*tile_n, (t+1)*tile_n) and n < width} v[m, n]
+    ([pith] Listing 2, EVTColBlockReductionStore: one value per row and N-block;
+    reading R2: sums, not means).
+    """
+    M, W = v.shape
+    nb = -(-W // tile_n) if W else 0
+    P = np.zeros((M, nb), dtype=np.float64)
+    for t in range(nb):
+        P[:, t] = v[:, t * tile_n:min((t + 1) * tile_n, W)].sum(axis=1)
+    return P
+
+
+def rowstat_reduce(partials, d: int, eps: float = 0.0, mode: str = "rsqrt_mean_eps") -> np.ndarray:
+    """The auxiliary row reduction over tile partials ([pith] Fig. 4 and Fig. 5).
+
+    mode "rsqrt_mean_eps": r[m] = 1 / sqrt(sum_t P[m, t] / d + eps)   (forward r)
+    mode "mean":           s[m] = sum_t P[m, t] / d                   (backward s)
+    """
+    P = _as_f64(partials)
+    total = P.sum(axis=1)
+    if mode == "rsqrt_mean_eps":
+        return 1.0 / np.sqrt(total / d + eps)
+    if mode == "mean":
+        return total / d
+    raise ValueError(mode)
+
+
+def rmsnorm_rows(h: np.ndarray, gamma: np.ndarray, eps: float):
+    """Textbook RMSNorm of each row: returns (r, r * h * gamma) with
+    r = 1 / sqrt(mean(h^2) + eps) (reading R1)."""
+    ms = np.mean(h * h, axis=1)
+    r = 1.0 / np.sqrt(ms + eps)
+    return r, (r[:, None] * h) * gamma[None, :]
+
+
+def gemm_rmsnorm_fwd(x, w0, z, gamma, w1, eps: float, rows=None,
+                     tile_n: int = PARTIAL_TILE_N) -> dict:
+    """y = RMSNorm(x W0 + z, gamma) W1, unfused, plus the rewrite's intermediates.
+
+    Follows [notes] key design 1 (both displayed equations) and [pith] Fig. 4:
+      h0 = x W0;  h1 = h0 + z;  r = 1/rms(h1);  y = (r h1 * gamma) W1     (direct)
+      h2 = h1 * gamma;  h3 = h2 W1;  y_deferred[i, j] = r[i] h3[i, j]      (deferred r)
+      partials = per-tile row sums of h1^2                                 (two-level r)
+    Returns fp64 arrays h1, h2, partials, r, y, y_deferred for the selected rows.
+    """
+    xr = _take_rows(_as_f64(x), rows)
+    zr = _take_rows(_as_f64(z), rows)
+    W0 = _as_f64(w0)
+    W1 = _as_f64(w1)
+    g = _as_f64(gamma)
+    h0 = matmul(xr, W0)
+    h1 = h0 + zr
+    r, normed = rmsnorm_rows(h1, g, eps)
+    y = matmul(normed, W1)
+    h2 = h1 * g[None, :]
+    h3 = matmul(h2, W1)
+    y_def = r[:, None] * h3
+    partials = tile_row_sums(h1 * h1, tile_n)
+    return dict(h1=h1, h2=h2, partials=partials, r=r, y=y, y_deferred=y_def)
+
+
+def rope_rotate(h: np.ndarray, positions: np.ndarray, n_q: int, n_k: int, n_v: int,
+                head_dim: int, theta: float) -> np.ndarray:
+    """Rotary position embedding of the Q and K blocks of h = [Q | K | V] (reading R5).
+
+    Each head's adjacent columns (2p, 2p+1) form one 2-D vector that is rotated by the
+    angle pos * theta^(-2p/head_dim) ([notes] key design 2; [pith] Fig. 7: RoPE
+    rotates each feature pair and returns two outputs). V is returned unchanged.
+    """
+    assert h.shape[1] == n_q + n_k + n_v
+    assert head_dim % 2 == 0 and n_q % head_dim == 0 and n_k % head_dim == 0
+    out = h.copy()
+    half = head_dim // 2
+    p = np.arange(half, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * p / head_dim)              # [half]
+    ang = positions.astype(np.float64)[:, None] * inv_freq[None, :]   # [rows, half]
+    c, s = np.cos(ang), np.sin(ang)
+    for base, width in ((0, n_q), (n_q, n_k)):
+        for h0 in range(base, base + width, head_dim):
+            e = h[:, h0:h0 + head_dim:2]
+            o = h[:, h0 + 1:h0 + head_dim:2]
+            out[:, h0:h0 + head_dim:2] = e * c - o * s
+            out[:, h0 + 1:h0 + head_dim:2] = e * s + o * c
+    return out
+
+
+def gemm_rope(x, w, n_q: int, n_k: int, n_v: int, head_dim: int, seq_len: int,
+              pos_offset: int = 0, theta: float = 10000.0, rows=None) -> np.ndarray:
+    """QKV projection followed by RoPE on Q and K: out = rope(x W).
+
+    The position of row i is (i + pos_offset) mod seq_len. The angles come from fp64
+    trigonometry directly, not from any precomputed table.
+    """
+    M = np.asarray(x).shape[0]
+    idx = np.arange(M) if rows is None else np.asarray(rows)
+    h = matmul(_take_rows(_as_f64(x), rows), w)
+    pos = (idx + pos_offset) % seq_len
+    return rope_rotate(h, pos, n_q, n_k, n_v, head_dim, theta)
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """silu(g) = g / (1 + exp(-g)) in fp64 (exp overflow for g << 0 gives -0)."""
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def gemm_swiglu(x, w, rows=None) -> np.ndarray:
+    """h = x W with interleaved columns; out[m, j] = silu(h[m, 2j]) * h[m, 2j+1]
+    ([notes] key design 2: even channel G, odd channel U, width halved; reading R6)."""
+    h = matmul(_take_rows(_as_f64(x), rows), w)
+    if h.shape[1] % 2:
+        raise ValueError("SwiGLU needs an even accumulator width")
+    G = h[:, 0::2]
+    U = h[:, 1::2]
+    return silu(G) * U
+
+
+def gemm_rmsnorm_bwd_stats(dy, w1, h2, rows=None, tile_n: int = PARTIAL_TILE_N) -> dict:
+    """Grad GEMM dH2 = dY W1^T and the RMSNorm-backward row statistic s.
+
+    [notes] key design 3: with grad_h2 = dY W1^T and y = h2 W1,
+        s = (1/d) sum_cols(grad_h2 * h2) = (1/d) diag(dY (h2 W1)^T) = (1/d) sum(dY * y).
+    Returns dh2, partials (per-tile row sums of dH2 * h2), s (first form) and
+    s_prime (last form), for the selected rows; d is the width of h2.
+    """
+    dyr = _take_rows(_as_f64(dy), rows)
+    h2r = _take_rows(_as_f64(h2), rows)
+    W1 = _as_f64(w1)
+    d = h2r.shape[1]
+    dh2 = matmul(dyr, W1.T)
+    prod = dh2 * h2r
+    s = prod.sum(axis=1) / d
+    y = matmul(h2r, W1)
+    s_prime = (dyr * y).sum(axis=1) / d
+    s_diag = np.diag(matmul(dyr, y.T)) / d if dyr.shape[0] <= 512 else None
+    return dict(dh2=dh2, partials=tile_row_sums(prod, tile_n), s=s, s_prime=s_prime,
+                s_diag=s_diag)
+
+
+def flops_gemm_rmsnorm_fwd(M: int, K: int, D: int, N1: int) -> int:
+    """Algorithmic flops of the forward rewrite: the two GEMMs (2MKD + 2MDN1)."""
+    return 2 * M * K * D + 2 * M * D * N1
