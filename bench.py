@@ -1,0 +1,346 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused GEMM-epilogue hot path on one MI355X.
+
+A step is one forward GEMM-RMSNorm-GEMM (GEMM1 with the residual / gamma / row-partial
+epilogue, the auxiliary row reduction, GEMM2 with the deferred row scale) on the
+Llama-3-8B-shaped workload: M = 8192 tokens, x[8192, 14336] W0[14336, 4096] (FFN
+down-projection), residual z[8192, 4096], W1[4096, 6144] (GQA QKV), eps = 1e-5, bf16
+inputs with fp32 accumulation, synthetic seeded data already resident in HBM.
+
+Prints ONE JSON line. `value` is the algorithmic TFLOP/s of the step (2MKD + 2MDN1 per
+step) over the synchronize-bracketed wall time of `--steps` steps. Per-kernel durations
+come from HIP events recorded on the stream the kernels run on. The other fused paths
+(GEMM+RoPE, GEMM+SwiGLU, the backward statistic) and the unfused baselines are timed
+after the headline and reported under "paths" (context, not the headline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused GEMM-epilogue TFLOP/s (% bf16 MFMA peak), 8192-class GEMM-RMSNorm-GEMM"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm1_residual_rmsnorm_llama8k.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources; stored HBM-traffic counters are used only while it matches."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "transformer_gemm_epilogue_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def to_dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def event_ms(pairs):
+    return [a.elapsed_time(b) for a, b in pairs]
+
+
+def time_reps(fn, reps, warmup=3):
+    """Median / mean / min milliseconds of fn() over reps, from HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array(event_ms(evs))
+    return dict(median_ms=float(np.median(t)), mean_ms=float(t.mean()), min_ms=float(t.min()))
+
+
+# --------------------------------------------------------------------------- headline
+def headline(args, coda, torch):
+    import workloads as W
+    wl = W.llama_fwd()
+    M, K, D, N1, eps = wl["M"], wl["K"], wl["D"], wl["N1"], wl["eps"]
+    x, w0, z, g, w1 = (to_dev(wl[k]) for k in ("x", "w0", "z", "gamma", "w1"))
+    h1 = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
+    h2 = torch.empty_like(h1)
+    part = torch.empty((M, coda.num_partials(D)), dtype=torch.float32, device="cuda")
+    r = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N1), dtype=torch.bfloat16, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        coda.coda_gemm_residual_rmsnorm_partials(x, w0, z, g, h1=h1, h2=h2, partials=part)
+        if ev is not None:
+            ev[1].record()
+        coda.coda_rowstat_reduce(part, D, eps, coda.ROWSTAT_RSQRT_MEAN_EPS, out=r)
+        if ev is not None:
+            ev[2].record()
+        coda.coda_gemm_rowscale(h2, w1, r, y=y)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    g1 = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    rs = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    g2 = np.array([e[2].elapsed_time(e[3]) for e in evs])
+
+    # the single fused entry point (same three launches), for cross-checking
+    fused = time_reps(lambda: coda.coda_gemm_rmsnorm_fwd(x, w0, z, g, w1, eps, h1=h1, h2=h2, partials=part,
+                                                         r=r, y=y), reps=max(5, args.steps // 2))
+
+    flop1 = 2.0 * M * K * D
+    flop2 = 2.0 * M * D * N1
+    flops = flop1 + flop2
+    ms_step = wall * 1e3 / args.steps
+    value = flops / (ms_step * 1e-3) / 1e12
+    g1_us = float(g1.mean() * 1e3)
+    achieved = flop1 / (g1.mean() * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("source_hash") == source_hash():
+            traffic = rec.get("hbm_bytes_per_launch")
+    nb = coda.num_partials(D)
+    aux_bytes = M * nb * 4 + M * 4
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3_8b_gemm_rmsnorm_gemm_fwd", "M": M, "K": K, "D": D, "N1": N1, "eps": eps,
+                   "seed": 3, "tokens_per_step": M, "inputs": "bf16, N(0,1) activations, N(0,1/fan_in) weights",
+                   "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": "gemm_epilogue_kernel<KN, EpiResidualRmsPartials> (GEMM1)",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "algorithmic_flop_per_launch": flop1, "avg_launch_us": round(g1_us, 2)},
+        "kernels_us": {"gemm1_residual_rmsnorm_partials": round(g1_us, 2),
+                       "rowstat_reduce": round(float(rs.mean() * 1e3), 2),
+                       "gemm2_rowscale": round(float(g2.mean() * 1e3), 2),
+                       "fused_entry_point_median": round(fused["median_ms"] * 1e3, 2)},
+        "kernels_tflops": {"gemm1": round(flop1 / (g1.mean() * 1e-3) / 1e12, 1),
+                           "gemm2": round(flop2 / (g2.mean() * 1e-3) / 1e12, 1)},
+        "rowstat_reduce_gbps_at_config": round(aux_bytes / (rs.mean() * 1e-3) / 1e9, 1),
+    }
+    bufs = dict(x=x, w0=w0, z=z, g=g, w1=w1, h1=h1, h2=h2, part=part, r=r, y=y, eps=eps)
+    return res, bufs
+
+
+# ------------------------------------------------------------------- unfused baseline
+def unfused_fwd(coda, torch, b, reps):
+    """Same MFMA main loop with a plain store, then a separate residual+RMSNorm kernel,
+    then the plain GEMM again (bf16 intermediates), and torch (hipBLASLt) + eager ops."""
+    x, w0, z, g, w1, eps = b["x"], b["w0"], b["z"], b["g"], b["w1"], b["eps"]
+    M, D = b["h1"].shape
+    h0 = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
+    h1 = torch.empty_like(h0)
+    o = torch.empty_like(h0)
+    r = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(b["y"])
+
+    def ours():
+        coda.coda_baseline_gemm(x, w0, c=h0)
+        coda.coda_baseline_residual_rmsnorm(h0, z, g, eps, h1=h1, r=r, o=o)
+        coda.coda_baseline_gemm(o, w1, c=y)
+
+    def torch_path():
+        hh = torch.matmul(x, w0) + z
+        oo = torch.nn.functional.rms_norm(hh, (D,), weight=g, eps=eps)
+        return torch.matmul(oo, w1)
+
+    t_ours = time_reps(ours, reps)
+    t_torch = time_reps(torch_path, reps)
+    t_norm = time_reps(lambda: coda.coda_baseline_residual_rmsnorm(h0, z, g, eps, h1=h1, r=r, o=o), reps)
+    t_mm1 = time_reps(lambda: torch.matmul(x, w0), reps)
+    t_mm2 = time_reps(lambda: torch.matmul(o, w1), reps)
+    return dict(same_mainloop_plus_separate_kernels_ms=t_ours["median_ms"],
+                torch_hipblaslt_eager_ms=t_torch["median_ms"],
+                separate_residual_rmsnorm_kernel_us=round(t_norm["median_ms"] * 1e3, 2),
+                separate_residual_rmsnorm_gbps=round(4 * M * D * 2 / (t_norm["median_ms"] * 1e-3) / 1e9, 1),
+                hipblaslt_gemm1_tflops=round(2 * M * x.shape[1] * D / (t_mm1["median_ms"] * 1e-3) / 1e12, 1),
+                hipblaslt_gemm2_tflops=round(2 * M * D * w1.shape[1] / (t_mm2["median_ms"] * 1e-3) / 1e12, 1))
+
+
+# ------------------------------------------------------------------ other fused paths
+def other_paths(coda, torch, reps):
+    import workloads as W
+    out = {}
+    # GEMM + RoPE (QKV projection)
+    wl = W.rope_qkv()
+    x, w = to_dev(wl["x"]), to_dev(wl["w"])
+    c, s = coda.coda_rope_tables(wl["seq_len"], wl["head_dim"], wl["theta"])
+    M, K, N = wl["M"], wl["K"], wl["n_q"] + wl["n_k"] + wl["n_v"]
+    qkv = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    h = torch.empty_like(qkv)
+    args = (wl["n_q"], wl["n_k"], wl["n_v"], wl["head_dim"], wl["seq_len"], 0)
+    tf = time_reps(lambda: coda.coda_gemm_rope(x, w, c, s, *args, out=qkv), reps)
+    tu = time_reps(lambda: (coda.coda_baseline_gemm(x, w, c=h), coda.coda_baseline_rope(h, c, s, *args, out=qkv)),
+                   reps)
+    tb = time_reps(lambda: torch.matmul(x, w), reps)
+    fl = 2.0 * M * K * N
+    out["gemm_rope_qkv_4096x12288x4096"] = dict(
+        fused_us=round(tf["median_ms"] * 1e3, 1), tflops=round(fl / (tf["median_ms"] * 1e-3) / 1e12, 1),
+        unfused_us=round(tu["median_ms"] * 1e3, 1), speedup_vs_unfused=round(tu["median_ms"] / tf["median_ms"], 3),
+        hipblaslt_gemm_only_tflops=round(fl / (tb["median_ms"] * 1e-3) / 1e12, 1))
+    del x, w, qkv, h
+    # GEMM + SwiGLU
+    wl = W.swiglu()
+    x, w = to_dev(wl["x"]), to_dev(wl["w"])
+    M, K, F = wl["M"], wl["K"], wl["F"]
+    o = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    h = torch.empty((M, 2 * F), dtype=torch.bfloat16, device="cuda")
+    tf = time_reps(lambda: coda.coda_gemm_swiglu(x, w, out=o), reps)
+    tu = time_reps(lambda: (coda.coda_baseline_gemm(x, w, c=h), coda.coda_baseline_swiglu(h, out=o)), reps)
+    tb = time_reps(lambda: torch.matmul(x, w), reps)
+    fl = 2.0 * M * K * 2 * F
+    out["gemm_swiglu_8192x8192x8192"] = dict(
+        fused_us=round(tf["median_ms"] * 1e3, 1), tflops=round(fl / (tf["median_ms"] * 1e-3) / 1e12, 1),
+        unfused_us=round(tu["median_ms"] * 1e3, 1), speedup_vs_unfused=round(tu["median_ms"] / tf["median_ms"], 3),
+        hipblaslt_gemm_only_tflops=round(fl / (tb["median_ms"] * 1e-3) / 1e12, 1))
+    del x, w, o, h
+    # backward statistic
+    wl = W.bwd_stats()
+    dy, w1, h2 = to_dev(wl["dy"]), to_dev(wl["w1"]), to_dev(wl["h2"])
+    M, D, N = wl["M"], wl["D"], wl["N"]
+    dh2 = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
+    part = torch.empty((M, coda.num_partials(D)), dtype=torch.float32, device="cuda")
+    sv = torch.empty((M,), dtype=torch.float32, device="cuda")
+    tf = time_reps(lambda: coda.coda_gemm_rmsnorm_bwd_stats(dy, w1, h2, dh2=dh2, partials=part, s=sv), reps)
+    tu = time_reps(lambda: (coda.coda_baseline_gemm(dy, w1, b_kn=False, c=dh2), coda.coda_baseline_rowdot(dh2, h2, s=sv)),
+                   reps)
+    fl = 2.0 * M * N * D
+    out["gemm_rmsnorm_bwd_stats_8192x4096x6144"] = dict(
+        fused_us=round(tf["median_ms"] * 1e3, 1), tflops=round(fl / (tf["median_ms"] * 1e-3) / 1e12, 1),
+        unfused_us=round(tu["median_ms"] * 1e3, 1), speedup_vs_unfused=round(tu["median_ms"] / tf["median_ms"], 3))
+    return out
+
+
+def aux_reduce_sweep(coda, torch, reps):
+    """Bandwidth of the auxiliary row reduction on partial buffers far above the 256 MiB
+    Infinity Cache (at the forward workload the buffer is 0.5 MiB and latency-bound)."""
+    res = {}
+    for mib in (256, 1024):
+        nb = 16
+        M = mib * 1024 * 1024 // (nb * 4)
+        P = torch.rand((M, nb), dtype=torch.float32, device="cuda")
+        o = torch.empty((M,), dtype=torch.float32, device="cuda")
+        t = time_reps(lambda: coda.coda_rowstat_reduce(P, 4096, 1e-5, coda.ROWSTAT_RSQRT_MEAN_EPS, out=o), reps)
+        byts = M * nb * 4 + M * 4
+        res[f"{mib}MiB"] = dict(us=round(t["median_ms"] * 1e3, 1),
+                                gbps=round(byts / (t["median_ms"] * 1e-3) / 1e9, 1),
+                                frac_of_hbm_peak=round(byts / (t["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 3))
+        del P, o
+    return res
+
+
+# --------------------------------------------------------------------- CPU oracle leg
+def cpu_baseline(target_s: float):
+    """The fp64 oracle, as it stands, on a row sample of the same workload (every op is
+    row-independent), timed on this host's cores; scaled to the metric's unit."""
+    import oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    wl = W.llama_fwd()
+    M, K, D, N1 = wl["M"], wl["K"], wl["D"], wl["N1"]
+
+    def run(n):
+        rows = np.arange(n) * (M // n)
+        t0 = time.perf_counter()
+        O.gemm_rmsnorm_fwd(wl["x"], wl["w0"], wl["z"], wl["gamma"], wl["w1"], wl["eps"], rows=rows)
+        return time.perf_counter() - t0
+
+    t = run(16)
+    n = int(min(M, max(16, 16 * target_s / max(t, 1e-3))))
+    t = run(n)
+    flops = 2.0 * n * K * D + 2.0 * n * D * N1
+    return {"value": round(flops / t / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {M} rows of the same workload (all five fp64 outputs per row, incl. "
+                      f"weight decode), {t:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=20, help="repetitions for the context measurements")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the fused GEMM-epilogue path is row-independent and "
+              "shards over tokens with no exchange; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import transformer_gemm_epilogue_amd as coda
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (there is no CPU path)", file=sys.stderr)
+        sys.exit(1)
+    coda.lib()
+    log(f"device: {torch.cuda.get_device_name(0)}")
+    res, bufs = headline(args, coda, torch)
+    log(f"headline: {res['value']} TFLOP/s, {res['ms_per_step']} ms/step")
+    if not args.headline_only:
+        res["unfused_fwd"] = unfused_fwd(coda, torch, bufs, args.reps)
+        res["speedup_vs_unfused_same_mainloop"] = round(
+            res["unfused_fwd"]["same_mainloop_plus_separate_kernels_ms"] / res["ms_per_step"], 3)
+        res["speedup_vs_torch_hipblaslt"] = round(res["unfused_fwd"]["torch_hipblaslt_eager_ms"] / res["ms_per_step"], 3)
+        del bufs
+        torch.cuda.empty_cache()
+        res["paths"] = other_paths(coda, torch, args.reps)
+        torch.cuda.empty_cache()
+        res["aux_reduce_sweep"] = aux_reduce_sweep(coda, torch, args.reps)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

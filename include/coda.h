@@ -1,0 +1,190 @@
+/*
+ * coda.h -- C ABI of libcoda.so: bf16 GEMMs on gfx950 (AMD Instinct MI355X) whose
+ * epilogues finish the Transformer's memory-bound operators while the output tile is
+ * still on chip, after the method of "CODA: Rewriting Transformer Blocks as
+ * GEMM-Epilogue Programs" (arXiv 2605.19269).
+ *
+ * Sources cited below:
+ *   [notes] the papernotes.org notes on CODA: section "方法详解" (method), key designs
+ *           ("关键设计") 1 to 4 and their displayed equations;
+ *   [pith]  the pith.science page on CODA: captions of Figures 4, 5 and 7 and the
+ *           fragments of Appendix A.1 / Listing 2 (epilogue visitors EVTResidual,
+ *           EVTColBlockReductionStore, EVTRowVecMulPostAct).
+ *
+ * Conventions for every entry point
+ *   - bf16 tensors are passed as uint16_t bit patterns; outputs are rounded from fp32
+ *     to bf16 with round-to-nearest-even. fp32 tensors are plain IEEE floats.
+ *   - Every tensor is a dense row-major array in DEVICE memory (hipMalloc'd or a torch
+ *     CUDA tensor's data pointer), and every bf16 pointer must be 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream. All work is
+ *     enqueued on that stream, asynchronously; the call returns before it finishes.
+ *   - Ownership: the caller owns and allocates every buffer, workspaces included. The
+ *     library allocates no device memory, keeps no state between calls and may be
+ *     called from several host threads at once (on different buffers).
+ *   - Errors: argument errors are detected before anything is enqueued and return a
+ *     nonzero status (nothing is written). A failed kernel launch returns
+ *     CODA_ERR_HIP. Faults during execution surface at the caller's next
+ *     synchronisation, as for any asynchronous HIP work.
+ *   - Shapes: M (rows / tokens) may be any value >= 0 (M == 0 is a no-op returning
+ *     CODA_OK). Depth K and every output width must be positive multiples of 8, and
+ *     at most 4194304 (2^22). Any M is handled by row predication; ragged K and widths
+ *     by zero-filled tails.
+ *   - Accumulation is fp32 on the MFMA units; epilogue math is fp32; only stores round.
+ *   - Results are deterministic: no atomics, fixed summation orders.
+ */
+#ifndef CODA_H
+#define CODA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define CODA_OK 0
+#define CODA_ERR_NULL 1      /* a required pointer is NULL */
+#define CODA_ERR_SHAPE 2     /* a size violates the shape rules above */
+#define CODA_ERR_ALIGN 3     /* a bf16 pointer is not 16-byte aligned (fp32: 8-byte) */
+#define CODA_ERR_WORKSPACE 4 /* a workspace size argument is too small */
+#define CODA_ERR_HIP 5       /* a HIP launch failed */
+#define CODA_ERR_ARG 6       /* another argument is invalid (mode, eps, theta, ...) */
+
+/* Width of one column tile of the row-partial workspace: partial t of a row covers
+ * output columns [t*256, (t+1)*256) (the last tile may be ragged). */
+#define CODA_PARTIAL_TILE_N 256
+
+/* Modes of coda_rowstat_reduce. */
+#define CODA_ROWSTAT_RSQRT_MEAN_EPS 0 /* out[m] = 1 / sqrt(sum_t P[m,t] / d + eps) */
+#define CODA_ROWSTAT_MEAN 1           /* out[m] = sum_t P[m,t] / d                  */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* coda_status_string(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+int coda_abi_version(void);
+
+/* Number of row partials nb = ceil(width / CODA_PARTIAL_TILE_N) that the epilogues
+ * write per row for an output of `width` columns. Returns CODA_ERR_NULL or
+ * CODA_ERR_SHAPE (width < 1). */
+int coda_rowstat_num_partials(int width, int* nb);
+
+/* ---------------------------------------------------------------------------------
+ * Forward GEMM-RMSNorm-GEMM, [notes] key design 1 (both equations) and [pith] Fig. 4:
+ *     y = RMSNorm(x W0 + z, gamma) W1 = r ((x W0 + z) * gamma) W1,  r = 1 / rms(x W0 + z)
+ * computed as three launches on `stream`:
+ *   (1) GEMM1 x W0 whose epilogue adds the residual, h1 = acc + z (stored), scales by
+ *       gamma into the side output h2 = h1 * gamma (stored), and writes per-tile row
+ *       partials P[m, t] = sum over the tile's columns of h1^2 taken from the fp32 h1
+ *       before any rounding ([pith] Listing 2: the square is of the unscaled output);
+ *   (2) the auxiliary reduction r[m] = 1 / sqrt(sum_t P[m, t] / D + eps)
+ *       ([pith] Fig. 4 and the formula under Fig. 5);
+ *   (3) GEMM2 h2 W1 whose epilogue applies the deferred row scale,
+ *       y[i, j] = r[i] * (h2 W1)[i, j] ([notes] key design 1).
+ * Arguments
+ *   x [M,K], w0 [K,D], z [M,D], gamma [D], w1 [D,N1]: bf16 inputs (read only).
+ *   eps: >= 0 and finite, added to the mean square inside the square root.
+ *   h1 [M,D], h2 [M,D]: bf16 outputs (h2 is also GEMM2's input).
+ *   partials [M, nb] fp32 workspace/output, nb = coda_rowstat_num_partials(D).
+ *   r [M] fp32 output.  y [M,N1] bf16 output.
+ * Output buffers must not overlap inputs or each other.
+ * ------------------------------------------------------------------------------- */
+int coda_gemm_rmsnorm_fwd(const uint16_t* x, const uint16_t* w0, const uint16_t* z,
+                          const uint16_t* gamma, const uint16_t* w1, int M, int K, int D,
+                          int N1, float eps, uint16_t* h1, uint16_t* h2, float* partials,
+                          float* r, uint16_t* y, void* stream);
+
+/* Stage (1) of coda_gemm_rmsnorm_fwd alone (same arguments and outputs). */
+int coda_gemm_residual_rmsnorm_partials(const uint16_t* x, const uint16_t* w0,
+                                        const uint16_t* z, const uint16_t* gamma, int M,
+                                        int K, int D, uint16_t* h1, uint16_t* h2,
+                                        float* partials, void* stream);
+
+/* Stage (3) of coda_gemm_rmsnorm_fwd alone: y[i, j] = r[i] * (h2 W1)[i, j].
+ * h2 [M,D] bf16, w1 [D,N1] bf16, r [M] fp32 -> y [M,N1] bf16. */
+int coda_gemm_rowscale(const uint16_t* h2, const uint16_t* w1, const float* r, int M, int D,
+                       int N1, uint16_t* y, void* stream);
+
+/* The auxiliary row reduction over tile partials ([pith] Fig. 4; [notes] key
+ * design 1 for r, key design 3 for s). partials [M, nb] fp32 row-major; out [M] fp32.
+ * Each row is summed in the fixed order t = 0 .. nb-1, then divided by d (> 0).
+ * mode CODA_ROWSTAT_RSQRT_MEAN_EPS: out = 1 / sqrt(sum / d + eps) (eps >= 0);
+ * mode CODA_ROWSTAT_MEAN: out = sum / d (eps ignored). nb >= 1. */
+int coda_rowstat_reduce(const float* partials, int M, int nb, int d, float eps, int mode,
+                        float* out, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * RoPE tables: cos_t[p_os, p] = cos(p_os * theta^(-2p/head_dim)) and sin_t likewise,
+ * for p_os in [0, seq_len), p in [0, head_dim/2), computed in fp64 on the device and
+ * rounded to fp32 (the tables the QKV epilogue reads; [notes] key design 2: the
+ * sin/cos vectors are precomputed and broadcast). cos_t, sin_t: [seq_len, head_dim/2]
+ * fp32 outputs, 8-byte aligned. head_dim even and >= 2, seq_len >= 1, theta > 0.
+ * ------------------------------------------------------------------------------- */
+int coda_rope_tables(float* cos_t, float* sin_t, int seq_len, int head_dim, double theta,
+                     void* stream);
+
+/* GEMM + RoPE for the fused QKV projection ([notes] key design 2; [pith] Fig. 7: each
+ * adjacent feature pair is rotated in registers and yields two outputs).
+ *   h = x W with x [M,K] bf16 and w [K, n_q+n_k+n_v] bf16; the output out [M, n_q+n_k+n_v]
+ *   bf16 holds [Q | K | V] in contiguous column blocks. In the Q and K blocks, within
+ *   each head of head_dim columns, the pair (2p, 2p+1) of row i is rotated by the angle
+ *   pos * theta_p with pos = (i + pos_offset) mod seq_len:
+ *       out[2p] = h[2p] cos - h[2p+1] sin,   out[2p+1] = h[2p] sin + h[2p+1] cos,
+ *   where cos/sin = cos_t/sin_t[pos, p] (from coda_rope_tables). V is stored unrotated.
+ * Rules: head_dim % 8 == 0; n_q, n_k, n_v >= 0 multiples of head_dim with a positive
+ * sum; seq_len >= 1; pos_offset >= 0. */
+int coda_gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t,
+                   const float* sin_t, int M, int K, int n_q, int n_k, int n_v, int head_dim,
+                   int seq_len, int pos_offset, uint16_t* out, void* stream);
+
+/* GEMM + SwiGLU ([notes] key design 2; [pith] Fig. 7): h = x W with x [M,K] bf16 and
+ * w [K, 2F] bf16 whose columns interleave gate and up (even column 2j = G_j, odd
+ * column 2j+1 = U_j); out [M,F] bf16 = silu(G) * U with silu(g) = g / (1 + exp(-g)).
+ * The halving and compaction happen in the epilogue. F % 8 == 0 (and F >= 8). */
+int coda_gemm_swiglu(const uint16_t* x, const uint16_t* w, int M, int K, int F,
+                     uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * RMSNorm-backward row statistic from the grad GEMM's epilogue ([notes] key design 3):
+ *   dh2 = dy W1^T                              (dy [M,N] bf16, w1 [D,N] bf16 -> dh2 [M,D])
+ *   P[m, t] = sum over the tile's columns of dh2 * h2, from the fp32 accumulator and
+ *             the bf16 h2 [M,D]
+ *   s[m] = (1/D) sum_t P[m, t]                 (auxiliary reduction, fixed order)
+ * which equals (1/D) sum_j dy[m, j] (h2 W1)[m, j] by the identity of key design 3.
+ * partials [M, nb] fp32 workspace/output (nb = coda_rowstat_num_partials(D));
+ * s [M] fp32 output. Two launches on `stream`.
+ * ------------------------------------------------------------------------------- */
+int coda_gemm_rmsnorm_bwd_stats(const uint16_t* dy, const uint16_t* w1, const uint16_t* h2,
+                                int M, int D, int N, uint16_t* dh2, float* partials,
+                                float* s, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Unfused baselines, for measurement and numerics comparison only (not the fused
+ * path): the same MFMA main loop with a plain store, and separate HBM-bound kernels
+ * for what the fused epilogues do (the standard operator-by-operator path).
+ * ------------------------------------------------------------------------------- */
+/* c [M,N] bf16 = a [M,K] b, with b [K,N] if b_kn != 0 else b [N,K] (c = a b^T). */
+int coda_baseline_gemm(const uint16_t* a, const uint16_t* b, int M, int K, int N, int b_kn,
+                       uint16_t* c, void* stream);
+/* h1 = h0 + z; r = 1/sqrt(mean(h1^2) + eps); o = r h1 * gamma. h0, z, h1, o [M,D] bf16
+ * (h1 rounded before the norm reads it back, as a separate operator would). */
+int coda_baseline_residual_rmsnorm(const uint16_t* h0, const uint16_t* z,
+                                   const uint16_t* gamma, int M, int D, float eps,
+                                   uint16_t* h1, float* r, uint16_t* o, void* stream);
+/* out = RoPE(h) on the Q and K blocks of h [M, n_q+n_k+n_v] (V copied). */
+int coda_baseline_rope(const uint16_t* h, const float* cos_t, const float* sin_t, int M,
+                       int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset,
+                       uint16_t* out, void* stream);
+/* out [M,F] = silu(h[:, 0::2]) * h[:, 1::2] for h [M,2F]. */
+int coda_baseline_swiglu(const uint16_t* h, int M, int F, uint16_t* out, void* stream);
+/* s[m] = (1/D) sum_k a[m,k] b[m,k] for a, b [M,D] bf16. */
+int coda_baseline_rowdot(const uint16_t* a, const uint16_t* b, int M, int D, float* s,
+                         void* stream);
+/* dst = src, `bytes` a positive multiple of 16: a plain copy kernel of known traffic. */
+int coda_baseline_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CODA_H */

@@ -1,0 +1,142 @@
+"""Host-side checks of the C ABI (no GPU compute).
+
+libcoda.so must load and export every function include/coda.h declares, and argument
+errors must be reported before anything is enqueued. Every call here fails
+validation (or is an M == 0 no-op), so no kernel is launched and no device memory is
+touched; the fake pointers are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_gemm_epilogue_amd as coda
+from transformer_gemm_epilogue_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "coda.h")
+
+OK, NULL, SHAPE, ALIGN, WS, HIP, ARG = 0, 1, 2, 3, 4, 5, 6
+P = 0x100000  # a 16-byte aligned fake device address (never dereferenced)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(coda_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB_PATH):
+        pytest.fail("libcoda.so is not built: run __graft_entry__.build() first")
+    return coda.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for need in ("coda_gemm_rmsnorm_fwd", "coda_rowstat_reduce", "coda_gemm_rope", "coda_gemm_swiglu",
+                 "coda_gemm_rmsnorm_bwd_stats"):
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    missing = [n for n in header_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_declared_symbol():
+    declared = set(header_functions()) - {"coda_status_string"}
+    assert declared == set(coda.SIGNATURES)
+
+
+def test_status_strings(L):
+    for st in range(7):
+        assert L.coda_status_string(st)
+    assert L.coda_abi_version() == 100
+
+
+def test_num_partials(L):
+    for width, nb in ((1, 1), (256, 1), (257, 2), (4096, 16), (6144, 24)):
+        assert coda.num_partials(width) == nb
+    out = ctypes.c_int(0)
+    assert L.coda_rowstat_num_partials(0, ctypes.byref(out)) == SHAPE
+    assert L.coda_rowstat_num_partials(8, None) == NULL
+
+
+def fwd(L, x=P, w0=P, z=P, g=P, w1=P, M=256, K=256, D=256, N1=256, eps=1e-6, h1=P, h2=P, part=P, r=P, y=P):
+    return L.coda_gemm_rmsnorm_fwd(x, w0, z, g, w1, M, K, D, N1, eps, h1, h2, part, r, y, None)
+
+
+def test_fwd_validation(L):
+    assert fwd(L, x=None) == NULL
+    assert fwd(L, y=None) == NULL
+    assert fwd(L, K=100) == SHAPE          # not a multiple of 8
+    assert fwd(L, D=0) == SHAPE
+    assert fwd(L, N1=(1 << 22) + 8) == SHAPE
+    assert fwd(L, M=-1) == SHAPE
+    assert fwd(L, x=P + 8) == ALIGN
+    assert fwd(L, h2=P + 2) == ALIGN
+    assert fwd(L, eps=-1.0) == ARG
+    assert fwd(L, eps=float("nan")) == ARG
+    assert fwd(L, eps=float("inf")) == ARG
+    assert fwd(L, M=0) == OK               # empty batch: nothing to do
+
+
+def test_rope_validation(L):
+    def call(M=64, K=64, n_q=128, n_k=128, n_v=128, hd=128, seq=64, off=0, cos=P, sin=P):
+        return L.coda_gemm_rope(P, P, cos, sin, M, K, n_q, n_k, n_v, hd, seq, off, P, None)
+    assert call(cos=None) == NULL
+    assert call(hd=12) == SHAPE
+    assert call(n_q=64) == SHAPE           # not a multiple of head_dim
+    assert call(n_q=0, n_k=0, n_v=0) == SHAPE
+    assert call(seq=0) == ARG
+    assert call(off=-1) == ARG
+    assert call(cos=P + 4) == ALIGN
+    assert call(M=0) == OK
+
+
+def test_swiglu_validation(L):
+    assert L.coda_gemm_swiglu(P, P, 64, 64, 12, P, None) == SHAPE
+    assert L.coda_gemm_swiglu(P, P, 64, 64, 0, P, None) == SHAPE
+    assert L.coda_gemm_swiglu(P, None, 64, 64, 16, P, None) == NULL
+    assert L.coda_gemm_swiglu(P, P, 64, 60, 16, P, None) == SHAPE
+    assert L.coda_gemm_swiglu(P, P, 0, 64, 16, P, None) == OK
+
+
+def test_bwd_validation(L):
+    assert L.coda_gemm_rmsnorm_bwd_stats(P, P, P, 64, 64, 64, P, P, None, None) == NULL
+    assert L.coda_gemm_rmsnorm_bwd_stats(P, P, P, 64, 63, 64, P, P, P, None) == SHAPE
+    assert L.coda_gemm_rmsnorm_bwd_stats(P, P, P + 8, 64, 64, 64, P, P, P, None) == ALIGN
+    assert L.coda_gemm_rmsnorm_bwd_stats(P, P, P, 0, 64, 64, P, P, P, None) == OK
+
+
+def test_rowstat_validation(L):
+    assert L.coda_rowstat_reduce(P, 64, 0, 64, 0.0, 0, P, None) == SHAPE
+    assert L.coda_rowstat_reduce(P, 64, 4, 0, 0.0, 0, P, None) == SHAPE
+    assert L.coda_rowstat_reduce(P, 64, 4, 64, 0.0, 7, P, None) == ARG
+    assert L.coda_rowstat_reduce(P, 64, 4, 64, -1.0, 0, P, None) == ARG
+    assert L.coda_rowstat_reduce(P + 2, 64, 4, 64, 0.0, 0, P, None) == ALIGN
+    assert L.coda_rowstat_reduce(P, 0, 4, 64, 0.0, 0, P, None) == OK
+
+
+def test_rope_tables_validation(L):
+    assert L.coda_rope_tables(P, P, 0, 128, 1e4, None) == SHAPE
+    assert L.coda_rope_tables(P, P, 16, 7, 1e4, None) == SHAPE
+    assert L.coda_rope_tables(P, P, 16, 128, 0.0, None) == ARG
+    assert L.coda_rope_tables(None, P, 16, 128, 1e4, None) == NULL
+
+
+def test_baseline_validation(L):
+    assert L.coda_baseline_gemm(P, P, 64, 60, 64, 1, P, None) == SHAPE
+    assert L.coda_baseline_copy(P, P, 15, None) == SHAPE
+    assert L.coda_baseline_copy(P, None, 16, None) == NULL
+    assert L.coda_baseline_residual_rmsnorm(P, P, P, 64, 12, 1e-5, P, P, P, None) == SHAPE
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((8, 8), dtype=torch.bfloat16)
+    with pytest.raises((ValueError, RuntimeError)):
+        coda.coda_gemm_swiglu(x, torch.zeros((8, 16), dtype=torch.bfloat16))

@@ -1,0 +1,318 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle on seeded inputs.
+
+Small cases span several 256x256 tiles with ragged tails in every dimension and are
+checked element by element in full. The five stated workloads run at full size in the
+same launch configuration the bench times, and are checked on sampled rows the oracle
+computes one by one (every operation is row-independent). Integer-valued inputs make
+the main loop's result exact, so those cases are compared bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_util import (assert_close, bf16_bits, errors, log, sample_rows, to_dev_bf16, to_dev_f32)
+
+pytestmark = pytest.mark.gpu
+
+TIGHT = 1e-4  # fp32 outputs (r, s, partials) against fp64: relative Frobenius bound
+
+
+@pytest.fixture(scope="module")
+def coda():
+    import torch
+    import transformer_gemm_epilogue_amd as c
+    assert torch.cuda.is_available()
+    c.lib()
+    return c
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def dec(t):
+    return O.decode_bf16(bf16_bits(t))
+
+
+# ------------------------------------------------------------------ forward GEMM-RMSNorm-GEMM
+def run_fwd(coda, wl):
+    dev = {k: to_dev_bf16(wl[k]) for k in ("x", "w0", "z", "gamma", "w1")}
+    h1, h2, part, r, y = coda.coda_gemm_rmsnorm_fwd(dev["x"], dev["w0"], dev["z"], dev["gamma"], dev["w1"],
+                                                    wl["eps"])
+    sync()
+    return h1, h2, part, r, y
+
+
+def check_fwd(got, ref, rows=None):
+    h1, h2, part, r, y = got
+    sel = (lambda a: a) if rows is None else (lambda a: a[rows])
+    assert_close("h1", sel(dec(h1)), ref["h1"])
+    assert_close("h2", sel(dec(h2)), ref["h2"])
+    assert_close("partials", sel(part.cpu().numpy()), ref["partials"], rel_fro=TIGHT)
+    assert_close("r", sel(r.cpu().numpy()), ref["r"], rel_fro=TIGHT)
+    assert_close("y", sel(dec(y)), ref["y"])
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 256, 256), (700, 328, 520, 264), (37, 64, 256, 8), (1, 8, 8, 8)])
+def test_fwd_small_full_compare(coda, shape):
+    M, K, D, N1 = shape
+    log(f"fwd M={M} K={K} D={D} N1={N1}")
+    wl = (W.tiny_fwd(0) if shape == (256, 256, 256, 256)
+          else W.gemm_rmsnorm_fwd_inputs(40 + M % 7, M, K, D, N1, 1e-5))
+    got = run_fwd(coda, wl)
+    ref = O.gemm_rmsnorm_fwd(wl["x"], wl["w0"], wl["z"], wl["gamma"], wl["w1"], wl["eps"])
+    check_fwd(got, ref)
+
+
+def test_fwd_llama_full_size_sampled(coda):
+    wl = W.llama_fwd()
+    log(f"fwd {wl.name}")
+    got = run_fwd(coda, wl)
+    rows = sample_rows(wl["M"], 40, seed=3)
+    ref = O.gemm_rmsnorm_fwd(wl["x"], wl["w0"], wl["z"], wl["gamma"], wl["w1"], wl["eps"], rows=rows)
+    check_fwd(got, ref, rows)
+    r = got[3].cpu().numpy()
+    assert np.all(np.isfinite(r)) and np.all(r > 0)
+
+
+def test_fwd_stages_equal_composition(coda):
+    """coda_gemm_residual_rmsnorm_partials + coda_rowstat_reduce + coda_gemm_rowscale
+    give bit-identical results to coda_gemm_rmsnorm_fwd."""
+    wl = W.gemm_rmsnorm_fwd_inputs(7, 520, 256, 512, 264, 1e-5)
+    dev = {k: to_dev_bf16(wl[k]) for k in ("x", "w0", "z", "gamma", "w1")}
+    h1, h2, part, r, y = coda.coda_gemm_rmsnorm_fwd(dev["x"], dev["w0"], dev["z"], dev["gamma"], dev["w1"],
+                                                    wl["eps"])
+    h1b, h2b, partb = coda.coda_gemm_residual_rmsnorm_partials(dev["x"], dev["w0"], dev["z"], dev["gamma"])
+    rb = coda.coda_rowstat_reduce(partb, 512, wl["eps"], coda.ROWSTAT_RSQRT_MEAN_EPS)
+    yb = coda.coda_gemm_rowscale(h2b, dev["w1"], rb)
+    sync()
+    for a, b in ((h1, h1b), (h2, h2b), (y, yb)):
+        assert np.array_equal(bf16_bits(a), bf16_bits(b))
+    assert np.array_equal(part.cpu().numpy(), partb.cpu().numpy())
+    assert np.array_equal(r.cpu().numpy(), rb.cpu().numpy())
+
+
+def test_fwd_deterministic(coda):
+    wl = W.gemm_rmsnorm_fwd_inputs(8, 600, 512, 768, 256, 1e-5)
+    a = run_fwd(coda, wl)
+    b = run_fwd(coda, wl)
+    for i in (0, 1, 4):
+        assert np.array_equal(bf16_bits(a[i]), bf16_bits(b[i]))
+    for i in (2, 3):
+        assert np.array_equal(a[i].cpu().numpy(), b[i].cpu().numpy())
+
+
+def test_fused_error_not_above_unfused_path(coda):
+    """Numerics of the rewrite: applying r after GEMM2 keeps y at least as close to the
+    exact result as the operator-by-operator bf16 path (GEMM, residual, RMSNorm, GEMM
+    with bf16 intermediates)."""
+    wl = W.llama_fwd(seed=3, M=512)
+    dev = {k: to_dev_bf16(wl[k]) for k in ("x", "w0", "z", "gamma", "w1")}
+    _, _, _, _, y = coda.coda_gemm_rmsnorm_fwd(dev["x"], dev["w0"], dev["z"], dev["gamma"], dev["w1"], wl["eps"])
+    h0 = coda.coda_baseline_gemm(dev["x"], dev["w0"])
+    _, _, o = coda.coda_baseline_residual_rmsnorm(h0, dev["z"], dev["gamma"], wl["eps"])
+    y_unf = coda.coda_baseline_gemm(o, dev["w1"])
+    sync()
+    ref = O.gemm_rmsnorm_fwd(wl["x"], wl["w0"], wl["z"], wl["gamma"], wl["w1"], wl["eps"])["y"]
+    e_f = errors(dec(y), ref)[0]
+    e_u = errors(dec(y_unf), ref)[0]
+    log(f"  y rel_fro fused={e_f:.4e} unfused={e_u:.4e}")
+    assert_close("y_unfused", dec(y_unf), ref)
+    assert e_f <= e_u * 1.02
+
+
+# ------------------------------------------------------------------------------ row reduce
+@pytest.mark.parametrize("nb", [1, 3, 16, 40, 100])
+def test_rowstat_reduce(coda, nb):
+    rng = np.random.default_rng(nb)
+    M = 1000
+    P = (rng.standard_normal((M, nb)) ** 2).astype(np.float32)
+    Pd = to_dev_f32(P)
+    d = 256 * nb - 17
+    r = coda.coda_rowstat_reduce(Pd, d, 1e-5, coda.ROWSTAT_RSQRT_MEAN_EPS)
+    s = coda.coda_rowstat_reduce(Pd, d, 0.0, coda.ROWSTAT_MEAN)
+    sync()
+    assert_close("r", r.cpu().numpy(), O.rowstat_reduce(P, d, 1e-5, "rsqrt_mean_eps"), rel_fro=1e-6)
+    assert_close("s", s.cpu().numpy(), O.rowstat_reduce(P, d, 0.0, "mean"), rel_fro=1e-6)
+
+
+def test_rowstat_reduce_ragged_partial_buffer_offset(coda):
+    """A partials view that is only 4-byte aligned takes the scalar-load path."""
+    import torch
+    rng = np.random.default_rng(5)
+    P = rng.random((130, 17)).astype(np.float32)
+    buf = torch.zeros(130 * 17 + 1, dtype=torch.float32, device="cuda")
+    buf[1:] = to_dev_f32(P.reshape(-1))
+    view = buf[1:].view(130, 17)
+    s = coda.coda_rowstat_reduce(view, 17, 0.0, coda.ROWSTAT_MEAN)
+    sync()
+    assert_close("s", s.cpu().numpy(), O.rowstat_reduce(P, 17, 0.0, "mean"), rel_fro=1e-6)
+
+
+# ------------------------------------------------------------------------------------ RoPE
+def test_rope_tables(coda):
+    seq, hd, theta = 4096, 128, 10000.0
+    c, s = coda.coda_rope_tables(seq, hd, theta)
+    sync()
+    ang = np.arange(seq)[:, None] * theta ** (-2.0 * np.arange(hd // 2)[None, :] / hd)
+    assert np.max(np.abs(c.cpu().numpy() - np.cos(ang))) < 1e-7
+    assert np.max(np.abs(s.cpu().numpy() - np.sin(ang))) < 1e-7
+
+
+def run_rope(coda, wl):
+    c, s = coda.coda_rope_tables(wl["seq_len"], wl["head_dim"], wl["theta"])
+    out = coda.coda_gemm_rope(to_dev_bf16(wl["x"]), to_dev_bf16(wl["w"]), c, s, wl["n_q"], wl["n_k"], wl["n_v"],
+                              wl["head_dim"], wl["seq_len"], wl["pos_offset"])
+    sync()
+    return dec(out)
+
+
+def oracle_rope(wl, rows=None):
+    return O.gemm_rope(wl["x"], wl["w"], wl["n_q"], wl["n_k"], wl["n_v"], wl["head_dim"], wl["seq_len"],
+                       wl["pos_offset"], wl["theta"], rows=rows)
+
+
+@pytest.mark.parametrize("case", [
+    dict(M=600, K=200, n_q=256, n_k=128, n_v=128, head_dim=128, seq_len=300, pos_offset=7),
+    dict(M=70, K=64, n_q=64, n_k=64, n_v=64, head_dim=64, seq_len=70, pos_offset=0),
+    dict(M=300, K=136, n_q=0, n_k=0, n_v=264, head_dim=8, seq_len=16, pos_offset=0),
+])
+def test_rope_small_full_compare(coda, case):
+    log(f"rope {case}")
+    wl = W.rope_qkv(seed=11, **case)
+    assert_close("qkv", run_rope(coda, wl), oracle_rope(wl))
+
+
+def test_rope_full_size_sampled(coda):
+    wl = W.rope_qkv()
+    log(f"rope {wl.name}")
+    got = run_rope(coda, wl)
+    rows = sample_rows(wl["M"], 48, seed=1)
+    ref = oracle_rope(wl, rows)
+    assert_close("qkv", got[rows], ref)
+    nqk = wl["n_q"] + wl["n_k"]
+    assert_close("q", got[rows][:, :wl["n_q"]], ref[:, :wl["n_q"]])
+    assert_close("k", got[rows][:, wl["n_q"]:nqk], ref[:, wl["n_q"]:nqk])
+    assert_close("v", got[rows][:, nqk:], ref[:, nqk:])
+
+
+# ---------------------------------------------------------------------------------- SwiGLU
+@pytest.mark.parametrize("shape", [(333, 136, 200), (256, 256, 128), (5, 64, 8)])
+def test_swiglu_small_full_compare(coda, shape):
+    M, K, F = shape
+    log(f"swiglu M={M} K={K} F={F}")
+    wl = W.swiglu(seed=12, M=M, K=K, F=F)
+    out = coda.coda_gemm_swiglu(to_dev_bf16(wl["x"]), to_dev_bf16(wl["w"]))
+    sync()
+    assert_close("swiglu", dec(out), O.gemm_swiglu(wl["x"], wl["w"]))
+
+
+def test_swiglu_full_size_sampled(coda):
+    wl = W.swiglu()
+    log(f"swiglu {wl.name}")
+    out = coda.coda_gemm_swiglu(to_dev_bf16(wl["x"]), to_dev_bf16(wl["w"]))
+    sync()
+    rows = sample_rows(wl["M"], 40, seed=2)
+    assert_close("swiglu", dec(out)[rows], O.gemm_swiglu(wl["x"], wl["w"], rows=rows))
+
+
+# ----------------------------------------------------------------------- backward statistic
+def run_bwd(coda, wl):
+    dh2, part, s = coda.coda_gemm_rmsnorm_bwd_stats(to_dev_bf16(wl["dy"]), to_dev_bf16(wl["w1"]),
+                                                    to_dev_bf16(wl["h2"]))
+    sync()
+    return dec(dh2), part.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("shape", [(517, 392, 264), (256, 256, 256), (3, 16, 8)])
+def test_bwd_small_full_compare(coda, shape):
+    M, D, N = shape
+    log(f"bwd M={M} D={D} N={N}")
+    wl = W.bwd_stats(seed=13, M=M, D=D, N=N)
+    dh2, part, s = run_bwd(coda, wl)
+    ref = O.gemm_rmsnorm_bwd_stats(wl["dy"], wl["w1"], wl["h2"])
+    assert_close("dh2", dh2, ref["dh2"])
+    assert_close("partials", part, ref["partials"], rel_fro=TIGHT)
+    assert_close("s", s, ref["s_prime"], rel_fro=TIGHT)
+
+
+def test_bwd_full_size_sampled(coda):
+    wl = W.bwd_stats()
+    log(f"bwd {wl.name}")
+    dh2, part, s = run_bwd(coda, wl)
+    rows = sample_rows(wl["M"], 40, seed=4)
+    ref = O.gemm_rmsnorm_bwd_stats(wl["dy"], wl["w1"], wl["h2"], rows=rows)
+    assert_close("dh2", dh2[rows], ref["dh2"])
+    assert_close("partials", part[rows], ref["partials"], rel_fro=TIGHT)
+    # graded against (1/d) sum(dY * (h2 W1)), the right-hand form of the identity
+    assert_close("s", s[rows], ref["s_prime"], rel_fro=TIGHT)
+
+
+# ------------------------------------------------------------------- exact integer results
+def test_integer_inputs_are_bit_exact(coda):
+    """Small integers (|v| <= 2, K <= 256) make every product and fp32 partial sum exact,
+    so the bf16 outputs must equal the round-to-nearest-even of the exact result."""
+    rng = np.random.default_rng(100)
+    M, K, N = 300, 136, 264
+    x = W.small_int_bf16(rng, (M, K), -2, 2)
+    w = W.small_int_bf16(rng, (K, N), -2, 2)
+    z = W.small_int_bf16(rng, (M, N), -3, 3)
+    exact = O.matmul(x, w)
+    want = W.f32_to_bf16_bits(exact.astype(np.float32))
+    xd, wd = to_dev_bf16(x), to_dev_bf16(w)
+    kn = coda.coda_baseline_gemm(xd, wd, b_kn=True)
+    nk = coda.coda_baseline_gemm(xd, to_dev_bf16(np.ascontiguousarray(w.T)), b_kn=False)
+    c, s = coda.coda_rope_tables(16, 8)
+    v_only = coda.coda_gemm_rope(xd, wd, c, s, 0, 0, N, 8, 16)
+    gamma = W.small_int_bf16(rng, (N,), 1, 1)
+    h1, h2, part = coda.coda_gemm_residual_rmsnorm_partials(xd, wd, to_dev_bf16(z), to_dev_bf16(gamma))
+    sync()
+    assert np.array_equal(bf16_bits(kn), want)
+    assert np.array_equal(bf16_bits(nk), want)
+    assert np.array_equal(bf16_bits(v_only), want)
+    h1_exact = exact + O.decode_bf16(z)
+    assert np.array_equal(bf16_bits(h1), W.f32_to_bf16_bits(h1_exact.astype(np.float32)))
+    assert np.array_equal(bf16_bits(h2), W.f32_to_bf16_bits(h1_exact.astype(np.float32)))
+    # the partial sums of squares of integers below 2^24 are exact in fp32 as well
+    assert np.array_equal(part.cpu().numpy().astype(np.float64), O.tile_row_sums(h1_exact ** 2))
+
+
+def test_integer_inputs_bwd_bit_exact(coda):
+    rng = np.random.default_rng(101)
+    M, D, N = 280, 264, 136
+    dy = W.small_int_bf16(rng, (M, N), -2, 2)
+    w1 = W.small_int_bf16(rng, (D, N), -2, 2)
+    h2 = W.small_int_bf16(rng, (M, D), -2, 2)
+    dh2, part, s = coda.coda_gemm_rmsnorm_bwd_stats(to_dev_bf16(dy), to_dev_bf16(w1), to_dev_bf16(h2))
+    sync()
+    ref = O.gemm_rmsnorm_bwd_stats(dy, w1, h2)
+    assert np.array_equal(bf16_bits(dh2), W.f32_to_bf16_bits(ref["dh2"].astype(np.float32)))
+    assert np.array_equal(part.cpu().numpy().astype(np.float64), ref["partials"])
+
+
+# ----------------------------------------------------------------------------- error paths
+def test_misaligned_pointer_is_rejected_and_writes_nothing(coda):
+    import torch
+    x = torch.zeros((64, 72), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((64, 16), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((64, 8), 7.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        coda.coda_gemm_swiglu(x[:, 8:], w, out=out)   # non-contiguous view: rejected by the binding
+    flat = torch.zeros(64 * 64 + 1, dtype=torch.bfloat16, device="cuda")
+    xm = flat[1:].view(64, 64)                          # contiguous but 2-byte aligned
+    with pytest.raises(coda.CodaError) as e:
+        coda.coda_gemm_swiglu(xm, w, out=out)
+    assert e.value.status == 3
+    sync()
+    assert torch.all(out == 7.0)
+
+
+def test_empty_batch_is_a_noop(coda):
+    import torch
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((64, 16), dtype=torch.bfloat16, device="cuda")
+    out = coda.coda_gemm_swiglu(x, w)
+    sync()
+    assert out.shape == (0, 8)

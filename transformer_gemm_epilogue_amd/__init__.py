@@ -1,0 +1,312 @@
+"""Python binding of libcoda.so: gfx950 bf16 GEMMs with Transformer epilogues.
+
+Argument marshalling only. Every step of the computation runs in the HIP kernels of
+libcoda.so; torch is used for device memory (output allocation) and for the current
+HIP stream. There is no CPU fallback: if the library is missing or a tensor is not
+on the GPU, the call raises.
+
+Function names match the C ABI in include/coda.h. bf16 tensors are torch.bfloat16
+CUDA tensors (their storage holds the bf16 bit patterns the C ABI takes as uint16).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+__all__ = [
+    "CodaError",
+    "lib",
+    "PARTIAL_TILE_N",
+    "ROWSTAT_RSQRT_MEAN_EPS",
+    "ROWSTAT_MEAN",
+    "num_partials",
+    "coda_gemm_rmsnorm_fwd",
+    "coda_gemm_residual_rmsnorm_partials",
+    "coda_gemm_rowscale",
+    "coda_rowstat_reduce",
+    "coda_rope_tables",
+    "coda_gemm_rope",
+    "coda_gemm_swiglu",
+    "coda_gemm_rmsnorm_bwd_stats",
+    "coda_baseline_gemm",
+    "coda_baseline_residual_rmsnorm",
+    "coda_baseline_rope",
+    "coda_baseline_swiglu",
+    "coda_baseline_rowdot",
+    "coda_baseline_copy",
+]
+
+PARTIAL_TILE_N = 256
+ROWSTAT_RSQRT_MEAN_EPS = 0
+ROWSTAT_MEAN = 1
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_D = ctypes.c_double
+_I64 = ctypes.c_int64
+
+# name -> argument types (every entry point returns int status)
+SIGNATURES = {
+    "coda_abi_version": [],
+    "coda_rowstat_num_partials": [_I, ctypes.POINTER(_I)],
+    "coda_gemm_rmsnorm_fwd": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P],
+    "coda_gemm_residual_rmsnorm_partials": [_P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
+    "coda_gemm_rowscale": [_P, _P, _P, _I, _I, _I, _P, _P],
+    "coda_rowstat_reduce": [_P, _I, _I, _I, _F, _I, _P, _P],
+    "coda_rope_tables": [_P, _P, _I, _I, _D, _P],
+    "coda_gemm_rope": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P],
+    "coda_gemm_swiglu": [_P, _P, _I, _I, _I, _P, _P],
+    "coda_gemm_rmsnorm_bwd_stats": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
+    "coda_baseline_gemm": [_P, _P, _I, _I, _I, _I, _P, _P],
+    "coda_baseline_residual_rmsnorm": [_P, _P, _P, _I, _I, _F, _P, _P, _P, _P],
+    "coda_baseline_rope": [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P],
+    "coda_baseline_swiglu": [_P, _I, _I, _P, _P],
+    "coda_baseline_rowdot": [_P, _P, _I, _I, _P, _P],
+    "coda_baseline_copy": [_P, _P, _I64, _P],
+}
+
+
+class CodaError(RuntimeError):
+    def __init__(self, name: str, status: int, message: str):
+        super().__init__(f"{name} failed: status {status} ({message})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcoda.so (built in-tree by build.py) and declare its signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run transformer_gemm_epilogue_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = _I
+        L.coda_status_string.argtypes = [_I]
+        L.coda_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _call(name: str, *args) -> None:
+    L = lib()
+    st = getattr(L, name)(*args)
+    if st != 0:
+        raise CodaError(name, st, L.coda_status_string(st).decode())
+
+
+def _torch():
+    import torch  # imported lazily: the library itself does not need it
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor (there is no CPU path)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _bf16(t, name):
+    return _dev(t, _torch().bfloat16, name)
+
+
+def _f32(t, name):
+    return _dev(t, _torch().float32, name)
+
+
+def _empty(shape, dtype, like):
+    return _torch().empty(shape, dtype=dtype, device=like.device)
+
+
+def num_partials(width: int) -> int:
+    nb = ctypes.c_int(0)
+    _call("coda_rowstat_num_partials", int(width), ctypes.byref(nb))
+    return nb.value
+
+
+# ------------------------------------------------------------------ fused entry points
+def coda_gemm_rmsnorm_fwd(x, w0, z, gamma, w1, eps, h1=None, h2=None, partials=None, r=None, y=None,
+                          stream=None):
+    """y = RMSNorm(x w0 + z, gamma) w1 via GEMM1-epilogue / row reduce / GEMM2-epilogue.
+    Returns (h1, h2, partials, r, y)."""
+    torch = _torch()
+    M, K = x.shape
+    D = w0.shape[1]
+    N1 = w1.shape[1]
+    if w0.shape[0] != K or z.shape != (M, D) or gamma.shape != (D,) or w1.shape[0] != D:
+        raise ValueError("coda_gemm_rmsnorm_fwd: inconsistent shapes")
+    h1 = _empty((M, D), torch.bfloat16, x) if h1 is None else h1
+    h2 = _empty((M, D), torch.bfloat16, x) if h2 is None else h2
+    partials = _empty((M, num_partials(D)), torch.float32, x) if partials is None else partials
+    r = _empty((M,), torch.float32, x) if r is None else r
+    y = _empty((M, N1), torch.bfloat16, x) if y is None else y
+    _call("coda_gemm_rmsnorm_fwd", _bf16(x, "x"), _bf16(w0, "w0"), _bf16(z, "z"), _bf16(gamma, "gamma"),
+          _bf16(w1, "w1"), M, K, D, N1, float(eps), _bf16(h1, "h1"), _bf16(h2, "h2"),
+          _f32(partials, "partials"), _f32(r, "r"), _bf16(y, "y"), _stream(stream))
+    return h1, h2, partials, r, y
+
+
+def coda_gemm_residual_rmsnorm_partials(x, w0, z, gamma, h1=None, h2=None, partials=None, stream=None):
+    torch = _torch()
+    M, K = x.shape
+    D = w0.shape[1]
+    if w0.shape[0] != K or z.shape != (M, D) or gamma.shape != (D,):
+        raise ValueError("coda_gemm_residual_rmsnorm_partials: inconsistent shapes")
+    h1 = _empty((M, D), torch.bfloat16, x) if h1 is None else h1
+    h2 = _empty((M, D), torch.bfloat16, x) if h2 is None else h2
+    partials = _empty((M, num_partials(D)), torch.float32, x) if partials is None else partials
+    _call("coda_gemm_residual_rmsnorm_partials", _bf16(x, "x"), _bf16(w0, "w0"), _bf16(z, "z"),
+          _bf16(gamma, "gamma"), M, K, D, _bf16(h1, "h1"), _bf16(h2, "h2"), _f32(partials, "partials"),
+          _stream(stream))
+    return h1, h2, partials
+
+
+def coda_gemm_rowscale(h2, w1, r, y=None, stream=None):
+    torch = _torch()
+    M, D = h2.shape
+    N1 = w1.shape[1]
+    if w1.shape[0] != D or r.shape != (M,):
+        raise ValueError("coda_gemm_rowscale: inconsistent shapes")
+    y = _empty((M, N1), torch.bfloat16, h2) if y is None else y
+    _call("coda_gemm_rowscale", _bf16(h2, "h2"), _bf16(w1, "w1"), _f32(r, "r"), M, D, N1, _bf16(y, "y"),
+          _stream(stream))
+    return y
+
+
+def coda_rowstat_reduce(partials, d, eps=0.0, mode=ROWSTAT_RSQRT_MEAN_EPS, out=None, stream=None):
+    torch = _torch()
+    M, nb = partials.shape
+    out = _empty((M,), torch.float32, partials) if out is None else out
+    _call("coda_rowstat_reduce", _f32(partials, "partials"), M, nb, int(d), float(eps), int(mode),
+          _f32(out, "out"), _stream(stream))
+    return out
+
+
+def coda_rope_tables(seq_len, head_dim, theta=10000.0, device="cuda", stream=None):
+    """Returns (cos_t, sin_t), each [seq_len, head_dim // 2] fp32, built on the GPU."""
+    torch = _torch()
+    cos_t = torch.empty((seq_len, head_dim // 2), dtype=torch.float32, device=device)
+    sin_t = torch.empty_like(cos_t)
+    _call("coda_rope_tables", _f32(cos_t, "cos_t"), _f32(sin_t, "sin_t"), int(seq_len), int(head_dim),
+          float(theta), _stream(stream))
+    return cos_t, sin_t
+
+
+def coda_gemm_rope(x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset=0, out=None, stream=None):
+    torch = _torch()
+    M, K = x.shape
+    N = n_q + n_k + n_v
+    if w.shape != (K, N):
+        raise ValueError("coda_gemm_rope: w must be [K, n_q + n_k + n_v]")
+    out = _empty((M, N), torch.bfloat16, x) if out is None else out
+    _call("coda_gemm_rope", _bf16(x, "x"), _bf16(w, "w"), _f32(cos_t, "cos_t"), _f32(sin_t, "sin_t"), M, K,
+          n_q, n_k, n_v, head_dim, seq_len, pos_offset, _bf16(out, "out"), _stream(stream))
+    return out
+
+
+def coda_gemm_swiglu(x, w, out=None, stream=None):
+    torch = _torch()
+    M, K = x.shape
+    if w.shape[0] != K or w.shape[1] % 2:
+        raise ValueError("coda_gemm_swiglu: w must be [K, 2F]")
+    F = w.shape[1] // 2
+    out = _empty((M, F), torch.bfloat16, x) if out is None else out
+    _call("coda_gemm_swiglu", _bf16(x, "x"), _bf16(w, "w"), M, K, F, _bf16(out, "out"), _stream(stream))
+    return out
+
+
+def coda_gemm_rmsnorm_bwd_stats(dy, w1, h2, dh2=None, partials=None, s=None, stream=None):
+    """dh2 = dy w1^T with row partials of dh2 * h2 in the epilogue, then s = mean.
+    Returns (dh2, partials, s)."""
+    torch = _torch()
+    M, N = dy.shape
+    D = w1.shape[0]
+    if w1.shape[1] != N or h2.shape != (M, D):
+        raise ValueError("coda_gemm_rmsnorm_bwd_stats: inconsistent shapes")
+    dh2 = _empty((M, D), torch.bfloat16, dy) if dh2 is None else dh2
+    partials = _empty((M, num_partials(D)), torch.float32, dy) if partials is None else partials
+    s = _empty((M,), torch.float32, dy) if s is None else s
+    _call("coda_gemm_rmsnorm_bwd_stats", _bf16(dy, "dy"), _bf16(w1, "w1"), _bf16(h2, "h2"), M, D, N,
+          _bf16(dh2, "dh2"), _f32(partials, "partials"), _f32(s, "s"), _stream(stream))
+    return dh2, partials, s
+
+
+# ------------------------------------------------------------------- unfused baselines
+def coda_baseline_gemm(a, b, b_kn=True, c=None, stream=None):
+    torch = _torch()
+    M, K = a.shape
+    N = b.shape[1] if b_kn else b.shape[0]
+    if (b.shape[0] if b_kn else b.shape[1]) != K:
+        raise ValueError("coda_baseline_gemm: inconsistent shapes")
+    c = _empty((M, N), torch.bfloat16, a) if c is None else c
+    _call("coda_baseline_gemm", _bf16(a, "a"), _bf16(b, "b"), M, K, N, 1 if b_kn else 0, _bf16(c, "c"),
+          _stream(stream))
+    return c
+
+
+def coda_baseline_residual_rmsnorm(h0, z, gamma, eps, h1=None, r=None, o=None, stream=None):
+    torch = _torch()
+    M, D = h0.shape
+    h1 = _empty((M, D), torch.bfloat16, h0) if h1 is None else h1
+    o = _empty((M, D), torch.bfloat16, h0) if o is None else o
+    r = _empty((M,), torch.float32, h0) if r is None else r
+    _call("coda_baseline_residual_rmsnorm", _bf16(h0, "h0"), _bf16(z, "z"), _bf16(gamma, "gamma"), M, D,
+          float(eps), _bf16(h1, "h1"), _f32(r, "r"), _bf16(o, "o"), _stream(stream))
+    return h1, r, o
+
+
+def coda_baseline_rope(h, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset=0, out=None, stream=None):
+    torch = _torch()
+    M = h.shape[0]
+    out = _empty(h.shape, torch.bfloat16, h) if out is None else out
+    _call("coda_baseline_rope", _bf16(h, "h"), _f32(cos_t, "cos_t"), _f32(sin_t, "sin_t"), M, n_q, n_k, n_v,
+          head_dim, seq_len, pos_offset, _bf16(out, "out"), _stream(stream))
+    return out
+
+
+def coda_baseline_swiglu(h, out=None, stream=None):
+    torch = _torch()
+    M, N2 = h.shape
+    F = N2 // 2
+    out = _empty((M, F), torch.bfloat16, h) if out is None else out
+    _call("coda_baseline_swiglu", _bf16(h, "h"), M, F, _bf16(out, "out"), _stream(stream))
+    return out
+
+
+def coda_baseline_rowdot(a, b, s=None, stream=None):
+    torch = _torch()
+    M, D = a.shape
+    s = _empty((M,), torch.float32, a) if s is None else s
+    _call("coda_baseline_rowdot", _bf16(a, "a"), _bf16(b, "b"), M, D, _f32(s, "s"), _stream(stream))
+    return s
+
+
+def coda_baseline_copy(src, dst, stream=None):
+    if src.numel() * src.element_size() != dst.numel() * dst.element_size():
+        raise ValueError("coda_baseline_copy: size mismatch")
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("coda_baseline_copy: contiguous GPU tensors required")
+    _call("coda_baseline_copy", ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+          src.numel() * src.element_size(), _stream(stream))
+    return dst

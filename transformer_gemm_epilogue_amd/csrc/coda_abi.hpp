@@ -1,0 +1,46 @@
+// Host-side argument checks shared by the C-ABI entry points. Every check runs before
+// anything is enqueued, so a failing call leaves device memory untouched.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "coda.h"
+
+namespace coda {
+
+constexpr int kMaxDim = 1 << 22;  // bound on K and output widths (keeps buffer ranges < 2^31)
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline int check_depth_or_width(int v) {
+  if (v < 8 || v > kMaxDim || (v % 8) != 0) return CODA_ERR_SHAPE;
+  return CODA_OK;
+}
+
+inline int check_rows(int M) { return M < 0 ? CODA_ERR_SHAPE : CODA_OK; }
+
+inline int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? CODA_OK : CODA_ERR_HIP;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+#define CODA_TRY(expr)            \
+  do {                            \
+    const int _st = (expr);       \
+    if (_st != CODA_OK) return _st; \
+  } while (0)
+
+#define CODA_NONNULL(p) \
+  do {                  \
+    if (!(p)) return CODA_ERR_NULL; \
+  } while (0)
+
+#define CODA_ALIGN16(p) \
+  do {                  \
+    if (!::coda::aligned((p), 16)) return CODA_ERR_ALIGN; \
+  } while (0)
+
+}  // namespace coda

@@ -1,0 +1,316 @@
+// Auxiliary kernels: the row reduction over tile partials, the RoPE table builder, and
+// the unfused baseline operators (kept for measurement and the numerics comparison).
+#include <algorithm>
+
+#include "coda_abi.hpp"
+#include "coda_common.hpp"
+
+using namespace coda;
+
+namespace {
+
+// ----------------------------------------------------------- auxiliary row reduction
+// One wave per 64 rows. The [64, nb] block of partials is streamed through LDS in
+// column chunks with coalesced 16-byte loads (the rows of a block are contiguous in
+// HBM), then each lane sums its own row in the fixed order t = 0, 1, ..., nb-1.
+constexpr int kRsRows = 64;
+constexpr int kRsCh = 32;
+
+template <bool kVec4>
+__global__ __launch_bounds__(64) void rowstat_reduce_kernel(const float* __restrict__ P, int M, int nb, float d,
+                                                            float eps, int mode, float* __restrict__ out) {
+  __shared__ float tile[kRsRows][kRsCh + 1];
+  const int m0 = blockIdx.x * kRsRows;
+  const int rows = min(kRsRows, M - m0);
+  const int t = threadIdx.x;
+  float s = 0.f;
+  for (int c0 = 0; c0 < nb; c0 += kRsCh) {
+    const int cw = min(kRsCh, nb - c0);
+    if constexpr (kVec4) {
+      const int q = cw >> 2;  // float4s per row in this chunk (nb % 4 == 0)
+      const int total = rows * q;
+      for (int e = t; e < total; e += 64) {
+        const int r = e / q, c = (e - r * q) * 4;
+        const float4 v = *(const float4*)(P + (size_t)(m0 + r) * nb + c0 + c);
+        tile[r][c] = v.x;
+        tile[r][c + 1] = v.y;
+        tile[r][c + 2] = v.z;
+        tile[r][c + 3] = v.w;
+      }
+    } else {
+      const int total = rows * cw;
+      for (int e = t; e < total; e += 64) {
+        const int r = e / cw, c = e - r * cw;
+        tile[r][c] = P[(size_t)(m0 + r) * nb + c0 + c];
+      }
+    }
+    __syncthreads();
+    if (t < rows)
+      for (int c = 0; c < cw; ++c) s += tile[t][c];
+    __syncthreads();
+  }
+  if (t < rows) {
+    const float mean = s / d;
+    out[m0 + t] = (mode == CODA_ROWSTAT_RSQRT_MEAN_EPS) ? 1.0f / sqrtf(mean + eps) : mean;
+  }
+}
+
+// ------------------------------------------------------------------------ RoPE tables
+__global__ void rope_tables_kernel(float* __restrict__ cos_t, float* __restrict__ sin_t, int seq_len, int half,
+                                   int head_dim, double theta) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)seq_len * half) return;
+  const int pos = (int)(i / half);
+  const int p = (int)(i - (long long)pos * half);
+  const double inv_freq = pow(theta, -2.0 * (double)p / (double)head_dim);
+  const double a = (double)pos * inv_freq;
+  cos_t[i] = (float)cos(a);
+  sin_t[i] = (float)sin(a);
+}
+
+// ---------------------------------------------------------------- unfused baselines
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  const float s = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return s;
+}
+
+// One row per 256-thread block: h1 = bf16(h0 + z); r from the stored bf16 h1 (as a
+// separate RMSNorm operator reads it); o = bf16(r h1 gamma).
+__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const uint16_t* __restrict__ h0,
+                                                                const uint16_t* __restrict__ z,
+                                                                const uint16_t* __restrict__ gamma, int D, float eps,
+                                                                uint16_t* __restrict__ h1, float* __restrict__ r,
+                                                                uint16_t* __restrict__ o) {
+  __shared__ float red[4];
+  const size_t base = (size_t)blockIdx.x * D;
+  float ss = 0.f;
+  for (int c = threadIdx.x * 8; c < D; c += 256 * 8) {
+    const u32x4_t a = *(const u32x4_t*)(h0 + base + c);
+    const u32x4_t b = *(const u32x4_t*)(z + base + c);
+    u32x4_t h;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w = pack_bf16x2(bf16_lo(a[q]) + bf16_lo(b[q]), bf16_hi(a[q]) + bf16_hi(b[q]));
+      h[q] = w;
+      ss += bf16_lo(w) * bf16_lo(w) + bf16_hi(w) * bf16_hi(w);
+    }
+    *(u32x4_t*)(h1 + base + c) = h;
+  }
+  const float tot = block_sum_256(ss, red);
+  const float rr = 1.0f / sqrtf(tot / (float)D + eps);
+  if (threadIdx.x == 0) r[blockIdx.x] = rr;
+  for (int c = threadIdx.x * 8; c < D; c += 256 * 8) {
+    const u32x4_t h = *(const u32x4_t*)(h1 + base + c);
+    const u32x4_t g = *(const u32x4_t*)(gamma + c);
+    u32x4_t v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = pack_bf16x2(rr * bf16_lo(h[q]) * bf16_lo(g[q]), rr * bf16_hi(h[q]) * bf16_hi(g[q]));
+    *(u32x4_t*)(o + base + c) = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
+                                                      int D, float* __restrict__ s) {
+  __shared__ float red[4];
+  const size_t base = (size_t)blockIdx.x * D;
+  float acc = 0.f;
+  for (int c = threadIdx.x * 8; c < D; c += 256 * 8) {
+    const u32x4_t x = *(const u32x4_t*)(a + base + c);
+    const u32x4_t y = *(const u32x4_t*)(b + base + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc += bf16_lo(x[q]) * bf16_lo(y[q]) + bf16_hi(x[q]) * bf16_hi(y[q]);
+  }
+  const float tot = block_sum_256(acc, red);
+  if (threadIdx.x == 0) s[blockIdx.x] = tot / (float)D;
+}
+
+// 8 consecutive columns (4 rotation pairs) per thread.
+__global__ __launch_bounds__(256) void rope_kernel(const uint16_t* __restrict__ h, const float* __restrict__ cos_t,
+                                                    const float* __restrict__ sin_t, int M, int N, int n_rot,
+                                                    int head_dim, int seq_len, int pos_offset,
+                                                    uint16_t* __restrict__ out) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per_row = N / 8;
+  if (i >= (long long)M * per_row) return;
+  const int m = (int)(i / per_row);
+  const int n = (int)(i - (long long)m * per_row) * 8;
+  const size_t off = (size_t)m * N + n;
+  u32x4_t v = *(const u32x4_t*)(h + off);
+  if (n < n_rot) {
+    const int pos = (int)(((long long)m + pos_offset) % seq_len);
+    const int half = head_dim >> 1;
+    const int p0 = (n % head_dim) >> 1;
+    const float4 c = *(const float4*)(cos_t + (size_t)pos * half + p0);
+    const float4 s = *(const float4*)(sin_t + (size_t)pos * half + p0);
+    const float cc[4] = {c.x, c.y, c.z, c.w};
+    const float sn[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float e = bf16_lo(v[q]), o = bf16_hi(v[q]);
+      v[q] = pack_bf16x2(e * cc[q] - o * sn[q], e * sn[q] + o * cc[q]);
+    }
+  }
+  *(u32x4_t*)(out + off) = v;
+}
+
+// 8 accumulator columns (4 gate/up pairs) -> 4 outputs per thread.
+__global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict__ h, int M, int F,
+                                                      uint16_t* __restrict__ out) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per_row = F / 4;
+  if (i >= (long long)M * per_row) return;
+  const int m = (int)(i / per_row);
+  const int j = (int)(i - (long long)m * per_row) * 4;
+  const u32x4_t v = *(const u32x4_t*)(h + (size_t)m * 2 * F + 2 * j);
+  float y[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float g = bf16_lo(v[q]), u = bf16_hi(v[q]);
+    y[q] = g / (1.0f + __expf(-g)) * u;
+  }
+  u32x2_t o;
+  o.x = pack_bf16x2(y[0], y[1]);
+  o.y = pack_bf16x2(y[2], y[3]);
+  *(u32x2_t*)(out + (size_t)m * F + j) = o;
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
+                                                    long long n16) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+inline unsigned blocks_for(long long n, int per_block) { return (unsigned)((n + per_block - 1) / per_block); }
+
+}  // namespace
+
+// Shared with the GEMM entry points (no argument checks: callers have checked).
+int coda_rowstat_reduce_impl(const float* partials, int M, int nb, int d, float eps, int mode, float* out,
+                             hipStream_t stream) {
+  const unsigned grid = blocks_for(M, kRsRows);
+  if (nb % 4 == 0 && aligned(partials, 16))
+    hipLaunchKernelGGL((rowstat_reduce_kernel<true>), dim3(grid), dim3(64), 0, stream, partials, M, nb, (float)d,
+                       eps, mode, out);
+  else
+    hipLaunchKernelGGL((rowstat_reduce_kernel<false>), dim3(grid), dim3(64), 0, stream, partials, M, nb,
+                       (float)d, eps, mode, out);
+  return launch_status();
+}
+
+extern "C" {
+
+int coda_rowstat_reduce(const float* partials, int M, int nb, int d, float eps, int mode, float* out,
+                        void* stream) {
+  CODA_TRY(check_rows(M));
+  if (nb < 1 || nb > kMaxDim || d < 1) return CODA_ERR_SHAPE;
+  if (mode != CODA_ROWSTAT_RSQRT_MEAN_EPS && mode != CODA_ROWSTAT_MEAN) return CODA_ERR_ARG;
+  if (mode == CODA_ROWSTAT_RSQRT_MEAN_EPS && (!(eps >= 0.0f) || !(eps < __builtin_huge_valf()))) return CODA_ERR_ARG;
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(partials);
+  CODA_NONNULL(out);
+  if (!aligned(partials, 4) || !aligned(out, 4)) return CODA_ERR_ALIGN;
+  return coda_rowstat_reduce_impl(partials, M, nb, d, eps, mode, out, as_stream(stream));
+}
+
+int coda_rope_tables(float* cos_t, float* sin_t, int seq_len, int head_dim, double theta, void* stream) {
+  CODA_NONNULL(cos_t);
+  CODA_NONNULL(sin_t);
+  if (seq_len < 1 || head_dim < 2 || head_dim % 2 != 0 || head_dim > kMaxDim) return CODA_ERR_SHAPE;
+  if (!(theta > 0.0) || !(theta < __builtin_huge_val())) return CODA_ERR_ARG;
+  if (!aligned(cos_t, 8) || !aligned(sin_t, 8)) return CODA_ERR_ALIGN;
+  const long long n = (long long)seq_len * (head_dim / 2);
+  hipLaunchKernelGGL(rope_tables_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, as_stream(stream), cos_t, sin_t,
+                     seq_len, head_dim / 2, head_dim, theta);
+  return launch_status();
+}
+
+int coda_baseline_residual_rmsnorm(const uint16_t* h0, const uint16_t* z, const uint16_t* gamma, int M, int D,
+                                   float eps, uint16_t* h1, float* r, uint16_t* o, void* stream) {
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(D));
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(h0);
+  CODA_NONNULL(z);
+  CODA_NONNULL(gamma);
+  CODA_NONNULL(h1);
+  CODA_NONNULL(r);
+  CODA_NONNULL(o);
+  CODA_ALIGN16(h0);
+  CODA_ALIGN16(z);
+  CODA_ALIGN16(gamma);
+  CODA_ALIGN16(h1);
+  CODA_ALIGN16(o);
+  hipLaunchKernelGGL(residual_rmsnorm_kernel, dim3(M), dim3(256), 0, as_stream(stream), h0, z, gamma, D, eps, h1, r,
+                     o);
+  return launch_status();
+}
+
+int coda_baseline_rowdot(const uint16_t* a, const uint16_t* b, int M, int D, float* s, void* stream) {
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(D));
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(a);
+  CODA_NONNULL(b);
+  CODA_NONNULL(s);
+  CODA_ALIGN16(a);
+  CODA_ALIGN16(b);
+  hipLaunchKernelGGL(rowdot_kernel, dim3(M), dim3(256), 0, as_stream(stream), a, b, D, s);
+  return launch_status();
+}
+
+int coda_baseline_rope(const uint16_t* h, const float* cos_t, const float* sin_t, int M, int n_q, int n_k, int n_v,
+                       int head_dim, int seq_len, int pos_offset, uint16_t* out, void* stream) {
+  CODA_TRY(check_rows(M));
+  if (head_dim < 8 || head_dim % 8 != 0) return CODA_ERR_SHAPE;
+  if (n_q < 0 || n_k < 0 || n_v < 0 || n_q % head_dim || n_k % head_dim || n_v % head_dim) return CODA_ERR_SHAPE;
+  const long long N = (long long)n_q + n_k + n_v;
+  if (N < 8 || N > kMaxDim) return CODA_ERR_SHAPE;
+  if (seq_len < 1 || pos_offset < 0) return CODA_ERR_ARG;
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(h);
+  CODA_NONNULL(cos_t);
+  CODA_NONNULL(sin_t);
+  CODA_NONNULL(out);
+  CODA_ALIGN16(h);
+  CODA_ALIGN16(out);
+  if (!aligned(cos_t, 16) || !aligned(sin_t, 16)) return CODA_ERR_ALIGN;
+  const long long n = (long long)M * (N / 8);
+  hipLaunchKernelGGL(rope_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, as_stream(stream), h, cos_t, sin_t, M,
+                     (int)N, n_q + n_k, head_dim, seq_len, pos_offset, out);
+  return launch_status();
+}
+
+int coda_baseline_swiglu(const uint16_t* h, int M, int F, uint16_t* out, void* stream) {
+  CODA_TRY(check_rows(M));
+  if (F < 8 || F % 8 != 0 || 2LL * F > kMaxDim) return CODA_ERR_SHAPE;
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(h);
+  CODA_NONNULL(out);
+  CODA_ALIGN16(h);
+  CODA_ALIGN16(out);
+  const long long n = (long long)M * (F / 4);
+  hipLaunchKernelGGL(swiglu_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, as_stream(stream), h, M, F, out);
+  return launch_status();
+}
+
+int coda_baseline_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  CODA_NONNULL(src);
+  CODA_NONNULL(dst);
+  if (bytes <= 0 || bytes % 16 != 0) return CODA_ERR_SHAPE;
+  CODA_ALIGN16(src);
+  CODA_ALIGN16(dst);
+  const long long n16 = bytes / 16;
+  const unsigned grid = (unsigned)std::min<long long>(blocks_for(n16, 256), 256LL * 16);
+  hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, as_stream(stream), (const u32x4_t*)src, (u32x4_t*)dst,
+                     n16);
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,213 @@
+// C-ABI entry points of the fused GEMM-epilogue programs (declared in coda.h).
+#include "coda_abi.hpp"
+#include "coda_gemm.hpp"
+
+using namespace coda;
+
+int coda_rowstat_reduce_impl(const float* partials, int M, int nb, int d, float eps, int mode,
+                             float* out, hipStream_t stream);
+
+namespace {
+
+template <bool kWKN, class Epi>
+int launch_gemm(const GemmProblem& p, const typename Epi::Args& ea, hipStream_t stream) {
+  const int grid = gemm_grid(p.M, p.N);
+  hipLaunchKernelGGL((gemm_epilogue_kernel<kWKN, Epi>), dim3(grid), dim3(kThreads), 0, stream, p, ea);
+  return launch_status();
+}
+
+// Shape rules first; an empty batch (M == 0) needs no buffers at all, so pointers are
+// checked only when there is work to do.
+int check_gemm1(const uint16_t* x, const uint16_t* w0, const uint16_t* z, const uint16_t* gamma, int M,
+                int K, int D, uint16_t* h1, uint16_t* h2, float* partials) {
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(K));
+  CODA_TRY(check_depth_or_width(D));
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(x);
+  CODA_NONNULL(w0);
+  CODA_NONNULL(z);
+  CODA_NONNULL(gamma);
+  CODA_NONNULL(h1);
+  CODA_NONNULL(h2);
+  CODA_NONNULL(partials);
+  CODA_ALIGN16(x);
+  CODA_ALIGN16(w0);
+  CODA_ALIGN16(z);
+  CODA_ALIGN16(gamma);
+  CODA_ALIGN16(h1);
+  CODA_ALIGN16(h2);
+  if (!aligned(partials, 4)) return CODA_ERR_ALIGN;
+  return CODA_OK;
+}
+
+int check_gemm2(const uint16_t* h2, const uint16_t* w1, const float* r, int M, int D, int N1, uint16_t* y) {
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(D));
+  CODA_TRY(check_depth_or_width(N1));
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(h2);
+  CODA_NONNULL(w1);
+  CODA_NONNULL(r);
+  CODA_NONNULL(y);
+  CODA_ALIGN16(h2);
+  CODA_ALIGN16(w1);
+  CODA_ALIGN16(y);
+  if (!aligned(r, 4)) return CODA_ERR_ALIGN;
+  return CODA_OK;
+}
+
+int run_gemm1(const uint16_t* x, const uint16_t* w0, const uint16_t* z, const uint16_t* gamma, int M, int K,
+              int D, uint16_t* h1, uint16_t* h2, float* partials, hipStream_t s) {
+  const GemmProblem p{x, w0, M, D, K};
+  const EpiResidualRmsPartials::Args ea{z, gamma, h1, h2, partials, (D + kBN - 1) / kBN};
+  return launch_gemm<true, EpiResidualRmsPartials>(p, ea, s);
+}
+
+int run_gemm2(const uint16_t* h2, const uint16_t* w1, const float* r, int M, int D, int N1, uint16_t* y,
+              hipStream_t s) {
+  const GemmProblem p{h2, w1, M, N1, D};
+  const EpiRowScale::Args ea{r, y};
+  return launch_gemm<true, EpiRowScale>(p, ea, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* coda_status_string(int status) {
+  switch (status) {
+    case CODA_OK: return "CODA_OK";
+    case CODA_ERR_NULL: return "CODA_ERR_NULL: a required pointer is NULL";
+    case CODA_ERR_SHAPE: return "CODA_ERR_SHAPE: a size violates the shape rules";
+    case CODA_ERR_ALIGN: return "CODA_ERR_ALIGN: a pointer is misaligned";
+    case CODA_ERR_WORKSPACE: return "CODA_ERR_WORKSPACE: workspace too small";
+    case CODA_ERR_HIP: return "CODA_ERR_HIP: a HIP launch failed";
+    case CODA_ERR_ARG: return "CODA_ERR_ARG: invalid argument";
+    default: return "unknown status";
+  }
+}
+
+int coda_abi_version(void) { return 100; }
+
+int coda_rowstat_num_partials(int width, int* nb) {
+  CODA_NONNULL(nb);
+  if (width < 1) return CODA_ERR_SHAPE;
+  *nb = (width + CODA_PARTIAL_TILE_N - 1) / CODA_PARTIAL_TILE_N;
+  return CODA_OK;
+}
+
+int coda_gemm_residual_rmsnorm_partials(const uint16_t* x, const uint16_t* w0, const uint16_t* z,
+                                        const uint16_t* gamma, int M, int K, int D, uint16_t* h1,
+                                        uint16_t* h2, float* partials, void* stream) {
+  CODA_TRY(check_gemm1(x, w0, z, gamma, M, K, D, h1, h2, partials));
+  if (M == 0) return CODA_OK;
+  return run_gemm1(x, w0, z, gamma, M, K, D, h1, h2, partials, as_stream(stream));
+}
+
+int coda_gemm_rowscale(const uint16_t* h2, const uint16_t* w1, const float* r, int M, int D, int N1,
+                       uint16_t* y, void* stream) {
+  CODA_TRY(check_gemm2(h2, w1, r, M, D, N1, y));
+  if (M == 0) return CODA_OK;
+  return run_gemm2(h2, w1, r, M, D, N1, y, as_stream(stream));
+}
+
+int coda_gemm_rmsnorm_fwd(const uint16_t* x, const uint16_t* w0, const uint16_t* z, const uint16_t* gamma,
+                          const uint16_t* w1, int M, int K, int D, int N1, float eps, uint16_t* h1,
+                          uint16_t* h2, float* partials, float* r, uint16_t* y, void* stream) {
+  if (!(eps >= 0.0f) || !(eps < __builtin_huge_valf())) return CODA_ERR_ARG;
+  CODA_TRY(check_gemm1(x, w0, z, gamma, M, K, D, h1, h2, partials));
+  CODA_TRY(check_gemm2(h2, w1, r, M, D, N1, y));
+  if (M == 0) return CODA_OK;
+  const hipStream_t s = as_stream(stream);
+  CODA_TRY(run_gemm1(x, w0, z, gamma, M, K, D, h1, h2, partials, s));
+  CODA_TRY(coda_rowstat_reduce_impl(partials, M, (D + kBN - 1) / kBN, D, eps, CODA_ROWSTAT_RSQRT_MEAN_EPS, r, s));
+  return run_gemm2(h2, w1, r, M, D, N1, y, s);
+}
+
+int coda_gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K,
+                   int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset, uint16_t* out,
+                   void* stream) {
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(K));
+  if (head_dim < 8 || head_dim % 8 != 0 || head_dim > kMaxDim) return CODA_ERR_SHAPE;
+  if (n_q < 0 || n_k < 0 || n_v < 0 || n_q % head_dim || n_k % head_dim || n_v % head_dim) return CODA_ERR_SHAPE;
+  const long long N = (long long)n_q + n_k + n_v;
+  if (N < 8 || N > kMaxDim) return CODA_ERR_SHAPE;
+  if (seq_len < 1 || pos_offset < 0) return CODA_ERR_ARG;
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(x);
+  CODA_NONNULL(w);
+  CODA_NONNULL(cos_t);
+  CODA_NONNULL(sin_t);
+  CODA_NONNULL(out);
+  CODA_ALIGN16(x);
+  CODA_ALIGN16(w);
+  CODA_ALIGN16(out);
+  if (!aligned(cos_t, 8) || !aligned(sin_t, 8)) return CODA_ERR_ALIGN;
+  const GemmProblem p{x, w, M, (int)N, K};
+  const EpiRope::Args ea{cos_t, sin_t, out, n_q + n_k, head_dim, seq_len, pos_offset};
+  return launch_gemm<true, EpiRope>(p, ea, as_stream(stream));
+}
+
+int coda_gemm_swiglu(const uint16_t* x, const uint16_t* w, int M, int K, int F, uint16_t* out, void* stream) {
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(K));
+  if (F < 8 || F % 8 != 0 || 2LL * F > kMaxDim) return CODA_ERR_SHAPE;
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(x);
+  CODA_NONNULL(w);
+  CODA_NONNULL(out);
+  CODA_ALIGN16(x);
+  CODA_ALIGN16(w);
+  CODA_ALIGN16(out);
+  const GemmProblem p{x, w, M, 2 * F, K};
+  const EpiSwiGLU::Args ea{out, F};
+  return launch_gemm<true, EpiSwiGLU>(p, ea, as_stream(stream));
+}
+
+int coda_gemm_rmsnorm_bwd_stats(const uint16_t* dy, const uint16_t* w1, const uint16_t* h2, int M, int D, int N,
+                                uint16_t* dh2, float* partials, float* s, void* stream) {
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(D));
+  CODA_TRY(check_depth_or_width(N));
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(dy);
+  CODA_NONNULL(w1);
+  CODA_NONNULL(h2);
+  CODA_NONNULL(dh2);
+  CODA_NONNULL(partials);
+  CODA_NONNULL(s);
+  CODA_ALIGN16(dy);
+  CODA_ALIGN16(w1);
+  CODA_ALIGN16(h2);
+  CODA_ALIGN16(dh2);
+  if (!aligned(partials, 4) || !aligned(s, 4)) return CODA_ERR_ALIGN;
+  const hipStream_t st = as_stream(stream);
+  // dy [M, N] times W1^T: depth = N, output width = D, W1 [D, N] is the NK layout.
+  const GemmProblem p{dy, w1, M, D, N};
+  const int nb = (D + kBN - 1) / kBN;
+  const EpiDotRowPartials::Args ea{h2, dh2, partials, nb};
+  CODA_TRY((launch_gemm<false, EpiDotRowPartials>(p, ea, st)));
+  return coda_rowstat_reduce_impl(partials, M, nb, D, 0.0f, CODA_ROWSTAT_MEAN, s, st);
+}
+
+int coda_baseline_gemm(const uint16_t* a, const uint16_t* b, int M, int K, int N, int b_kn, uint16_t* c,
+                       void* stream) {
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(K));
+  CODA_TRY(check_depth_or_width(N));
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(a);
+  CODA_NONNULL(b);
+  CODA_NONNULL(c);
+  CODA_ALIGN16(a);
+  CODA_ALIGN16(b);
+  CODA_ALIGN16(c);
+  const GemmProblem p{a, b, M, N, K};
+  const EpiStore::Args ea{c};
+  if (b_kn) return launch_gemm<true, EpiStore>(p, ea, as_stream(stream));
+  return launch_gemm<false, EpiStore>(p, ea, as_stream(stream));
+}
+
+}  // extern "C"
