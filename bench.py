@@ -310,6 +310,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the plain 1 GiB copy kernel (reference for HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused GEMM-epilogue path is row-independent and "
@@ -322,6 +324,14 @@ def main():
         sys.exit(1)
     coda.lib()
     log(f"device: {torch.cuda.get_device_name(0)}")
+    if args.copy_calibration:
+        src = torch.ones((1 << 29,), dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            coda.coda_baseline_copy(src, dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": src.numel() * 2, "launches": args.steps}), flush=True)
+        return
     res, bufs = headline(args, coda, torch)
     log(f"headline: {res['value']} TFLOP/s, {res['ms_per_step']} ms/step")
     if not args.headline_only:

@@ -5,9 +5,9 @@
 // contiguous), W either [K, N] row-major ("KN", features contiguous: the forward
 // projections) or [N, K] row-major ("NK", depth contiguous: the grad GEMM dY W1^T).
 //
-// Workgroup tile: 256 tokens x 256 features x 64 depth per step, 256 threads = 4 waves
-// in a 2 x 2 arrangement, each wave owning 128 tokens x 128 features = 4 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16 (16 fp32 accumulators per lane per block).
+// Workgroup tile: 256 tokens x 256 features, 256 threads = 4 waves (one per SIMD) in a
+// 2 x 2 arrangement, each wave owning 128 tokens x 128 features = 4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane, held in AGPRs).
 //
 // Transposed MFMA formulation. The MFMA "A" operand (rows of the MFMA output) is the
 // W slice, so MFMA rows are FEATURES; the "B" operand is the X slice, so MFMA columns
@@ -17,12 +17,21 @@
 // lane's registers, and a row statistic is an in-lane sum plus one exchange between
 // the two 32-lane halves.
 //
-// LDS: two stages of [X tile 256x64 | W tile 256x64] bf16 (depth contiguous, 128 B per
-// row, 16-byte chunks XOR-swizzled per row), 128 KiB. X and NK-W tiles are copied
-// chunk for chunk; a KN-W tile is transposed in registers (8x8 bf16 blocks with
-// v_perm_b32) on its way to LDS so both operands are depth-contiguous for the MFMA.
-// Global loads use raw buffer descriptors: rows past M, depth past K and columns past
-// N read as zero, so ragged edges need no special path.
+// Data movement. Both operand tiles go from HBM straight into LDS with
+// buffer_load_dwordx4 ... lds (no register staging), through a ring of 4 LDS stages of
+// 32 depth each, so three depth-steps are in flight while one is consumed. X and NK-W
+// tiles are stored depth-contiguous ([row][32] bf16, 64 B per row); a KN-W tile keeps
+// its natural [32][256] layout and is transposed on the way out of LDS by
+// ds_read_b64_tr_b16 into the depth-contiguous MFMA operand. All tiles XOR-swizzle
+// their 16-byte chunks per row so that both the DMA writes and the operand reads are
+// free of bank conflicts. Raw buffer descriptors make rows past M, depth past K and
+// columns past N read as zero, so ragged edges need no special path.
+//
+// Pipeline of one depth-step (stage S), per wave:
+//   read the k16-step 1 operands of S | MFMAs of k16-step 0 of S |
+//   wait for this thread's loads of stage S+1, barrier (stage S+1 complete for every
+//   wave, stage S-1 no longer read by anyone) | issue the loads of stage S+3 into the
+//   slot of S-1 | read the k16-step 0 operands of S+1 | MFMAs of k16-step 1 of S.
 #pragma once
 
 #include "coda_common.hpp"
@@ -31,16 +40,16 @@ namespace coda {
 
 constexpr int kBM = 256;       // tokens per workgroup tile
 constexpr int kBN = 256;       // features per workgroup tile (== CODA_PARTIAL_TILE_N)
-constexpr int kBK = 64;        // depth per main-loop step
+constexpr int kBK = 32;        // depth per LDS stage
+constexpr int kStages = 4;     // LDS ring depth
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kTileBytes = kBM * kBK * 2;    // one operand tile: 32 KiB
-constexpr int kStageBytes = 2 * kTileBytes;  // X tile + W tile
+constexpr int kTileBytes = kBM * kBK * 2;    // one operand tile per stage: 16 KiB
+constexpr int kLoadsPerStage = 8;            // 16-byte DMA loads per thread per stage
 constexpr int kStgPitch = 132;               // epilogue staging row pitch, bf16 elements
 constexpr int kStgWaveBytes = 128 * kStgPitch * 2;
-constexpr int kRedOff = 4 * kStgWaveBytes;   // row-partial exchange area
-constexpr int kLdsBytes = kRedOff + 4 * 128 * 4;
-static_assert(kLdsBytes >= 2 * kStageBytes, "LDS must hold both main-loop stages");
-static_assert(kLdsBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
+constexpr int kStageBytes = kStgWaveBytes > 2 * kTileBytes ? kStgWaveBytes : 2 * kTileBytes;
+constexpr int kRedBytes = 4 * 128 * 4;
+static_assert(kStages * kStageBytes + kRedBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
 
 struct GemmProblem {
   const uint16_t* x;  // [M, K]
@@ -48,13 +57,27 @@ struct GemmProblem {
   int M, N, K;
 };
 
-// Row swizzle of the 16-byte chunks of a 128-byte LDS row. Consecutive rows (MFMA
-// operand reads) and rows 8 apart (transposed W writes) land on distinct banks.
-__device__ __forceinline__ uint32_t swz(int row) {
-  return (uint32_t)(((row >> 1) & 7) ^ ((row & 1) << 2) ^ ((row >> 3) & 7));
+// LDS of one workgroup: four stage slots (each also serves one wave's epilogue staging
+// block) and the row-partial exchange area. Separate objects let the compiler tell
+// the DMA writes into one slot from operand reads of another.
+struct LdsRing {
+  char* slot[kStages];
+  float* red;
+};
+
+// Swizzle of the four 16-byte chunks of a depth-contiguous 64-byte row (X and NK-W
+// tiles): operand reads hit 8 consecutive rows (32 banks) or 16 (64 banks) at one
+// logical chunk; rows of equal parity (resp. equal residue mod 4) differ in bank line.
+__device__ __forceinline__ uint32_t swz_k(int row) { return (uint32_t)(((row >> 1) ^ (row >> 3)) & 3); }
+__device__ __forceinline__ uint32_t krow_off(int row, int chunk) {
+  return ((uint32_t)row << 6) | (((uint32_t)chunk ^ swz_k(row)) << 4);
 }
-__device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
-  return ((uint32_t)row << 7) | (((uint32_t)chunk ^ swz(row)) << 4);
+// Swizzle of the 32 chunks of a 512-byte KN-W row: a transposed read touches 4
+// consecutive depth rows x 2 (or 4) chunks; rows r = 0..3 (mod 4) XOR with 0, 6, 10,
+// 12, which spreads those 8 (16) chunks over distinct banks.
+__device__ __forceinline__ uint32_t swz_n(int row) { return (0xCA60u >> (4 * (row & 3))) & 0xFu; }
+__device__ __forceinline__ uint32_t nrow_off(int row, int chunk) {
+  return ((uint32_t)row << 9) | (((uint32_t)chunk ^ swz_n(row)) << 4);
 }
 
 // Workgroup -> output tile. Workgroups are dispatched round-robin over the 8 XCDs, so
@@ -76,101 +99,185 @@ __device__ __forceinline__ void tile_coords(int M, int N, int& m0, int& n0) {
   n0 = (rem / gm) * kBN;
 }
 
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor as four SGPR words (for the inline-asm LDS DMA below).
+__device__ __forceinline__ i32x4_t rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4_t r;
+  r.x = (int)(uint32_t)a;
+  r.y = (int)(uint32_t)(a >> 32);  // stride 0, no swizzle
+  r.z = (int)bytes;
+  r.w = (int)kBufferWord3;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// One 16-byte-per-lane DMA from HBM into LDS: lane i's 16 bytes land at
+// lds_base + 16 i. Issued from inline asm so that the compiler neither reorders LDS
+// accesses across it nor inserts its own conservative vmcnt waits; completion is
+// tracked explicitly with wait_vmcnt before the barrier that publishes a stage.
+__device__ __forceinline__ void dma16(const i32x4_t& rsrc, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(N): wait until at most N vector-memory loads of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8_t read_tr_pair(const char* p0, const char* p1) {
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p0));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p1));
+  const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 template <bool kWKN>
-__device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int n0,
-                                              char* __restrict__ smem, f32x16_t (&acc)[4][4]) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int M = p.M, N = p.N, K = p.K;
+struct Mainloop {
+  // per-thread DMA descriptors
+  i32x4_t xrs, wrs_nk;
+  uint32_t wave_u;       // wave index, wave-uniform (SGPR)
+  uint32_t x_off[4];     // byte offsets of this lane's X chunks (depth 0 of the tile)
+  uint32_t x_kchunk[4];  // logical depth chunk (0..3) of each X load
+  uint32_t w_off[4];     // KN: offset within the stage's depth rows; NK: like x_off
+  uint32_t w_kchunk[4];
+  bool w_col_ok[4];
+  const uint16_t* wbase;
+  int M, N, K, m0, n0;
+  // operand read offsets within a slot
+  uint32_t xr_off[2];        // per k16-step (j-th block adds j*32 rows)
+  uint32_t wr_off[2][4][2];  // KN: per k16-step, n-block, half; NK: [ks][i][0]
 
-  // X tile loads: thread -> rows (tid >> 3) + 32 i, 16-byte chunk (tid & 7).
-  const int lr = tid >> 3, lc = tid & 7;
-  const int x_rows = min(kBM, M - m0);
-  const __amdgpu_buffer_rsrc_t xrs =
-      make_rsrc(p.x + (size_t)m0 * K, (uint32_t)x_rows * (uint32_t)K * 2u);
-  const uint32_t rstride = (uint32_t)K * 2u;
-  const uint32_t x_off0 = (uint32_t)lr * rstride + (uint32_t)lc * 16u;
-
-  // NK-W tile loads: same pattern as X over feature rows.
-  const __amdgpu_buffer_rsrc_t wrs_nk =
-      kWKN ? make_rsrc(p.w, 0u)
-           : make_rsrc(p.w + (size_t)n0 * K, (uint32_t)min(kBN, N - n0) * (uint32_t)K * 2u);
-  // KN-W tile loads: thread -> depth rows 8*(tid>>5) + i, features 8*(tid&31) .. +7.
-  const int kb = tid >> 5, nb8 = tid & 31;
-  const bool kn_col_ok = n0 + 8 * nb8 < N;
-  const uint32_t kn_off0 = ((uint32_t)(8 * kb) * (uint32_t)N + (uint32_t)(8 * nb8)) * 2u;
-  const uint32_t kn_rstride = (uint32_t)N * 2u;
-
-  u32x4_t xr[8], wr[8];
-
-  auto load = [&](int k0) {
-    const uint32_t koff = (uint32_t)k0 * 2u;
-    const bool kx_ok = k0 + lc * 8 < K;
+  __device__ __forceinline__ void init(const GemmProblem& p, int m0_, int n0_) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    wave_u = (uint32_t)wave;
+    M = p.M;
+    N = p.N;
+    K = p.K;
+    m0 = m0_;
+    n0 = n0_;
+    wbase = p.w;
+    const uint32_t kb = (uint32_t)K * 2u;
+    xrs = rsrc_words(p.x + (size_t)m0 * K, (uint32_t)min(kBM, M - m0) * kb);
+    wrs_nk = kWKN ? rsrc_words(p.w, 0u) : rsrc_words(p.w + (size_t)n0 * K, (uint32_t)min(kBN, N - n0) * kb);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      xr[i] = buffer_load_16(xrs, kx_ok ? x_off0 + (uint32_t)i * 32u * rstride + koff : kOutOfRange);
+    for (int j = 0; j < 4; ++j) {
+      // X (and NK-W): instruction j of wave w fills rows (4w + j)*16 .. +15 of the tile
+      const int row = (wave * 4 + j) * 16 + (lane >> 2);
+      const uint32_t c = (uint32_t)(lane & 3) ^ swz_k(row);
+      x_kchunk[j] = c;
+      x_off[j] = (uint32_t)row * kb + c * 16u;
+      if constexpr (kWKN) {
+        // KN-W: instruction j of wave w fills depth rows (4w + j)*2 .. +1
+        const int wrow = (wave * 4 + j) * 2 + (lane >> 5);
+        const uint32_t wc = (uint32_t)(lane & 31) ^ swz_n(wrow);
+        w_col_ok[j] = n0 + 8 * (int)wc < N;
+        w_off[j] = ((uint32_t)wrow * (uint32_t)N + 8u * wc) * 2u;
+        w_kchunk[j] = (uint32_t)wrow;  // depth row within the stage
+      } else {
+        w_off[j] = x_off[j];
+        w_kchunk[j] = c;
+        w_col_ok[j] = true;
+      }
+    }
+    const int r32 = lane & 31, hs = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      xr_off[ks] = krow_off(wm * 128 + r32, 2 * ks + hs);
+      if constexpr (kWKN) {
+        const int g = lane >> 4, s = lane & 15, e = s >> 2, q = s & 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int nb = wn * 128 + i * 32 + (g & 1) * 16 + 4 * q;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int row = ks * 16 + (g >> 1) * 8 + 4 * h + e;
+            wr_off[ks][i][h] = kTileBytes + nrow_off(row, nb >> 3) + (uint32_t)((nb >> 2) & 1) * 8u;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          wr_off[ks][i][0] = kTileBytes + krow_off(wn * 128 + i * 32 + r32, 2 * ks + hs);
+          wr_off[ks][i][1] = 0;
+        }
+      }
+    }
+  }
+
+  // Issue the 8 DMA loads of depth-step kt into `slot`.
+  __device__ __forceinline__ void issue(char* slot, int kt) const {
+    const int k0 = kt * kBK;
+    const uint32_t xs = lds_addr(slot) + wave_u * 4096u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = k0 + 8 * (int)x_kchunk[j] < K;
+      dma16(xrs, xs + j * 1024u, ok ? x_off[j] + (uint32_t)k0 * 2u : kOutOfRange);
+    }
+    const uint32_t ws = lds_addr(slot) + (uint32_t)kTileBytes + wave_u * 4096u;
     if constexpr (kWKN) {
       const int krows = min(kBK, K - k0);
-      const __amdgpu_buffer_rsrc_t wrs =
-          make_rsrc(p.w + (size_t)k0 * N + n0, ((uint32_t)krows * (uint32_t)N - (uint32_t)n0) * 2u);
+      const i32x4_t wrs =
+          rsrc_words(wbase + (size_t)k0 * N + n0, ((uint32_t)krows * (uint32_t)N - (uint32_t)n0) * 2u);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        wr[i] = buffer_load_16(wrs, kn_col_ok ? kn_off0 + (uint32_t)i * kn_rstride : kOutOfRange);
+      for (int j = 0; j < 4; ++j) dma16(wrs, ws + j * 1024u, w_col_ok[j] ? w_off[j] : kOutOfRange);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        wr[i] = buffer_load_16(wrs_nk, kx_ok ? x_off0 + (uint32_t)i * 32u * rstride + koff : kOutOfRange);
-    }
-  };
-
-  auto store = [&](char* stage) {
-    char* xs = stage;
-    char* ws = stage + kTileBytes;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *(u32x4_t*)(xs + tile_off(lr + 32 * i, lc)) = xr[i];
-    if constexpr (kWKN) {
-      // 8x8 bf16 transpose: wr[i] holds depth 8kb+i for features 8nb8..8nb8+7; write
-      // feature row 8nb8+j, chunk kb = depth 8kb..8kb+7 in order.
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int d = j >> 1;
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        u32x4_t o;
-        o.x = __builtin_amdgcn_perm(wr[1][d], wr[0][d], sel);
-        o.y = __builtin_amdgcn_perm(wr[3][d], wr[2][d], sel);
-        o.z = __builtin_amdgcn_perm(wr[5][d], wr[4][d], sel);
-        o.w = __builtin_amdgcn_perm(wr[7][d], wr[6][d], sel);
-        *(u32x4_t*)(ws + tile_off(8 * nb8 + j, kb)) = o;
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = k0 + 8 * (int)w_kchunk[j] < K;
+        dma16(wrs_nk, ws + j * 1024u, ok ? w_off[j] + (uint32_t)k0 * 2u : kOutOfRange);
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) *(u32x4_t*)(ws + tile_off(lr + 32 * i, lc)) = wr[i];
     }
-  };
+  }
 
-  const int r32 = lane & 31, hsel = lane >> 5;
-  auto compute = [&](const char* stage) {
-    const char* xs = stage;
-    const char* ws = stage + kTileBytes;
+  __device__ __forceinline__ void read(const char* slot, int ks, bf16x8_t (&a)[4], bf16x8_t (&b)[4]) const {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8_t a[4], b[4];
+    for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8_t*)(slot + xr_off[ks] + j * 32 * 64);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *(const bf16x8_t*)(ws + tile_off(wn * 128 + i * 32 + r32, 2 * ks + hsel));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        b[i] = *(const bf16x8_t*)(xs + tile_off(wm * 128 + i * 32 + r32, 2 * ks + hsel));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (kWKN)
+        a[i] = read_tr_pair(slot + wr_off[ks][i][0], slot + wr_off[ks][i][1]);
+      else
+        a[i] = *(const bf16x8_t*)(slot + wr_off[ks][i][0]);
     }
-  };
+  }
+};
 
+__device__ __forceinline__ void mfma_block(f32x16_t (&acc)[4][4], const bf16x8_t (&a)[4], const bf16x8_t (&b)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// Wait until this thread's loads of the step after `kt` have landed; `ahead` is how many
+// later steps (0..2) have been issued behind it.
+__device__ __forceinline__ void wait_next(int ahead) {
+  if (ahead >= 2)
+    wait_vmcnt<2 * kLoadsPerStage>();
+  else if (ahead == 1)
+    wait_vmcnt<kLoadsPerStage>();
+  else
+    wait_vmcnt<0>();
+}
+
+template <bool kWKN>
+__device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int n0, const LdsRing& lds,
+                                              f32x16_t (&acc)[4][4]) {
+  Mainloop<kWKN> ml;
+  ml.init(p, m0, n0);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -178,17 +285,42 @@ __device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int KT = (K + kBK - 1) / kBK;
-  load(0);
-  store(smem);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool more = kt + 1 < KT;
-    if (more) load((kt + 1) * kBK);
-    compute(smem + (kt & 1) * kStageBytes);
-    if (more) store(smem + ((kt + 1) & 1) * kStageBytes);
-    __syncthreads();
+  const int KT = (p.K + kBK - 1) / kBK;
+  // prologue: steps 0, 1, 2 in flight; wait for step 0
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < KT) ml.issue(lds.slot[s], s);
+  wait_next(min(KT - 1, 2) );  // step 0 landed (steps 1, 2 may still fly)
+  __builtin_amdgcn_s_barrier();
+
+  bf16x8_t a0[4], b0[4], a1[4], b1[4];
+  ml.read(lds.slot[0], 0, a0, b0);
+
+  auto step = [&](const int S, const int kt) {
+    const char* cur = lds.slot[S];
+    ml.read(cur, 1, a1, b1);
+    mfma_block(acc, a0, b0);
+    if (kt + 1 < KT) {
+      wait_next(min(KT - 1, kt + 2) - (kt + 1));
+      __builtin_amdgcn_s_barrier();
+      if (kt + 3 < KT) ml.issue(lds.slot[(S + 3) % kStages], kt + 3);
+      ml.read(lds.slot[(S + 1) % kStages], 0, a0, b0);
+    }
+    mfma_block(acc, a1, b1);
+  };
+
+  int kt = 0;
+  for (; kt + kStages <= KT; kt += kStages) {
+    step(0, kt);
+    step(1, kt + 1);
+    step(2, kt + 2);
+    step(3, kt + 3);
   }
+  if (kt < KT) step(0, kt);
+  if (kt + 1 < KT) step(1, kt + 1);
+  if (kt + 2 < KT) step(2, kt + 2);
+  // all operand reads are done before the slots are reused by the epilogue
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------------------------
@@ -209,7 +341,9 @@ struct EpiLane {
   __device__ __forceinline__ int scol(int i, int g) const { return 32 * i + 8 * g + 4 * (lane >> 5); }
 };
 
-__device__ __forceinline__ char* stage_base(char* smem, int wave) { return smem + wave * kStgWaveBytes; }
+__device__ __forceinline__ char* stage_base(const LdsRing& lds, int wave) {
+  return wave == 0 ? lds.slot[0] : wave == 1 ? lds.slot[1] : wave == 2 ? lds.slot[2] : lds.slot[3];
+}
 
 __device__ __forceinline__ void stage_put8(char* stg, int r, int c, uint32_t lo, uint32_t hi) {
   u32x2_t v;
@@ -250,11 +384,11 @@ __device__ __forceinline__ void stage_flush(const char* stg, uint16_t* __restric
 // Combine per-lane row partials into one fp32 value per (token, 256-column tile) and
 // store it at partials[m * nb + tile]. Order is fixed: in-lane sum, the two 32-lane
 // halves, then wave wn = 0 plus wave wn = 1.
-__device__ __forceinline__ void store_row_partials(float (&part)[4], char* smem, const EpiLane& L,
+__device__ __forceinline__ void store_row_partials(float (&part)[4], const LdsRing& lds, const EpiLane& L,
                                                    float* __restrict__ partials, int nb, int M) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) part[j] += __shfl_xor(part[j], 32);
-  float* red = (float*)(smem + kRedOff);
+  float* red = lds.red;
   if (L.lane < 32) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) red[(L.wm * 2 + L.wn) * 128 + 32 * j + L.lane] = part[j];
@@ -280,9 +414,9 @@ struct EpiStore {
     uint16_t* out;
   };
   __device__ __forceinline__ static void apply(f32x16_t (&acc)[4][4], const Args& a, const GemmProblem& p,
-                                               int m0, int n0, char* smem) {
+                                               int m0, int n0, const LdsRing& lds) {
     const EpiLane L(m0, n0);
-    char* stg = stage_base(smem, L.wave);
+    char* stg = stage_base(lds, L.wave);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -308,10 +442,10 @@ struct EpiResidualRmsPartials {
     int nb;
   };
   __device__ __forceinline__ static void apply(f32x16_t (&acc)[4][4], const Args& a, const GemmProblem& p,
-                                               int m0, int n0, char* smem) {
+                                               int m0, int n0, const LdsRing& lds) {
     const EpiLane L(m0, n0);
     const int M = p.M, N = p.N;
-    char* stg = stage_base(smem, L.wave);
+    char* stg = stage_base(lds, L.wave);
     float part[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -352,7 +486,7 @@ struct EpiResidualRmsPartials {
       }
     __syncthreads();
     stage_flush<128>(stg, a.h2, (size_t)N, M, N, m0 + L.wm * 128, n0 + L.wn * 128, L.lane);
-    store_row_partials(part, smem, L, a.partials, a.nb, M);
+    store_row_partials(part, lds, L, a.partials, a.nb, M);
   }
 };
 
@@ -363,9 +497,9 @@ struct EpiRowScale {
     uint16_t* y;
   };
   __device__ __forceinline__ static void apply(f32x16_t (&acc)[4][4], const Args& a, const GemmProblem& p,
-                                               int m0, int n0, char* smem) {
+                                               int m0, int n0, const LdsRing& lds) {
     const EpiLane L(m0, n0);
-    char* stg = stage_base(smem, L.wave);
+    char* stg = stage_base(lds, L.wave);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int m = L.row(j);
@@ -394,9 +528,9 @@ struct EpiRope {
     int pos_offset;
   };
   __device__ __forceinline__ static void apply(f32x16_t (&acc)[4][4], const Args& a, const GemmProblem& p,
-                                               int m0, int n0, char* smem) {
+                                               int m0, int n0, const LdsRing& lds) {
     const EpiLane L(m0, n0);
-    char* stg = stage_base(smem, L.wave);
+    char* stg = stage_base(lds, L.wave);
     const int half = a.head_dim >> 1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -439,9 +573,9 @@ struct EpiSwiGLU {
     int F;  // output width (= N / 2)
   };
   __device__ __forceinline__ static void apply(f32x16_t (&acc)[4][4], const Args& a, const GemmProblem& p,
-                                               int m0, int n0, char* smem) {
+                                               int m0, int n0, const LdsRing& lds) {
     const EpiLane L(m0, n0);
-    char* stg = stage_base(smem, L.wave);
+    char* stg = stage_base(lds, L.wave);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -466,10 +600,10 @@ struct EpiDotRowPartials {
     int nb;
   };
   __device__ __forceinline__ static void apply(f32x16_t (&acc)[4][4], const Args& a, const GemmProblem& p,
-                                               int m0, int n0, char* smem) {
+                                               int m0, int n0, const LdsRing& lds) {
     const EpiLane L(m0, n0);
     const int M = p.M, N = p.N;
-    char* stg = stage_base(smem, L.wave);
+    char* stg = stage_base(lds, L.wave);
     float part[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -489,19 +623,24 @@ struct EpiDotRowPartials {
     }
     __syncthreads();
     stage_flush<128>(stg, a.dh2, (size_t)N, M, N, m0 + L.wm * 128, n0 + L.wn * 128, L.lane);
-    store_row_partials(part, smem, L, a.partials, a.nb, M);
+    store_row_partials(part, lds, L, a.partials, a.nb, M);
   }
 };
 
 template <bool kWKN, class Epi>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_epilogue_kernel(GemmProblem p, typename Epi::Args ea) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char slot0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char slot1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char slot2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char slot3[kStageBytes];
+  __shared__ __attribute__((aligned(16))) float red[kRedBytes / 4];
+  const LdsRing lds{{slot0, slot1, slot2, slot3}, red};
   int m0, n0;
   tile_coords(p.M, p.N, m0, n0);
   f32x16_t acc[4][4];
-  gemm_mainloop<kWKN>(p, m0, n0, smem, acc);
-  Epi::apply(acc, ea, p, m0, n0, smem);
+  gemm_mainloop<kWKN>(p, m0, n0, lds, acc);
+  Epi::apply(acc, ea, p, m0, n0, lds);
 }
 
 inline int gemm_grid(int M, int N) { return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN); }
