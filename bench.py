@@ -99,6 +99,12 @@ def headline(args, coda, torch):
         if ev is not None:
             ev[3].record()
 
+    # Clock settle: the MI355X ramps its clocks over the first tens of milliseconds of
+    # MFMA load, so untimed steps run for `--settle-s` seconds before the warm-up steps.
+    t_end = time.perf_counter() + args.settle_s
+    while time.perf_counter() < t_end:
+        step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -292,9 +298,10 @@ def cpu_baseline(target_s: float):
         O.gemm_rmsnorm_fwd(wl["x"], wl["w0"], wl["z"], wl["gamma"], wl["w1"], wl["eps"], rows=rows)
         return time.perf_counter() - t0
 
-    t = run(16)
-    n = int(min(M, max(16, 16 * target_s / max(t, 1e-3))))
-    t = run(n)
+    t = run(512)
+    n = int(min(M, max(512, 512 * target_s / max(t, 1e-3))))
+    if n != 512:
+        t = run(n)
     flops = 2.0 * n * K * D + 2.0 * n * D * N1
     return {"value": round(flops / t / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} of {M} rows of the same workload (all five fp64 outputs per row, incl. "
@@ -307,7 +314,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--reps", type=int, default=20, help="repetitions for the context measurements")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--settle-s", type=float, default=1.0, help="untimed clock-settle time before warm-up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
