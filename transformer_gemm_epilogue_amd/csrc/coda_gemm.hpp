@@ -5,9 +5,10 @@
 // contiguous), W either [K, N] row-major ("KN", features contiguous: the forward
 // projections) or [N, K] row-major ("NK", depth contiguous: the grad GEMM dY W1^T).
 //
-// Workgroup tile: 256 tokens x 256 features, 256 threads = 4 waves (one per SIMD) in a
-// 2 x 2 arrangement, each wave owning 128 tokens x 128 features = 4 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane, held in AGPRs).
+// Workgroup tile: 256 tokens x 256 features, 512 threads = 8 waves, two per SIMD, in a
+// 2 (tokens) x 4 (features) arrangement; each wave owns 128 tokens x 64 features = 2 x 4
+// blocks of v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane). While one wave of
+// a SIMD waits on a barrier or an LDS read, the other keeps the MFMA pipe busy.
 //
 // Transposed MFMA formulation. The MFMA "A" operand (rows of the MFMA output) is the
 // W slice, so MFMA rows are FEATURES; the "B" operand is the X slice, so MFMA columns
@@ -27,29 +28,39 @@
 // free of bank conflicts. Raw buffer descriptors make rows past M, depth past K and
 // columns past N read as zero, so ragged edges need no special path.
 //
-// Pipeline of one depth-step (stage S), per wave:
-//   read the k16-step 1 operands of S | MFMAs of k16-step 0 of S |
-//   wait for this thread's loads of stage S+1, barrier (stage S+1 complete for every
-//   wave, stage S-1 no longer read by anyone) | issue the loads of stage S+3 into the
-//   slot of S-1 | read the k16-step 0 operands of S+1 | MFMAs of k16-step 1 of S.
+// Schedule of one depth-step S (two k16 sub-steps), per wave:
+//   read the sub-step-1 operands of S | 8 MFMAs of sub-step 0 of S |
+//   wait for this thread's loads of S+1, barrier (S+1 complete for every wave, S-1 no
+//   longer read by anyone) | 8 MFMAs of sub-step 1 of S, interleaved one for one with
+//   the reads of sub-step 0 of S+1 and the DMA loads of S+3 into the slot of S-1.
+// The order is pinned with scheduling barriers; the code is straight-line (the DMA of
+// steps past the end only zero-fills a free slot) so the compiler's LDS wait counts
+// never make an MFMA wait for reads issued after its operands.
 #pragma once
 
 #include "coda_common.hpp"
 
 namespace coda {
 
-constexpr int kBM = 256;       // tokens per workgroup tile
-constexpr int kBN = 256;       // features per workgroup tile (== CODA_PARTIAL_TILE_N)
-constexpr int kBK = 32;        // depth per LDS stage
-constexpr int kStages = 4;     // LDS ring depth
-constexpr int kThreads = 256;  // 4 waves
-constexpr int kTileBytes = kBM * kBK * 2;    // one operand tile per stage: 16 KiB
-constexpr int kLoadsPerStage = 8;            // 16-byte DMA loads per thread per stage
-constexpr int kStgPitch = 132;               // epilogue staging row pitch, bf16 elements
+constexpr int kBM = 256;        // tokens per workgroup tile
+constexpr int kBN = 256;        // features per workgroup tile (== CODA_PARTIAL_TILE_N)
+constexpr int kBK = 32;         // depth per LDS stage
+constexpr int kStages = 4;      // LDS ring depth
+constexpr int kWaves = 8;       // two per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWavesN = 4;      // waves along features
+constexpr int kNI = 2;          // 32-feature MFMA blocks per wave
+constexpr int kMJ = 4;          // 32-token MFMA blocks per wave
+constexpr int kWaveN = 32 * kNI;  // features per wave (64)
+constexpr int kXJ = 16 / kWaves;  // 1 KiB DMA instructions per wave per operand per step
+constexpr int kLoadsPerStep = 2 * kXJ;  // 16-byte DMA loads per thread per step
+constexpr int kTileBytes = kBM * kBK * 2;  // one operand tile per stage: 16 KiB
+constexpr int kStgPitch = kWaveN + 4;      // epilogue staging row pitch, bf16 elements
 constexpr int kStgWaveBytes = 128 * kStgPitch * 2;
-constexpr int kStageBytes = kStgWaveBytes > 2 * kTileBytes ? kStgWaveBytes : 2 * kTileBytes;
-constexpr int kRedBytes = 4 * 128 * 4;
-static_assert(kStages * kStageBytes + kRedBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
+constexpr int kSlotBytes = 2 * kStgWaveBytes > 2 * kTileBytes ? 2 * kStgWaveBytes : 2 * kTileBytes;
+constexpr int kRedFloats = 2 * kWavesN * 128;
+static_assert(kStages * kSlotBytes + 4 * kRedFloats <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
+static_assert(kWaves == 2 * kWavesN && kWavesN * kWaveN == kBN, "wave layout covers the tile");
 
 struct GemmProblem {
   const uint16_t* x;  // [M, K]
@@ -57,9 +68,8 @@ struct GemmProblem {
   int M, N, K;
 };
 
-// LDS of one workgroup: four stage slots (each also serves one wave's epilogue staging
-// block) and the row-partial exchange area. Separate objects let the compiler tell
-// the DMA writes into one slot from operand reads of another.
+// LDS of one workgroup: four stage slots (each also holds two waves' epilogue staging
+// blocks) and the row-partial exchange area.
 struct LdsRing {
   char* slot[kStages];
   float* red;
@@ -105,8 +115,9 @@ __device__ __forceinline__ void tile_coords(int M, int N, int& m0, int& n0) {
 __device__ __forceinline__ int k_rotation(int KT) { return (int)((blockIdx.x % 8) * (KT / 8)); }
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
-// Raw buffer descriptor as four SGPR words (for the inline-asm LDS DMA below).
+// Raw buffer descriptor as four words (for the inline-asm LDS DMA below).
 __device__ __forceinline__ i32x4_t rsrc_words(const void* base, uint32_t bytes) {
   const uint64_t a = (uint64_t)(uintptr_t)base;
   i32x4_t r;
@@ -123,7 +134,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(
 // lds_base + 16 i. Issued from inline asm so that the compiler neither reorders LDS
 // accesses across it nor inserts its own conservative vmcnt waits; completion is
 // tracked explicitly with wait_vmcnt before the barrier that publishes a stage.
-__device__ __forceinline__ void dma16(const i32x4_t& rsrc, uint32_t lds_base, uint32_t voff) {
+__device__ __forceinline__ void dma16(const i32x4_t& rsrc_in, uint32_t lds_base, uint32_t voff) {
+  i32x4_t rsrc;  // the descriptor must live in SGPRs
+  rsrc.x = __builtin_amdgcn_readfirstlane(rsrc_in.x);
+  rsrc.y = __builtin_amdgcn_readfirstlane(rsrc_in.y);
+  rsrc.z = __builtin_amdgcn_readfirstlane(rsrc_in.z);
+  rsrc.w = __builtin_amdgcn_readfirstlane(rsrc_in.w);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds_base), "v"(voff), "s"(rsrc)
@@ -137,37 +153,28 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x8_t __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ bf16x8_t read_tr_pair(const char* p0, const char* p1) {
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p0));
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p1));
-  const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8_t, v);
-}
+typedef __attribute__((address_space(3))) const bf16x8_t* lds_b128_ptr;
+typedef __attribute__((address_space(3))) i16x4_t* lds_tr_ptr;
 
 template <bool kWKN>
 struct Mainloop {
-  // per-thread DMA descriptors
-  i32x4_t xrs, wrs_nk;
-  uint32_t wave_u;       // wave index, wave-uniform (SGPR)
-  uint32_t x_off[4];     // byte offsets of this lane's X chunks (depth 0 of the tile)
-  uint32_t x_kchunk[4];  // logical depth chunk (0..3) of each X load
-  uint32_t w_off[4];     // KN: offset within the stage's depth rows; NK: like x_off
-  uint32_t w_kchunk[4];
-  bool w_col_ok[4];
+  i32x4_t xrs, wrs_nk;    // descriptors of the tile's X rows and (NK) W rows
+  uint32_t wave_u;        // wave index, wave-uniform
+  uint32_t x_off[kXJ];    // byte offsets of this lane's X chunks (depth 0 of the tile)
+  uint32_t x_kchunk[kXJ]; // logical depth chunk (0..3) of each X load
+  uint32_t w_off[kXJ];    // KN: offset within the stage's depth rows; NK: like x_off
+  uint32_t w_kchunk[kXJ];
+  bool w_col_ok[kXJ];
   const uint16_t* wbase;
   int M, N, K, m0, n0;
-  int KT, kstart;  // depth steps and the rotated first step
-  // operand read offsets within a slot
-  uint32_t xr_off[2];        // per k16-step (j-th block adds j*32 rows)
-  uint32_t wr_off[2][4][2];  // KN: per k16-step, n-block, half; NK: [ks][i][0]
+  int KT, kstart;           // depth steps and the rotated first step
+  uint32_t xr_off[2];       // operand read offsets within a slot, per k16 sub-step
+  uint32_t wr_off[2][kNI][2];
 
   __device__ __forceinline__ void init(const GemmProblem& p, int m0_, int n0_) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
     wave_u = (uint32_t)wave;
     M = p.M;
     N = p.N;
@@ -181,19 +188,19 @@ struct Mainloop {
     xrs = rsrc_words(p.x + (size_t)m0 * K, (uint32_t)min(kBM, M - m0) * kb);
     wrs_nk = kWKN ? rsrc_words(p.w, 0u) : rsrc_words(p.w + (size_t)n0 * K, (uint32_t)min(kBN, N - n0) * kb);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // X (and NK-W): instruction j of wave w fills rows (4w + j)*16 .. +15 of the tile
-      const int row = (wave * 4 + j) * 16 + (lane >> 2);
+    for (int j = 0; j < kXJ; ++j) {
+      // X (and NK-W): instruction j of wave w fills rows (kXJ w + j)*16 .. +15 of the tile
+      const int row = (wave * kXJ + j) * 16 + (lane >> 2);
       const uint32_t c = (uint32_t)(lane & 3) ^ swz_k(row);
       x_kchunk[j] = c;
       x_off[j] = (uint32_t)row * kb + c * 16u;
       if constexpr (kWKN) {
-        // KN-W: instruction j of wave w fills depth rows (4w + j)*2 .. +1
-        const int wrow = (wave * 4 + j) * 2 + (lane >> 5);
+        // KN-W: instruction j of wave w fills depth rows (kXJ w + j)*2 .. +1
+        const int wrow = (wave * kXJ + j) * 2 + (lane >> 5);
         const uint32_t wc = (uint32_t)(lane & 31) ^ swz_n(wrow);
         w_col_ok[j] = n0 + 8 * (int)wc < N;
         w_off[j] = ((uint32_t)wrow * (uint32_t)N + 8u * wc) * 2u;
-        w_kchunk[j] = (uint32_t)wrow;  // depth row within the stage
+        w_kchunk[j] = (uint32_t)wrow;
       } else {
         w_off[j] = x_off[j];
         w_kchunk[j] = c;
@@ -205,10 +212,12 @@ struct Mainloop {
     for (int ks = 0; ks < 2; ++ks) {
       xr_off[ks] = krow_off(wm * 128 + r32, 2 * ks + hs);
       if constexpr (kWKN) {
+        // transposed read: in each 16-lane group, lane 4e+q points at depth row e of the
+        // group's 4 rows, features 4q..4q+3; lane i receives feature i of all 4 rows
         const int g = lane >> 4, s = lane & 15, e = s >> 2, q = s & 3;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int nb = wn * 128 + i * 32 + (g & 1) * 16 + 4 * q;
+        for (int i = 0; i < kNI; ++i) {
+          const int nb = wn * kWaveN + i * 32 + (g & 1) * 16 + 4 * q;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int row = ks * 16 + (g >> 1) * 8 + 4 * h + e;
@@ -217,105 +226,117 @@ struct Mainloop {
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          wr_off[ks][i][0] = kTileBytes + krow_off(wn * 128 + i * 32 + r32, 2 * ks + hs);
+        for (int i = 0; i < kNI; ++i) {
+          wr_off[ks][i][0] = kTileBytes + krow_off(wn * kWaveN + i * 32 + r32, 2 * ks + hs);
           wr_off[ks][i][1] = 0;
         }
       }
     }
   }
 
-  // Issue the 8 DMA loads of the kt-th depth step (rotated) into `slot`.
-  __device__ __forceinline__ void issue(char* slot, int kt) const {
-    const int ks = kt + kstart;
-    const int k0 = (ks >= KT ? ks - KT : ks) * kBK;
-    const uint32_t xs = lds_addr(slot) + wave_u * 4096u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+  // DMA load number j (0 .. kLoadsPerStep-1) of the kt-th depth step (rotated) into
+  // `slot`. Steps past the end (kt >= KT) issue out-of-range loads that only zero-fill
+  // a slot nobody reads.
+  __device__ __forceinline__ void issue_one(char* slot, int kt, int j) const {
+    const int ksr = kt + kstart;
+    const int k0 = (kt >= KT) ? K : (ksr >= KT ? ksr - KT : ksr) * kBK;
+    if (j < kXJ) {
+      const uint32_t xs = lds_addr(slot) + wave_u * (kXJ * 1024u);
       const bool ok = k0 + 8 * (int)x_kchunk[j] < K;
       dma16(xrs, xs + j * 1024u, ok ? x_off[j] + (uint32_t)k0 * 2u : kOutOfRange);
-    }
-    const uint32_t ws = lds_addr(slot) + (uint32_t)kTileBytes + wave_u * 4096u;
-    if constexpr (kWKN) {
-      const int krows = min(kBK, K - k0);
-      const i32x4_t wrs =
-          rsrc_words(wbase + (size_t)k0 * N + n0, ((uint32_t)krows * (uint32_t)N - (uint32_t)n0) * 2u);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dma16(wrs, ws + j * 1024u, w_col_ok[j] ? w_off[j] : kOutOfRange);
     } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool ok = k0 + 8 * (int)w_kchunk[j] < K;
-        dma16(wrs_nk, ws + j * 1024u, ok ? w_off[j] + (uint32_t)k0 * 2u : kOutOfRange);
+      const int jj = j - kXJ;
+      const uint32_t ws = lds_addr(slot) + (uint32_t)kTileBytes + wave_u * (kXJ * 1024u);
+      if constexpr (kWKN) {
+        const int krows = max(0, min(kBK, K - k0));
+        const i32x4_t wrs = rsrc_words(wbase + (size_t)min(k0, K - 1) * N + n0,
+                                       krows ? ((uint32_t)krows * (uint32_t)N - (uint32_t)n0) * 2u : 0u);
+        dma16(wrs, ws + jj * 1024u, w_col_ok[jj] ? w_off[jj] : kOutOfRange);
+      } else {
+        const bool ok = k0 + 8 * (int)w_kchunk[jj] < K;
+        dma16(wrs_nk, ws + jj * 1024u, ok ? w_off[jj] + (uint32_t)k0 * 2u : kOutOfRange);
       }
     }
   }
 
-  __device__ __forceinline__ void read(const char* slot, int ks, bf16x8_t (&a)[4], bf16x8_t (&b)[4]) const {
+  __device__ __forceinline__ void issue(char* slot, int kt) const {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8_t*)(slot + xr_off[ks] + j * 32 * 64);
+    for (int j = 0; j < kLoadsPerStep; ++j) issue_one(slot, kt, j);
+  }
+
+  __device__ __forceinline__ void read(const char* slot, int ks, bf16x8_t (&a)[kNI], bf16x8_t (&b)[kMJ]) const {
+    // Opaque, wave-uniform slot base: keeps the compiler from hoisting one address
+    // register per (slot, read) out of the loop.
+    uint32_t base = lds_addr(slot);
+    asm volatile("" : "+s"(base));
+    const uint32_t xb = base + xr_off[ks];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (kWKN)
-        a[i] = read_tr_pair(slot + wr_off[ks][i][0], slot + wr_off[ks][i][1]);
-      else
-        a[i] = *(const bf16x8_t*)(slot + wr_off[ks][i][0]);
+    for (int j = 0; j < kMJ; ++j) b[j] = *(lds_b128_ptr)(uintptr_t)(xb + j * 32 * 64);
+#pragma unroll
+    for (int i = 0; i < kNI; ++i) {
+      if constexpr (kWKN) {
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr_ptr)(uintptr_t)(base + wr_off[ks][i][0]));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr_ptr)(uintptr_t)(base + wr_off[ks][i][1]));
+        a[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else {
+        a[i] = *(lds_b128_ptr)(uintptr_t)(base + wr_off[ks][i][0]);
+      }
     }
   }
 };
 
-__device__ __forceinline__ void mfma_block(f32x16_t (&acc)[4][4], const bf16x8_t (&a)[4], const bf16x8_t (&b)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-}
-
-// Wait until this thread's loads of the step after `kt` have landed; `ahead` is how many
-// later steps (0..2) have been issued behind it.
-__device__ __forceinline__ void wait_next(int ahead) {
-  if (ahead >= 2)
-    wait_vmcnt<2 * kLoadsPerStage>();
-  else if (ahead == 1)
-    wait_vmcnt<kLoadsPerStage>();
-  else
-    wait_vmcnt<0>();
-}
-
 template <bool kWKN>
 __device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int n0, const LdsRing& lds,
-                                              f32x16_t (&acc)[4][4]) {
+                                              f32x16_t (&acc)[kNI][kMJ]) {
   Mainloop<kWKN> ml;
   ml.init(p, m0, n0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kNI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kMJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int KT = (p.K + kBK - 1) / kBK;
+  const int KT = ml.KT;
+  constexpr int kReads = kMJ + (kWKN ? 2 * kNI : kNI);  // LDS read instructions per k16 sub-step
+  constexpr int kMfma = kNI * kMJ;                      // MFMAs per k16 sub-step
+  constexpr int L = kLoadsPerStep;
+
   // prologue: steps 0, 1, 2 in flight; wait for step 0
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < KT) ml.issue(lds.slot[s], s);
-  wait_next(min(KT - 1, 2) );  // step 0 landed (steps 1, 2 may still fly)
+  for (int s = 0; s < kStages - 1; ++s) ml.issue(lds.slot[s], s);
+  wait_vmcnt<2 * L>();
   __builtin_amdgcn_s_barrier();
 
-  bf16x8_t a0[4], b0[4], a1[4], b1[4];
+  bf16x8_t a0[kNI], b0[kMJ], a1[kNI], b1[kMJ];
   ml.read(lds.slot[0], 0, a0, b0);
 
   auto step = [&](const int S, const int kt) {
-    const char* cur = lds.slot[S];
-    ml.read(cur, 1, a1, b1);
-    mfma_block(acc, a0, b0);
-    if (kt + 1 < KT) {
-      wait_next(min(KT - 1, kt + 2) - (kt + 1));
-      __builtin_amdgcn_s_barrier();
-      if (kt + 3 < KT) ml.issue(lds.slot[(S + 3) % kStages], kt + 3);
-      ml.read(lds.slot[(S + 1) % kStages], 0, a0, b0);
+    ml.read(lds.slot[S], 1, a1, b1);
+#pragma unroll
+    for (int i = 0; i < kNI; ++i)
+#pragma unroll
+      for (int j = 0; j < kMJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);  // sub-step-1 reads first
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);   // then the sub-step-0 MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<L>();  // this thread's loads of step kt+1 have landed (kt+2 may fly)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8_t na[kNI], nb[kMJ];
+    ml.read(lds.slot[(S + 1) % kStages], 0, na, nb);
+#pragma unroll
+    for (int r = 0; r < kMfma; ++r) {
+      const int i = r / kMJ, j = r % kMJ;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
+      if (r < L) ml.issue_one(lds.slot[(S + 3) % kStages], kt + 3, r);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if (r < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
     }
-    mfma_block(acc, a1, b1);
+#pragma unroll
+    for (int i = 0; i < kNI; ++i) a0[i] = na[i];
+#pragma unroll
+    for (int j = 0; j < kMJ; ++j) b0[j] = nb[j];
   };
 
   int kt = 0;
@@ -328,30 +349,32 @@ __device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int 
   if (kt < KT) step(0, kt);
   if (kt + 1 < KT) step(1, kt + 1);
   if (kt + 2 < KT) step(2, kt + 2);
-  // all operand reads are done before the slots are reused by the epilogue
-  __syncthreads();
+  wait_vmcnt<0>();  // trailing zero-fill loads land before the epilogue reuses LDS
+  __syncthreads();  // all operand reads are done before the slots hold staging data
 }
 
 // ------------------------------------------------------------------------------------
 // Epilogue helpers. Accumulator block acc[i][j] of a lane covers features
-//   n = n0 + wn*128 + 32 i + 8 g + 4 (lane >> 5) + e,  (register v = 4 g + e)
+//   n = n0 + wn*64 + 32 i + 8 g + 4 (lane >> 5) + e,  (register v = 4 g + e)
 // for the token m = m0 + wm*128 + 32 j + (lane & 31).
 struct EpiLane {
   int lane, wave, wm, wn, m0, n0;
   __device__ __forceinline__ EpiLane(int m0_, int n0_)
-      : lane(threadIdx.x & 63), wave(threadIdx.x >> 6), wm((threadIdx.x >> 6) >> 1),
-        wn((threadIdx.x >> 6) & 1), m0(m0_), n0(n0_) {}
+      : lane(threadIdx.x & 63), wave(threadIdx.x >> 6), wm((threadIdx.x >> 6) / kWavesN),
+        wn((threadIdx.x >> 6) % kWavesN), m0(m0_), n0(n0_) {}
   __device__ __forceinline__ int row(int j) const { return m0 + wm * 128 + 32 * j + (lane & 31); }
   __device__ __forceinline__ int col(int i, int g) const {
-    return n0 + wn * 128 + 32 * i + 8 * g + 4 * (lane >> 5);
+    return n0 + wn * kWaveN + 32 * i + 8 * g + 4 * (lane >> 5);
   }
   // wave-local staging coordinates
   __device__ __forceinline__ int srow(int j) const { return 32 * j + (lane & 31); }
   __device__ __forceinline__ int scol(int i, int g) const { return 32 * i + 8 * g + 4 * (lane >> 5); }
 };
 
+// Each wave stages its [128 x 64] block in half of one LDS slot.
 __device__ __forceinline__ char* stage_base(const LdsRing& lds, int wave) {
-  return wave == 0 ? lds.slot[0] : wave == 1 ? lds.slot[1] : wave == 2 ? lds.slot[2] : lds.slot[3];
+  char* s = (wave >> 1) == 0 ? lds.slot[0] : (wave >> 1) == 1 ? lds.slot[1] : (wave >> 1) == 2 ? lds.slot[2] : lds.slot[3];
+  return s + (wave & 1) * kStgWaveBytes;
 }
 
 __device__ __forceinline__ void stage_put8(char* stg, int r, int c, uint32_t lo, uint32_t hi) {
@@ -364,8 +387,8 @@ __device__ __forceinline__ void stage_put4(char* stg, int r, int c, uint32_t w) 
   *(uint32_t*)(stg + (r * kStgPitch + c) * 2) = w;
 }
 
-// Write a wave's staged [128 rows x ncols] bf16 block (ncols = 128 or 64) to
-// out[row0 + r, col0 + c] (row pitch ldo elements) with 16-byte row-contiguous stores.
+// Write a wave's staged [128 rows x kCols] bf16 block to out[row0 + r, col0 + c] (row
+// pitch ldo elements) with 16-byte row-contiguous stores.
 template <int kCols>
 __device__ __forceinline__ void stage_flush(const char* stg, uint16_t* __restrict__ out, size_t ldo,
                                             int M, int ncols_total, int row0, int col0, int lane) {
@@ -392,21 +415,26 @@ __device__ __forceinline__ void stage_flush(const char* stg, uint16_t* __restric
 
 // Combine per-lane row partials into one fp32 value per (token, 256-column tile) and
 // store it at partials[m * nb + tile]. Order is fixed: in-lane sum, the two 32-lane
-// halves, then wave wn = 0 plus wave wn = 1.
-__device__ __forceinline__ void store_row_partials(float (&part)[4], const LdsRing& lds, const EpiLane& L,
+// halves, then the four feature-waves wn = 0, 1, 2, 3 in turn.
+__device__ __forceinline__ void store_row_partials(float (&part)[kMJ], const LdsRing& lds, const EpiLane& L,
                                                    float* __restrict__ partials, int nb, int M) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) part[j] += __shfl_xor(part[j], 32);
+  for (int j = 0; j < kMJ; ++j) part[j] += __shfl_xor(part[j], 32);
   float* red = lds.red;
   if (L.lane < 32) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) red[(L.wm * 2 + L.wn) * 128 + 32 * j + L.lane] = part[j];
+    for (int j = 0; j < kMJ; ++j) red[(L.wm * kWavesN + L.wn) * 128 + 32 * j + L.lane] = part[j];
   }
   __syncthreads();
   const int t = threadIdx.x;
-  const int wm = t >> 7, r = t & 127;
-  const int m = L.m0 + t;
-  if (m < M) partials[(size_t)m * nb + L.n0 / kBN] = red[(wm * 2) * 128 + r] + red[(wm * 2 + 1) * 128 + r];
+  if (t < kBM) {
+    const int wm = t >> 7, r = t & 127;
+    const int m = L.m0 + t;
+    float s = red[(wm * kWavesN + 0) * 128 + r];
+#pragma unroll
+    for (int w = 1; w < kWavesN; ++w) s += red[(wm * kWavesN + w) * 128 + r];
+    if (m < M) partials[(size_t)m * nb + L.n0 / kBN] = s;
+  }
 }
 
 __device__ __forceinline__ u32x2_t load_bf16x4(const uint16_t* __restrict__ base, size_t idx, bool ok) {
@@ -417,25 +445,27 @@ __device__ __forceinline__ u32x2_t load_bf16x4(const uint16_t* __restrict__ base
   return v;
 }
 
+typedef f32x16_t AccTile[kNI][kMJ];
+
 // ---------------------------------------------------------------- plain store (baseline)
 struct EpiStore {
   struct Args {
     uint16_t* out;
   };
-  __device__ __forceinline__ static void apply(f32x16_t (&acc)[4][4], const Args& a, const GemmProblem& p,
-                                               int m0, int n0, const LdsRing& lds) {
+  __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
+                                               const LdsRing& lds) {
     const EpiLane L(m0, n0);
     char* stg = stage_base(lds, L.wave);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kMJ; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kNI; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           stage_put8(stg, L.srow(j), L.scol(i, g), pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
                      pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
     __syncthreads();
-    stage_flush<128>(stg, a.out, (size_t)p.N, p.M, p.N, m0 + L.wm * 128, n0 + L.wn * 128, L.lane);
+    stage_flush<kWaveN>(stg, a.out, (size_t)p.N, p.M, p.N, m0 + L.wm * 128, n0 + L.wn * kWaveN, L.lane);
   }
 };
 
@@ -450,18 +480,18 @@ struct EpiResidualRmsPartials {
     float* partials;
     int nb;
   };
-  __device__ __forceinline__ static void apply(f32x16_t (&acc)[4][4], const Args& a, const GemmProblem& p,
-                                               int m0, int n0, const LdsRing& lds) {
+  __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
+                                               const LdsRing& lds) {
     const EpiLane L(m0, n0);
     const int M = p.M, N = p.N;
     char* stg = stage_base(lds, L.wave);
-    float part[4];
+    float part[kMJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kMJ; ++j) {
       part[j] = 0.f;
       const int m = L.row(j);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kNI; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int n = L.col(i, g);
@@ -479,22 +509,22 @@ struct EpiResidualRmsPartials {
         }
     }
     __syncthreads();
-    stage_flush<128>(stg, a.h1, (size_t)N, M, N, m0 + L.wm * 128, n0 + L.wn * 128, L.lane);
+    stage_flush<kWaveN>(stg, a.h1, (size_t)N, M, N, m0 + L.wm * 128, n0 + L.wn * kWaveN, L.lane);
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kNI; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n = L.col(i, g);
         const u32x2_t gg = load_bf16x4(a.gamma, (size_t)n, n < N);
         const float g0 = bf16_lo(gg.x), g1 = bf16_hi(gg.x), g2 = bf16_lo(gg.y), g3 = bf16_hi(gg.y);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kMJ; ++j)
           stage_put8(stg, L.srow(j), L.scol(i, g), pack_bf16x2(acc[i][j][4 * g] * g0, acc[i][j][4 * g + 1] * g1),
                      pack_bf16x2(acc[i][j][4 * g + 2] * g2, acc[i][j][4 * g + 3] * g3));
       }
     __syncthreads();
-    stage_flush<128>(stg, a.h2, (size_t)N, M, N, m0 + L.wm * 128, n0 + L.wn * 128, L.lane);
+    stage_flush<kWaveN>(stg, a.h2, (size_t)N, M, N, m0 + L.wm * 128, n0 + L.wn * kWaveN, L.lane);
     store_row_partials(part, lds, L, a.partials, a.nb, M);
   }
 };
@@ -505,23 +535,23 @@ struct EpiRowScale {
     const float* r;
     uint16_t* y;
   };
-  __device__ __forceinline__ static void apply(f32x16_t (&acc)[4][4], const Args& a, const GemmProblem& p,
-                                               int m0, int n0, const LdsRing& lds) {
+  __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
+                                               const LdsRing& lds) {
     const EpiLane L(m0, n0);
     char* stg = stage_base(lds, L.wave);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kMJ; ++j) {
       const int m = L.row(j);
       const float rr = m < p.M ? a.r[m] : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kNI; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           stage_put8(stg, L.srow(j), L.scol(i, g), pack_bf16x2(rr * acc[i][j][4 * g], rr * acc[i][j][4 * g + 1]),
                      pack_bf16x2(rr * acc[i][j][4 * g + 2], rr * acc[i][j][4 * g + 3]));
     }
     __syncthreads();
-    stage_flush<128>(stg, a.y, (size_t)p.N, p.M, p.N, m0 + L.wm * 128, n0 + L.wn * 128, L.lane);
+    stage_flush<kWaveN>(stg, a.y, (size_t)p.N, p.M, p.N, m0 + L.wm * 128, n0 + L.wn * kWaveN, L.lane);
   }
 };
 
@@ -536,19 +566,19 @@ struct EpiRope {
     int seq_len;
     int pos_offset;
   };
-  __device__ __forceinline__ static void apply(f32x16_t (&acc)[4][4], const Args& a, const GemmProblem& p,
-                                               int m0, int n0, const LdsRing& lds) {
+  __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
+                                               const LdsRing& lds) {
     const EpiLane L(m0, n0);
     char* stg = stage_base(lds, L.wave);
     const int half = a.head_dim >> 1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kMJ; ++j) {
       const int m = L.row(j);
       const int pos = m < p.M ? (int)(((long long)m + a.pos_offset) % a.seq_len) : 0;
       const float* crow = a.cos_t + (size_t)pos * half;
       const float* srow = a.sin_t + (size_t)pos * half;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kNI; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int n = L.col(i, g);
@@ -569,7 +599,7 @@ struct EpiRope {
         }
     }
     __syncthreads();
-    stage_flush<128>(stg, a.out, (size_t)p.N, p.M, p.N, m0 + L.wm * 128, n0 + L.wn * 128, L.lane);
+    stage_flush<kWaveN>(stg, a.out, (size_t)p.N, p.M, p.N, m0 + L.wm * 128, n0 + L.wn * kWaveN, L.lane);
   }
 };
 
@@ -581,14 +611,14 @@ struct EpiSwiGLU {
     uint16_t* out;
     int F;  // output width (= N / 2)
   };
-  __device__ __forceinline__ static void apply(f32x16_t (&acc)[4][4], const Args& a, const GemmProblem& p,
-                                               int m0, int n0, const LdsRing& lds) {
+  __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
+                                               const LdsRing& lds) {
     const EpiLane L(m0, n0);
     char* stg = stage_base(lds, L.wave);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kMJ; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kNI; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const float y0 = silu_f32(acc[i][j][4 * g + 0]) * acc[i][j][4 * g + 1];
@@ -596,7 +626,8 @@ struct EpiSwiGLU {
           stage_put4(stg, L.srow(j), L.scol(i, g) >> 1, pack_bf16x2(y0, y1));
         }
     __syncthreads();
-    stage_flush<64>(stg, a.out, (size_t)a.F, p.M, a.F, m0 + L.wm * 128, (n0 >> 1) + L.wn * 64, L.lane);
+    stage_flush<kWaveN / 2>(stg, a.out, (size_t)a.F, p.M, a.F, m0 + L.wm * 128, (n0 >> 1) + L.wn * (kWaveN / 2),
+                            L.lane);
   }
 };
 
@@ -608,18 +639,18 @@ struct EpiDotRowPartials {
     float* partials;
     int nb;
   };
-  __device__ __forceinline__ static void apply(f32x16_t (&acc)[4][4], const Args& a, const GemmProblem& p,
-                                               int m0, int n0, const LdsRing& lds) {
+  __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
+                                               const LdsRing& lds) {
     const EpiLane L(m0, n0);
     const int M = p.M, N = p.N;
     char* stg = stage_base(lds, L.wave);
-    float part[4];
+    float part[kMJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kMJ; ++j) {
       part[j] = 0.f;
       const int m = L.row(j);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kNI; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int n = L.col(i, g);
@@ -631,23 +662,23 @@ struct EpiDotRowPartials {
         }
     }
     __syncthreads();
-    stage_flush<128>(stg, a.dh2, (size_t)N, M, N, m0 + L.wm * 128, n0 + L.wn * 128, L.lane);
+    stage_flush<kWaveN>(stg, a.dh2, (size_t)N, M, N, m0 + L.wm * 128, n0 + L.wn * kWaveN, L.lane);
     store_row_partials(part, lds, L, a.partials, a.nb, M);
   }
 };
 
 template <bool kWKN, class Epi>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void gemm_epilogue_kernel(GemmProblem p, typename Epi::Args ea) {
-  __shared__ __attribute__((aligned(1024))) char slot0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char slot1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char slot2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char slot3[kStageBytes];
-  __shared__ __attribute__((aligned(16))) float red[kRedBytes / 4];
+  __shared__ __attribute__((aligned(1024))) char slot0[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char slot1[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char slot2[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char slot3[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) float red[kRedFloats];
   const LdsRing lds{{slot0, slot1, slot2, slot3}, red};
   int m0, n0;
   tile_coords(p.M, p.N, m0, n0);
-  f32x16_t acc[4][4];
+  AccTile acc;
   gemm_mainloop<kWKN>(p, m0, n0, lds, acc);
   Epi::apply(acc, ea, p, m0, n0, lds);
 }
