@@ -74,6 +74,30 @@ def time_reps(fn, reps, warmup=3):
     return dict(median_ms=float(np.median(t)), mean_ms=float(t.mean()), min_ms=float(t.min()))
 
 
+def time_interleaved(fns, reps, rounds=4, warmup=2):
+    """Median milliseconds per callable, all timed in alternating rounds (forward order on
+    even rounds, reverse on odd) so that every variant sees the same clock and thermal
+    state; back-to-back blocks of one variant would compare different clocks."""
+    import torch
+    names = list(fns)
+    for n in names:
+        for _ in range(warmup):
+            fns[n]()
+    torch.cuda.synchronize()
+    times = {n: [] for n in names}
+    per = max(1, reps // rounds)
+    for k in range(rounds):
+        for n in (names if k % 2 == 0 else names[::-1]):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(per)]
+            for a, b in evs:
+                a.record()
+                fns[n]()
+                b.record()
+            torch.cuda.synchronize()
+            times[n] += event_ms(evs)
+    return {n: float(np.median(t)) for n, t in times.items()}
+
+
 # --------------------------------------------------------------------------- headline
 def headline(args, coda, torch):
     import workloads as W
@@ -173,8 +197,10 @@ def headline(args, coda, torch):
 
 # ------------------------------------------------------------------- unfused baseline
 def unfused_fwd(coda, torch, b, reps):
-    """Same MFMA main loop with a plain store, then a separate residual+RMSNorm kernel,
-    then the plain GEMM again (bf16 intermediates), and torch (hipBLASLt) + eager ops."""
+    """The fused forward entry point against (a) the same MFMA main loop with a plain
+    store, then a separate residual+RMSNorm kernel, then the plain GEMM again (bf16
+    intermediates), and (b) torch (hipBLASLt) + eager ops; the three are timed
+    interleaved."""
     x, w0, z, g, w1, eps = b["x"], b["w0"], b["z"], b["g"], b["w1"], b["eps"]
     M, D = b["h1"].shape
     h0 = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
@@ -193,13 +219,17 @@ def unfused_fwd(coda, torch, b, reps):
         oo = torch.nn.functional.rms_norm(hh, (D,), weight=g, eps=eps)
         return torch.matmul(oo, w1)
 
-    t_ours = time_reps(ours, reps)
-    t_torch = time_reps(torch_path, reps)
+    def fused():
+        coda.coda_gemm_rmsnorm_fwd(x, w0, z, g, w1, eps, h1=b["h1"], h2=b["h2"], partials=b["part"], r=b["r"],
+                                   y=b["y"])
+
+    t = time_interleaved({"fused": fused, "ours": ours, "torch": torch_path}, 2 * reps)
     t_norm = time_reps(lambda: coda.coda_baseline_residual_rmsnorm(h0, z, g, eps, h1=h1, r=r, o=o), reps)
     t_mm1 = time_reps(lambda: torch.matmul(x, w0), reps)
     t_mm2 = time_reps(lambda: torch.matmul(o, w1), reps)
-    return dict(same_mainloop_plus_separate_kernels_ms=t_ours["median_ms"],
-                torch_hipblaslt_eager_ms=t_torch["median_ms"],
+    return dict(fused_entry_point_ms=t["fused"],
+                same_mainloop_plus_separate_kernels_ms=t["ours"],
+                torch_hipblaslt_eager_ms=t["torch"],
                 separate_residual_rmsnorm_kernel_us=round(t_norm["median_ms"] * 1e3, 2),
                 separate_residual_rmsnorm_gbps=round(4 * M * D * 2 / (t_norm["median_ms"] * 1e-3) / 1e9, 1),
                 hipblaslt_gemm1_tflops=round(2 * M * x.shape[1] * D / (t_mm1["median_ms"] * 1e-3) / 1e12, 1),
@@ -207,6 +237,13 @@ def unfused_fwd(coda, torch, b, reps):
 
 
 # ------------------------------------------------------------------ other fused paths
+def path_record(t, fl):
+    return dict(fused_us=round(t["fused"] * 1e3, 1), tflops=round(fl / (t["fused"] * 1e-3) / 1e12, 1),
+                unfused_us=round(t["unfused"] * 1e3, 1), speedup_vs_unfused=round(t["unfused"] / t["fused"], 3),
+                hipblaslt_gemm_only_us=round(t["hipblaslt"] * 1e3, 1),
+                hipblaslt_gemm_only_tflops=round(fl / (t["hipblaslt"] * 1e-3) / 1e12, 1))
+
+
 def other_paths(coda, torch, reps):
     import workloads as W
     out = {}
@@ -218,15 +255,12 @@ def other_paths(coda, torch, reps):
     qkv = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     h = torch.empty_like(qkv)
     args = (wl["n_q"], wl["n_k"], wl["n_v"], wl["head_dim"], wl["seq_len"], 0)
-    tf = time_reps(lambda: coda.coda_gemm_rope(x, w, c, s, *args, out=qkv), reps)
-    tu = time_reps(lambda: (coda.coda_baseline_gemm(x, w, c=h), coda.coda_baseline_rope(h, c, s, *args, out=qkv)),
-                   reps)
-    tb = time_reps(lambda: torch.matmul(x, w), reps)
+    t = time_interleaved({
+        "fused": lambda: coda.coda_gemm_rope(x, w, c, s, *args, out=qkv),
+        "unfused": lambda: (coda.coda_baseline_gemm(x, w, c=h), coda.coda_baseline_rope(h, c, s, *args, out=qkv)),
+        "hipblaslt": lambda: torch.matmul(x, w)}, reps)
     fl = 2.0 * M * K * N
-    out["gemm_rope_qkv_4096x12288x4096"] = dict(
-        fused_us=round(tf["median_ms"] * 1e3, 1), tflops=round(fl / (tf["median_ms"] * 1e-3) / 1e12, 1),
-        unfused_us=round(tu["median_ms"] * 1e3, 1), speedup_vs_unfused=round(tu["median_ms"] / tf["median_ms"], 3),
-        hipblaslt_gemm_only_tflops=round(fl / (tb["median_ms"] * 1e-3) / 1e12, 1))
+    out["gemm_rope_qkv_4096x12288x4096"] = path_record(t, fl)
     del x, w, qkv, h
     # GEMM + SwiGLU
     wl = W.swiglu()
@@ -234,14 +268,12 @@ def other_paths(coda, torch, reps):
     M, K, F = wl["M"], wl["K"], wl["F"]
     o = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
     h = torch.empty((M, 2 * F), dtype=torch.bfloat16, device="cuda")
-    tf = time_reps(lambda: coda.coda_gemm_swiglu(x, w, out=o), reps)
-    tu = time_reps(lambda: (coda.coda_baseline_gemm(x, w, c=h), coda.coda_baseline_swiglu(h, out=o)), reps)
-    tb = time_reps(lambda: torch.matmul(x, w), reps)
+    t = time_interleaved({
+        "fused": lambda: coda.coda_gemm_swiglu(x, w, out=o),
+        "unfused": lambda: (coda.coda_baseline_gemm(x, w, c=h), coda.coda_baseline_swiglu(h, out=o)),
+        "hipblaslt": lambda: torch.matmul(x, w)}, reps)
     fl = 2.0 * M * K * 2 * F
-    out["gemm_swiglu_8192x8192x8192"] = dict(
-        fused_us=round(tf["median_ms"] * 1e3, 1), tflops=round(fl / (tf["median_ms"] * 1e-3) / 1e12, 1),
-        unfused_us=round(tu["median_ms"] * 1e3, 1), speedup_vs_unfused=round(tu["median_ms"] / tf["median_ms"], 3),
-        hipblaslt_gemm_only_tflops=round(fl / (tb["median_ms"] * 1e-3) / 1e12, 1))
+    out["gemm_swiglu_8192x8192x8192"] = path_record(t, fl)
     del x, w, o, h
     # backward statistic
     wl = W.bwd_stats()
@@ -250,13 +282,14 @@ def other_paths(coda, torch, reps):
     dh2 = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
     part = torch.empty((M, coda.num_partials(D)), dtype=torch.float32, device="cuda")
     sv = torch.empty((M,), dtype=torch.float32, device="cuda")
-    tf = time_reps(lambda: coda.coda_gemm_rmsnorm_bwd_stats(dy, w1, h2, dh2=dh2, partials=part, s=sv), reps)
-    tu = time_reps(lambda: (coda.coda_baseline_gemm(dy, w1, b_kn=False, c=dh2), coda.coda_baseline_rowdot(dh2, h2, s=sv)),
-                   reps)
+    w1t = w1.t().contiguous()
+    t = time_interleaved({
+        "fused": lambda: coda.coda_gemm_rmsnorm_bwd_stats(dy, w1, h2, dh2=dh2, partials=part, s=sv),
+        "unfused": lambda: (coda.coda_baseline_gemm(dy, w1, b_kn=False, c=dh2),
+                            coda.coda_baseline_rowdot(dh2, h2, s=sv)),
+        "hipblaslt": lambda: torch.matmul(dy, w1t)}, reps)
     fl = 2.0 * M * N * D
-    out["gemm_rmsnorm_bwd_stats_8192x4096x6144"] = dict(
-        fused_us=round(tf["median_ms"] * 1e3, 1), tflops=round(fl / (tf["median_ms"] * 1e-3) / 1e12, 1),
-        unfused_us=round(tu["median_ms"] * 1e3, 1), speedup_vs_unfused=round(tu["median_ms"] / tf["median_ms"], 3))
+    out["gemm_rmsnorm_bwd_stats_8192x4096x6144"] = path_record(t, fl)
     return out
 
 
@@ -344,9 +377,9 @@ def main():
     log(f"headline: {res['value']} TFLOP/s, {res['ms_per_step']} ms/step")
     if not args.headline_only:
         res["unfused_fwd"] = unfused_fwd(coda, torch, bufs, args.reps)
-        res["speedup_vs_unfused_same_mainloop"] = round(
-            res["unfused_fwd"]["same_mainloop_plus_separate_kernels_ms"] / res["ms_per_step"], 3)
-        res["speedup_vs_torch_hipblaslt"] = round(res["unfused_fwd"]["torch_hipblaslt_eager_ms"] / res["ms_per_step"], 3)
+        u = res["unfused_fwd"]
+        res["speedup_vs_unfused_same_mainloop"] = round(u["same_mainloop_plus_separate_kernels_ms"] / u["fused_entry_point_ms"], 3)
+        res["speedup_vs_torch_hipblaslt"] = round(u["torch_hipblaslt_eager_ms"] / u["fused_entry_point_ms"], 3)
         del bufs
         torch.cuda.empty_cache()
         res["paths"] = other_paths(coda, torch, args.reps)

@@ -9,50 +9,36 @@ using namespace coda;
 
 namespace {
 
-// ----------------------------------------------------------- auxiliary row reduction
-// One wave per 64 rows. The [64, nb] block of partials is streamed through LDS in
-// column chunks with coalesced 16-byte loads (the rows of a block are contiguous in
-// HBM), then each lane sums its own row in the fixed order t = 0, 1, ..., nb-1.
-constexpr int kRsRows = 64;
-constexpr int kRsCh = 32;
+// Auxiliary row reduction of the per-tile partials: one thread per row sums its row in
+// the fixed order t = 0, 1, ..., nb-1 (deterministic, independent of the launch) and
+// applies the row statistic. Loads go out four 16-byte vectors at a time per thread, so
+// a wave has 4 KiB of HBM reads in flight with no LDS or barrier; this is a pure
+// streaming kernel (nb * 4 bytes read and 4 written per row).
+constexpr int kRsThreads = 256;
 
 template <bool kVec4>
-__global__ __launch_bounds__(64) void rowstat_reduce_kernel(const float* __restrict__ P, int M, int nb, float d,
-                                                            float eps, int mode, float* __restrict__ out) {
-  __shared__ float tile[kRsRows][kRsCh + 1];
-  const int m0 = blockIdx.x * kRsRows;
-  const int rows = min(kRsRows, M - m0);
-  const int t = threadIdx.x;
+__global__ __launch_bounds__(kRsThreads) void rowstat_reduce_kernel(const float* __restrict__ P, int M, int nb,
+                                                                    float d, float eps, int mode,
+                                                                    float* __restrict__ out) {
+  const int m = blockIdx.x * kRsThreads + threadIdx.x;
+  if (m >= M) return;
+  const float* row = P + (size_t)m * nb;
   float s = 0.f;
-  for (int c0 = 0; c0 < nb; c0 += kRsCh) {
-    const int cw = min(kRsCh, nb - c0);
-    if constexpr (kVec4) {
-      const int q = cw >> 2;  // float4s per row in this chunk (nb % 4 == 0)
-      const int total = rows * q;
-      for (int e = t; e < total; e += 64) {
-        const int r = e / q, c = (e - r * q) * 4;
-        const float4 v = *(const float4*)(P + (size_t)(m0 + r) * nb + c0 + c);
-        tile[r][c] = v.x;
-        tile[r][c + 1] = v.y;
-        tile[r][c + 2] = v.z;
-        tile[r][c + 3] = v.w;
-      }
-    } else {
-      const int total = rows * cw;
-      for (int e = t; e < total; e += 64) {
-        const int r = e / cw, c = e - r * cw;
-        tile[r][c] = P[(size_t)(m0 + r) * nb + c0 + c];
-      }
+  if constexpr (kVec4) {
+    for (int c0 = 0; c0 < nb; c0 += 16) {  // nb % 4 == 0
+      float4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (c0 + 4 * q < nb) v[q] = *(const float4*)(row + c0 + 4 * q);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (c0 + 4 * q < nb) s = (((s + v[q].x) + v[q].y) + v[q].z) + v[q].w;
     }
-    __syncthreads();
-    if (t < rows)
-      for (int c = 0; c < cw; ++c) s += tile[t][c];
-    __syncthreads();
+  } else {
+    for (int c = 0; c < nb; ++c) s += row[c];
   }
-  if (t < rows) {
-    const float mean = s / d;
-    out[m0 + t] = (mode == CODA_ROWSTAT_RSQRT_MEAN_EPS) ? 1.0f / sqrtf(mean + eps) : mean;
-  }
+  const float mean = s / d;
+  out[m] = (mode == CODA_ROWSTAT_RSQRT_MEAN_EPS) ? 1.0f / sqrtf(mean + eps) : mean;
 }
 
 // ------------------------------------------------------------------------ RoPE tables
@@ -194,12 +180,12 @@ inline unsigned blocks_for(long long n, int per_block) { return (unsigned)((n + 
 // Shared with the GEMM entry points (no argument checks: callers have checked).
 int coda_rowstat_reduce_impl(const float* partials, int M, int nb, int d, float eps, int mode, float* out,
                              hipStream_t stream) {
-  const unsigned grid = blocks_for(M, kRsRows);
+  const unsigned grid = blocks_for(M, kRsThreads);
   if (nb % 4 == 0 && aligned(partials, 16))
-    hipLaunchKernelGGL((rowstat_reduce_kernel<true>), dim3(grid), dim3(64), 0, stream, partials, M, nb, (float)d,
-                       eps, mode, out);
+    hipLaunchKernelGGL((rowstat_reduce_kernel<true>), dim3(grid), dim3(kRsThreads), 0, stream, partials, M, nb,
+                       (float)d, eps, mode, out);
   else
-    hipLaunchKernelGGL((rowstat_reduce_kernel<false>), dim3(grid), dim3(64), 0, stream, partials, M, nb,
+    hipLaunchKernelGGL((rowstat_reduce_kernel<false>), dim3(grid), dim3(kRsThreads), 0, stream, partials, M, nb,
                        (float)d, eps, mode, out);
   return launch_status();
 }
