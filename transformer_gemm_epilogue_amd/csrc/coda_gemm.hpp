@@ -19,8 +19,9 @@
 // (even, odd) feature pairs of RoPE and SwiGLU stay in one lane's registers.
 //
 // Data movement. Both operand tiles go from HBM straight into LDS with
-// buffer_load_dwordx4 ... lds (no register staging), through a ring of 4 LDS stages of
-// 32 depth each, so three depth-steps are in flight while one is consumed. X and NK-W
+// buffer_load_dwordx4 ... lds (no register staging), through a ring of 5 LDS stages of
+// 32 depth each (160 KiB), so loads for up to four depth-steps are in flight while one
+// is consumed. X and NK-W
 // tiles are stored depth-contiguous ([row][32] bf16, 64 B per row); a KN-W tile keeps
 // its natural [32][256] layout and is transposed on the way out of LDS by
 // ds_read_b64_tr_b16 into the depth-contiguous MFMA operand. All tiles XOR-swizzle
@@ -29,10 +30,15 @@
 // columns past N read as zero, so ragged edges need no special path.
 //
 // Schedule of one depth-step S (two k16 sub-steps), per wave:
-//   read the sub-step-1 operands of S | 8 MFMAs of sub-step 0 of S |
-//   wait for this thread's loads of S+1, barrier (S+1 complete for every wave, S-1 no
-//   longer read by anyone) | 8 MFMAs of sub-step 1 of S, interleaved one for one with
-//   the reads of sub-step 0 of S+1 and the DMA loads of S+3 into the slot of S-1.
+//   read the sub-step-1 operands of S | 8 MFMAs of sub-step 0 of S, and the W half of
+//   the DMA of S+3 into the slot of S-2 | wait for this thread's loads of S+1, barrier
+//   (S+1 complete for every wave, S-1 no longer read by anyone) | 8 MFMAs of sub-step 1
+//   of S, interleaved one for one with the reads of sub-step 0 of S+1 and the X half of
+//   the DMA of S+4 into the slot of S-1.
+// A slot is written only after the barrier that follows its last reader's consumption,
+// and the load issue is spread over the whole step: on gfx950 the operand delivery is
+// bounded by how many DMA loads are in flight (texture data path busy, waiting on L1),
+// and the fifth stage raises that bound from 8 to 12 loads per wave.
 // The order is pinned with scheduling barriers; the code is straight-line (the DMA of
 // steps past the end only zero-fills a free slot) so the compiler's LDS wait counts
 // never make an MFMA wait for reads issued after its operands.
@@ -45,7 +51,7 @@ namespace coda {
 constexpr int kBM = 256;        // tokens per workgroup tile
 constexpr int kBN = 256;        // features per workgroup tile (== CODA_PARTIAL_TILE_N)
 constexpr int kBK = 32;         // depth per LDS stage
-constexpr int kStages = 4;      // LDS ring depth
+constexpr int kStages = 5;      // LDS ring depth
 constexpr int kWaves = 8;       // two per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWavesN = 4;      // waves along features
@@ -59,8 +65,8 @@ constexpr int kSlotBytes = 2 * kTileBytes;  // one stage: X tile + W tile
 constexpr int kStgRows = 64;                // tokens a wave re-lays out at a time
 constexpr int kStgWaveBytes = kStgRows * kWaveN * 4;  // fp32: 16 KiB per wave
 constexpr int kRedFloats = 2 * kWavesN * 128;
-static_assert(kWaves * kStgWaveBytes <= kStages * kSlotBytes, "staging reuses the stage slots");
-static_assert(kStages * kSlotBytes + 4 * kRedFloats <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
+static_assert(kWaves * kStgWaveBytes + 4 * kRedFloats <= kStages * kSlotBytes, "staging and red reuse the slots");
+static_assert(kStages * kSlotBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
 static_assert(kWaves == 2 * kWavesN && kWavesN * kWaveN == kBN, "wave layout covers the tile");
 
 struct GemmProblem {
@@ -69,8 +75,8 @@ struct GemmProblem {
   int M, N, K;
 };
 
-// LDS of one workgroup: four stage slots (after the main loop each holds two waves'
-// epilogue staging areas) and the row-partial exchange area.
+// LDS of one workgroup: five stage slots. After the main loop, slots 0..3 hold the eight
+// waves' epilogue staging areas and slot 4 the row-partial exchange area.
 struct LdsRing {
   char* slot[kStages];
   float* red;
@@ -306,10 +312,12 @@ __device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int 
   constexpr int kMfma = kNI * kMJ;                      // MFMAs per k16 sub-step
   constexpr int L = kLoadsPerStep;
 
-  // prologue: steps 0, 1, 2 in flight; wait for step 0
+  // prologue: steps 0, 1, 2 and the X half of step 3 in flight; wait for step 0
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) ml.issue(lds.slot[s], s);
-  wait_vmcnt<2 * L>();
+  for (int s = 0; s < 3; ++s) ml.issue(lds.slot[s], s);
+  ml.issue_one(lds.slot[3], 3, 0);
+  ml.issue_one(lds.slot[3], 3, 1);
+  wait_vmcnt<10>();
   __builtin_amdgcn_s_barrier();
 
   bf16x8_t a0[kNI], b0[kMJ], a1[kNI], b1[kMJ];
@@ -323,8 +331,11 @@ __device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int 
       for (int j = 0; j < kMJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);  // sub-step-1 reads first
     __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);   // then the sub-step-0 MFMAs
+    // W half of step kt+3 into the slot of kt-2 (free since the previous barrier)
+    ml.issue_one(lds.slot[(S + 3) % kStages], kt + 3, 2);
+    ml.issue_one(lds.slot[(S + 3) % kStages], kt + 3, 3);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<L>();  // this thread's loads of step kt+1 have landed (kt+2 may fly)
+    wait_vmcnt<8>();  // this thread's loads of step kt+1 have landed
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     bf16x8_t na[kNI], nb[kMJ];
@@ -333,7 +344,8 @@ __device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int 
     for (int r = 0; r < kMfma; ++r) {
       const int i = r / kMJ, j = r % kMJ;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
-      if (r < L) ml.issue_one(lds.slot[(S + 3) % kStages], kt + 3, r);
+      // X half of step kt+4 into the slot of kt-1 (free since this step's barrier)
+      if (r < 2) ml.issue_one(lds.slot[(S + 4) % kStages], kt + 4, r);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       if (r < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
     }
@@ -349,10 +361,12 @@ __device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int 
     step(1, kt + 1);
     step(2, kt + 2);
     step(3, kt + 3);
+    step(4, kt + 4);
   }
   if (kt < KT) step(0, kt);
   if (kt + 1 < KT) step(1, kt + 1);
   if (kt + 2 < KT) step(2, kt + 2);
+  if (kt + 3 < KT) step(3, kt + 3);
   wait_vmcnt<0>();  // trailing zero-fill loads land before the epilogue reuses LDS
   __syncthreads();  // all operand reads are done before the slots hold staging data
 }
@@ -750,9 +764,9 @@ struct EpiDotRowPartials {
 template <bool kWKN, class Epi>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void gemm_epilogue_kernel(GemmProblem p, typename Epi::Args ea) {
-  __shared__ __attribute__((aligned(1024))) char smem[kStages * kSlotBytes + 4 * kRedFloats];
-  const LdsRing lds{{smem, smem + kSlotBytes, smem + 2 * kSlotBytes, smem + 3 * kSlotBytes},
-                    (float*)(smem + kStages * kSlotBytes)};
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kSlotBytes];
+  const LdsRing lds{{smem, smem + kSlotBytes, smem + 2 * kSlotBytes, smem + 3 * kSlotBytes, smem + 4 * kSlotBytes},
+                    (float*)(smem + kWaves * kStgWaveBytes)};
   int m0, n0;
   tile_coords(p.M, p.N, m0, n0);
   AccTile acc;
