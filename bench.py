@@ -38,14 +38,17 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# The sources that define GEMM1's kernel (main loop, residual epilogue) and its launch.
+GEMM1_SOURCES = ("coda_common.hpp", "coda_abi.hpp", "coda_gemm.hpp", "coda_gemm.hip")
+
+
 def source_hash() -> str:
-    """Hash of the HIP sources; stored HBM-traffic counters are used only while it matches."""
+    """Hash of GEMM1's HIP sources; stored HBM-traffic counters are used only while it matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "transformer_gemm_epilogue_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in GEMM1_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
