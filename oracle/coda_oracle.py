@@ -44,6 +44,12 @@ the design notes of the repository):
       silu(g) = g / (1 + exp(-g)); the output width is half the accumulator width.
   R7  Backward statistic: h2 is the GEMM2 input and y = h2 W1 ([notes] key design 3);
       s = (1/d) sum_cols(dY W1^T * h2), also computed as (1/d) sum(dY * y).
+  R8  Rest of the RMSNorm backward ([notes] key design 3 and the duality paragraph
+      before its statistic; [pith] Fig. 9): the forward is o = r h1 gamma (the GEMM2
+      input of R7, normalised), y = o W1. With dO = dY W1^T the chain rule gives
+      dh1 = r gamma dO - r^2 s h1 with s = (1/d) sum_cols(dO * o), plus the gradient
+      g_res that reaches h1 through the residual stream; dgamma = sum_rows(dO r h1).
+      Column partials of dgamma are sums over 256-row tiles, like R2's row partials.
 """
 from __future__ import annotations
 
@@ -62,6 +68,7 @@ __all__ = [
     "silu",
     "gemm_swiglu",
     "gemm_rmsnorm_bwd_stats",
+    "rmsnorm_bwd",
     "flops_gemm_rmsnorm_fwd",
 ]
 
@@ -69,6 +76,8 @@ __all__ = [
 # columns [t*256, (t+1)*256) (the last tile may be ragged). This is the layout
 # contract of the workspace, stated by the library's interface documentation.
 PARTIAL_TILE_N = 256
+# Height of one row tile of the column-partial workspace [ceil(M/256), D] of dgamma.
+PARTIAL_TILE_M = 256
 
 
 def decode_bf16(bits) -> np.ndarray:
@@ -244,6 +253,51 @@ def gemm_rmsnorm_bwd_stats(dy, w1, h2, rows=None, tile_n: int = PARTIAL_TILE_N) 
     s_diag = np.diag(matmul(dyr, y.T)) / d if dyr.shape[0] <= 512 else None
     return dict(dh2=dh2, partials=tile_row_sums(prod, tile_n), s=s, s_prime=s_prime,
                 s_diag=s_diag)
+
+
+def rmsnorm_bwd(h1, gamma, w1, dy, eps: float, g_res=None, rows=None, cols=None,
+                tile_m: int = PARTIAL_TILE_M) -> dict:
+    """Rest of the RMSNorm backward around the grad GEMM (reading R8).
+
+    Forward, non-deferred form of [notes] key design 1: r = 1/sqrt(mean(h1^2) + eps),
+    o = r * h1 * gamma (GEMM2 input), y = o W1. With upstream gradient dY [M, N]:
+        dO     = dY W1^T                                  (the grad GEMM)
+        s      = (1/d) sum_cols(dO * o) = (1/d) sum(dY * y)  (key design 3)
+        dh1    = r * gamma * dO - r^2 * s * h1  (+ g_res)
+        dgamma = sum_rows(dO * r * h1)
+    Derivation: o_k = r h1_k gamma_k and dr/dh1_j = -r^3 h1_j / d, so
+    dh1_j = r gamma_j dO_j - (r^3 h1_j / d) sum_k dO_k gamma_k h1_k = r gamma_j dO_j -
+    r^2 s h1_j.
+
+    Row outputs (r, y, s, s_out, dh1) are for the selected ``rows`` (all by default).
+    ``dgamma`` sums over all rows of the input (or only the selected rows when ``rows``
+    is given); ``cols`` limits the dgamma / dgamma_partials columns (cheap at full size:
+    only those columns of dO are formed). ``dgamma_partials[t, c]`` sums rows
+    [t*tile_m, (t+1)*tile_m) of the selected rows' order.
+    """
+    H1 = _as_f64(h1)
+    G = _as_f64(gamma)
+    W1 = _as_f64(w1)
+    DY = _as_f64(dy)
+    d = H1.shape[1]
+    h1r = _take_rows(H1, rows)
+    dyr = _take_rows(DY, rows)
+    r = 1.0 / np.sqrt((h1r * h1r).sum(axis=1) / d + eps)
+    o = r[:, None] * h1r * G[None, :]
+    y = matmul(o, W1)
+    dO = matmul(dyr, W1.T)
+    s = (dO * o).sum(axis=1) / d
+    s_out = (dyr * y).sum(axis=1) / d
+    dh1 = r[:, None] * G[None, :] * dO - (r * r * s)[:, None] * h1r
+    if g_res is not None:
+        dh1 = dh1 + _take_rows(_as_f64(g_res), rows)
+    c = np.arange(d) if cols is None else np.asarray(cols)
+    dO_c = dO[:, c] if cols is None else matmul(dyr, W1[c, :].T)
+    contrib = dO_c * r[:, None] * h1r[:, c]
+    nt = (contrib.shape[0] + tile_m - 1) // tile_m
+    parts = np.stack([contrib[t * tile_m:(t + 1) * tile_m].sum(axis=0) for t in range(nt)])
+    return dict(r=r, y=y, dO=dO, s=s, s_out=s_out, dh1=dh1, dgamma=contrib.sum(axis=0),
+                dgamma_partials=parts, cols=c)
 
 
 def flops_gemm_rmsnorm_fwd(M: int, K: int, D: int, N1: int) -> int:

@@ -347,3 +347,79 @@ def test_planted_bwd_transpose_fails_pin():
     wrong = O.matmul(dy, O.decode_bf16(w1))        # dY W1 instead of dY W1^T
     assert rel(O.gemm_rmsnorm_bwd_stats(dy, w1, h2)["dh2"], H2.grad.numpy()) < 1e-14
     assert rel(wrong, H2.grad.numpy()) > 0.1
+
+
+# ------------------------------------------- rest of the RMSNorm backward (reading R8)
+def _rbwd_case(seed=30, M=40, D=48, N=36):
+    rng = np.random.default_rng(seed)
+    return dict(h1=normal_bf16(rng, (M, D), 1.0), gamma=normal_bf16(rng, (D,), 0.1, 1.0),
+                w1=normal_bf16(rng, (D, N), 1 / math.sqrt(D)), dy=normal_bf16(rng, (M, N), 0.1),
+                g_res=normal_bf16(rng, (M, D), 0.1), eps=1e-5)
+
+
+def _rbwd(c, **kw):
+    return O.rmsnorm_bwd(c["h1"], c["gamma"], c["w1"], c["dy"], c["eps"], g_res=c["g_res"], **kw)
+
+
+def _autograd_rmsnorm_bwd(c):
+    # torch's rms_norm (a library routine) then the GEMM; the residual stream adds
+    # g_res . h1 to the loss, so its gradient reaches h1 unchanged.
+    h1 = torch.from_numpy(O.decode_bf16(c["h1"])).requires_grad_(True)
+    g = torch.from_numpy(O.decode_bf16(c["gamma"])).requires_grad_(True)
+    w1 = torch.from_numpy(O.decode_bf16(c["w1"]))
+    y = torch.nn.functional.rms_norm(h1, (h1.shape[1],), weight=g, eps=c["eps"]) @ w1
+    loss = (y * torch.from_numpy(O.decode_bf16(c["dy"]))).sum() + \
+        (h1 * torch.from_numpy(O.decode_bf16(c["g_res"]))).sum()
+    loss.backward()
+    return h1.grad.numpy(), g.grad.numpy(), y.detach().numpy()
+
+
+def test_rmsnorm_bwd_matches_autograd():
+    c = _rbwd_case()
+    dh1, dg, y = _autograd_rmsnorm_bwd(c)
+    res = _rbwd(c)
+    assert rel(res["dh1"], dh1) < 1e-12
+    assert rel(res["dgamma"], dg) < 1e-12
+    assert rel(res["y"], y) < 1e-13
+    assert rel(res["s_out"], res["s"]) < 1e-12   # key design 3: the statistic from dY . y
+
+
+def test_rmsnorm_bwd_row_col_sampling_and_tile_partials():
+    c = _rbwd_case(seed=31, M=600, D=24, N=20)
+    full = _rbwd(c)
+    rows = np.array([0, 5, 255, 256, 599])
+    sub = _rbwd(c, rows=rows)
+    for k in ("r", "s", "s_out", "dh1"):
+        assert np.allclose(sub[k], full[k][rows], rtol=1e-13, atol=0), k
+    cols = np.array([0, 7, 23])
+    sc = _rbwd(c, cols=cols)
+    assert np.allclose(sc["dgamma"], full["dgamma"][cols], rtol=1e-13, atol=1e-15)
+    # 3 row tiles of 256 (the last one ragged, 88 rows) add up to dgamma
+    assert full["dgamma_partials"].shape == (3, 24)
+    assert np.allclose(full["dgamma_partials"].sum(axis=0), full["dgamma"], rtol=1e-13, atol=1e-15)
+    # brute force of the ragged tile: plain Python loops over rows 512..599, column 7
+    H1, G, W1, DY = (O.decode_bf16(c[k]) for k in ("h1", "gamma", "w1", "dy"))
+    acc = 0.0
+    for m in range(512, 600):
+        ms = sum(float(v) * float(v) for v in H1[m]) / 24
+        r = 1.0 / math.sqrt(ms + c["eps"])
+        dO = sum(float(DY[m, j]) * float(W1[7, j]) for j in range(20))
+        acc += dO * r * float(H1[m, 7])
+    assert abs(full["dgamma_partials"][2, 7] - acc) <= 1e-12 * max(1.0, abs(acc))
+
+
+def test_planted_rmsnorm_bwd_mistakes_fail_pin():
+    c = _rbwd_case(seed=32)
+    dh1, dg, _ = _autograd_rmsnorm_bwd(c)
+    res = _rbwd(c)
+    r, s, dO = res["r"], res["s"], res["dO"]
+    H1, G, GR = (O.decode_bf16(c[k]) for k in ("h1", "gamma", "g_res"))
+    assert rel(res["dh1"], dh1) < 1e-12
+    planted = {
+        "r^3 in the statistic term": r[:, None] * G * dO - (r ** 3 * s)[:, None] * H1 + GR,
+        "gamma dropped": r[:, None] * dO - (r * r * s)[:, None] * H1 + GR,
+        "residual gradient dropped": r[:, None] * G * dO - (r * r * s)[:, None] * H1,
+    }
+    for name, bad in planted.items():
+        assert rel(bad, dh1) > 1e-3, name
+    assert rel((dO * H1).sum(axis=0), dg) > 1e-3          # dgamma without r

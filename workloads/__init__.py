@@ -140,6 +140,20 @@ def bwd_stats(seed: int = 4, M: int = 8192, D: int = 4096, N: int = 6144) -> Wor
                     dict(M=M, D=D, N=N))
 
 
+def rmsnorm_bwd_full(seed: int = 5, M: int = 8192, D: int = 4096, N: int = 6144) -> Workload:
+    """Rest of the RMSNorm backward at the backward workload's shapes: h1[M,D] ~ N(0,1);
+    gamma = 1 + 0.1 N(0,1); W1[D,N] ~ N(0,1/D); dY[M,N] ~ N(0,1e-2); residual-stream
+    gradient g_res[M,D] ~ N(0,1e-2); eps = 1e-5; drawn in that order."""
+    rng = _rng(seed)
+    h1 = normal_bf16(rng, (M, D), 1.0)
+    gamma = normal_bf16(rng, (D,), 0.1, 1.0)
+    w1 = normal_bf16(rng, (D, N), 1.0 / np.sqrt(D))
+    dy = normal_bf16(rng, (M, N), 0.1)
+    g_res = normal_bf16(rng, (M, D), 0.1)
+    return Workload(f"rmsnorm_bwd_M{M}_D{D}_N{N}", seed, dict(h1=h1, gamma=gamma, w1=w1, dy=dy, g_res=g_res),
+                    dict(M=M, D=D, N=N, eps=1e-5))
+
+
 # The five workloads at their stated sizes (seed i for workload i).
 WORKLOADS = {
     "tiny_fwd": tiny_fwd,
