@@ -293,6 +293,39 @@ def other_paths(coda, torch, reps):
         "hipblaslt": lambda: torch.matmul(dy, w1t)}, reps)
     fl = 2.0 * M * N * D
     out["gemm_rmsnorm_bwd_stats_8192x4096x6144"] = path_record(t, fl)
+    del dy, w1, h2, dh2, part, sv, w1t
+    torch.cuda.empty_cache()
+    # rest of the RMSNorm backward (dh1 with the residual-stream gradient, dgamma)
+    wl = W.rmsnorm_bwd_full()
+    dy, w1, h1, g, gres = (to_dev(wl[k]) for k in ("dy", "w1", "h1", "gamma", "g_res"))
+    M, D, N, eps = wl["M"], wl["D"], wl["N"], wl["eps"]
+    hf = h1.float()
+    r = torch.rsqrt((hf * hf).mean(dim=1) + eps).contiguous()
+    y = coda.coda_gemm_rowscale((hf * g.float()).to(torch.bfloat16).contiguous(), w1, r)
+    sv = torch.empty((M,), dtype=torch.float32, device="cuda")
+    dh1 = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
+    pg = torch.empty((coda.num_row_tiles(M), D), dtype=torch.float32, device="cuda")
+    dg = torch.empty((D,), dtype=torch.float32, device="cuda")
+    dO = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
+    w1t = w1.t().contiguous()
+
+    def unfused():
+        # grad GEMM storing dO, then the RMSNorm backward as separate (torch eager) operators
+        coda.coda_baseline_gemm(dy, w1, b_kn=False, c=dO)
+        d = dO.float()
+        rr = r[:, None]
+        o = hf * rr * g.float()
+        ss = (d * o).mean(dim=1, keepdim=True)
+        out_dh1 = (rr * g.float() * d - rr * rr * ss * hf + gres.float()).to(torch.bfloat16)
+        out_dg = (d * rr * hf).sum(dim=0)
+        return out_dh1, out_dg
+
+    t = time_interleaved({
+        "fused": lambda: coda.coda_rmsnorm_bwd(dy, w1, h1, g, r, y, g_res=gres, s=sv, dh1=dh1, dgamma_partials=pg,
+                                               dgamma=dg),
+        "unfused": unfused,
+        "hipblaslt": lambda: torch.matmul(dy, w1t)}, reps)
+    out["rmsnorm_bwd_dx_dgamma_8192x4096x6144"] = path_record(t, fl)
     return out
 
 

@@ -159,6 +159,55 @@ int coda_gemm_rmsnorm_bwd_stats(const uint16_t* dy, const uint16_t* w1, const ui
                                 float* s, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * The rest of the RMSNorm backward ([notes] key design 3 and the duality paragraph
+ * before its statistic; [pith] Fig. 9). Forward (key design 1, non-deferred form):
+ * r = 1/sqrt(mean(h1^2) + eps), o = r h1 * gamma (the GEMM2 input), y = o W1.
+ * Backward with upstream gradient dy [M,N]:
+ *   dO     = dy W1^T                      (grad GEMM, never written to HBM here)
+ *   s      = (1/D) sum_cols(dO * o) = (1/D) sum_j dy[m, j] y[m, j]   (key design 3:
+ *            the statistic is available before the grad GEMM, from the output side)
+ *   dh1    = r gamma dO - r^2 s h1 (+ g_res, the gradient reaching h1 through the
+ *            residual stream)           -> stored bf16 in the grad GEMM's epilogue
+ *   dgamma = sum_rows(dO r h1)          -> fp32 column partials per 256-row tile in the
+ *            epilogue, then a column reduction in the fixed order of the tiles.
+ * Layouts: dy [M,N] bf16; w1 [D,N] bf16 (the forward GEMM2 weight, read as W1^T);
+ * h1, g_res, dh1 [M,D] bf16; gamma [D] bf16; r, s [M] fp32; y [M,N] bf16 (the forward
+ * output); dgamma_partials [T, D] fp32 with T = coda_colstat_num_partials(M) (row tile
+ * t covers rows [256 t, 256 t + 256)); dgamma [D] fp32. Rules as for the other GEMMs:
+ * D % 8 == 0 and N % 8 == 0 (both >= 8); bf16 pointers 16-byte aligned, fp32 pointers
+ * 4-byte aligned; outputs must not overlap inputs or each other.
+ * ------------------------------------------------------------------------------- */
+/* T = ceil(rows / 256): row tiles of the dgamma column-partial workspace. Returns
+ * CODA_ERR_NULL or CODA_ERR_SHAPE (rows < 0). */
+int coda_colstat_num_partials(int rows, int* tiles);
+
+/* s[m] = (1/d) sum_j dy[m, j] y[m, j] for dy, y [M,N] bf16 (one wave per row, lane
+ * partial sums then a fixed butterfly: deterministic). d >= 1. M == 0 is a no-op. */
+int coda_rowdot_stat(const uint16_t* dy, const uint16_t* y, int M, int N, int d, float* s,
+                     void* stream);
+
+/* out[n] = sum_t partials[t, n], t = 0 .. tiles-1 in order, for partials [tiles, width]
+ * fp32; tiles == 0 writes zeros (partials may then be NULL). */
+int coda_colsum_reduce(const float* partials, int tiles, int width, float* out, void* stream);
+
+/* The grad GEMM dy W1^T with the RMSNorm-backward epilogue: dh1 and dgamma_partials as
+ * above, from the caller's r and s (e.g. s from coda_rowdot_stat, or from the epilogue
+ * of the GEMM that produced dy). g_res may be NULL (no residual-stream gradient).
+ * One launch; M == 0 is a no-op. */
+int coda_gemm_rmsnorm_bwd_dx(const uint16_t* dy, const uint16_t* w1, const uint16_t* h1,
+                             const uint16_t* gamma, const float* r, const float* s,
+                             const uint16_t* g_res, int M, int D, int N, uint16_t* dh1,
+                             float* dgamma_partials, void* stream);
+
+/* All of it: s from (dy, y), the grad GEMM with its epilogue, and dgamma. Three
+ * launches on `stream`. s [M], dh1, dgamma_partials and dgamma are outputs. With M == 0
+ * only dgamma is written (zeros: a sum over no rows), so dgamma is always required. */
+int coda_rmsnorm_bwd(const uint16_t* dy, const uint16_t* w1, const uint16_t* h1,
+                     const uint16_t* gamma, const float* r, const uint16_t* y,
+                     const uint16_t* g_res, int M, int D, int N, float* s, uint16_t* dh1,
+                     float* dgamma_partials, float* dgamma, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Unfused baselines, for measurement and numerics comparison only (not the fused
  * path): the same MFMA main loop with a plain store, and separate HBM-bound kernels
  * for what the fused epilogues do (the standard operator-by-operator path).

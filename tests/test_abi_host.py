@@ -140,3 +140,49 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros((8, 8), dtype=torch.bfloat16)
     with pytest.raises((ValueError, RuntimeError)):
         coda.coda_gemm_swiglu(x, torch.zeros((8, 16), dtype=torch.bfloat16))
+
+
+def test_rmsnorm_bwd_validation(L):
+    t = ctypes.c_int(-1)
+    assert L.coda_colstat_num_partials(513, ctypes.byref(t)) == OK and t.value == 3
+    assert L.coda_colstat_num_partials(0, ctypes.byref(t)) == OK and t.value == 0
+    assert L.coda_colstat_num_partials(-1, ctypes.byref(t)) == SHAPE
+    assert L.coda_colstat_num_partials(8, None) == NULL
+    # output-side statistic
+    assert L.coda_rowdot_stat(P, P, 64, 12, 64, P, None) == SHAPE        # N % 8 != 0
+    assert L.coda_rowdot_stat(P, P, 64, 64, 0, P, None) == SHAPE         # d < 1
+    assert L.coda_rowdot_stat(P, P, -1, 64, 64, P, None) == SHAPE
+    assert L.coda_rowdot_stat(None, P, 64, 64, 64, P, None) == NULL
+    assert L.coda_rowdot_stat(P + 8, P, 64, 64, 64, P, None) == ALIGN
+    assert L.coda_rowdot_stat(P, P, 64, 64, 64, P + 2, None) == ALIGN
+    assert L.coda_rowdot_stat(None, None, 0, 64, 64, None, None) == OK   # empty batch: no-op
+    # column reduction
+    assert L.coda_colsum_reduce(P, -1, 64, P, None) == SHAPE
+    assert L.coda_colsum_reduce(P, 2, 0, P, None) == SHAPE
+    assert L.coda_colsum_reduce(None, 2, 64, P, None) == NULL
+    assert L.coda_colsum_reduce(P, 2, 64, None, None) == NULL
+    assert L.coda_colsum_reduce(P + 2, 2, 64, P, None) == ALIGN
+    # grad GEMM with the RMSNorm-backward epilogue
+    #        dy w1 h1 gamma r  s  g_res   M   D   N  dh1 pgamma
+    good = [P, P, P, P, P, P, None, 64, 64, 64, P, P, None]
+    def dx(**kw):
+        a = list(good)
+        names = ["dy", "w1", "h1", "gamma", "r", "s", "g_res", "M", "D", "N", "dh1", "pgamma", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return L.coda_gemm_rmsnorm_bwd_dx(*a)
+    assert dx(D=12) == SHAPE and dx(N=4) == SHAPE and dx(M=-1) == SHAPE
+    for k in ("dy", "w1", "h1", "gamma", "r", "s", "dh1", "pgamma"):
+        assert dx(**{k: None}) == NULL, k
+    assert dx(h1=P + 8) == ALIGN and dx(g_res=P + 8) == ALIGN and dx(r=P + 2) == ALIGN
+    assert dx(M=0, dy=None, w1=None, h1=None, gamma=None, r=None, s=None, dh1=None, pgamma=None) == OK
+    # the combined call validates before launching anything
+    full = [P, P, P, P, P, P, None, 64, 64, 64, P, P, P, P, None]
+    bad = list(full); bad[5] = None      # y
+    assert L.coda_rmsnorm_bwd(*bad) == NULL
+    bad = list(full); bad[13] = None     # dgamma
+    assert L.coda_rmsnorm_bwd(*bad) == NULL
+    bad = list(full); bad[13] = P + 2
+    assert L.coda_rmsnorm_bwd(*bad) == ALIGN
+    bad = list(full); bad[8] = 20        # D % 8
+    assert L.coda_rmsnorm_bwd(*bad) == SHAPE

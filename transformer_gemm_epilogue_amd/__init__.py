@@ -60,6 +60,11 @@ SIGNATURES = {
     "coda_gemm_rope": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P],
     "coda_gemm_swiglu": [_P, _P, _I, _I, _I, _P, _P],
     "coda_gemm_rmsnorm_bwd_stats": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
+    "coda_colstat_num_partials": [_I, _P],
+    "coda_rowdot_stat": [_P, _P, _I, _I, _I, _P, _P],
+    "coda_colsum_reduce": [_P, _I, _I, _P, _P],
+    "coda_gemm_rmsnorm_bwd_dx": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P],
+    "coda_rmsnorm_bwd": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P],
     "coda_baseline_gemm": [_P, _P, _I, _I, _I, _I, _P, _P],
     "coda_baseline_residual_rmsnorm": [_P, _P, _P, _I, _I, _F, _P, _P, _P, _P],
     "coda_baseline_rope": [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P],
@@ -250,6 +255,74 @@ def coda_gemm_rmsnorm_bwd_stats(dy, w1, h2, dh2=None, partials=None, s=None, str
     _call("coda_gemm_rmsnorm_bwd_stats", _bf16(dy, "dy"), _bf16(w1, "w1"), _bf16(h2, "h2"), M, D, N,
           _bf16(dh2, "dh2"), _f32(partials, "partials"), _f32(s, "s"), _stream(stream))
     return dh2, partials, s
+
+
+def num_row_tiles(rows: int) -> int:
+    """Row tiles (of 256) of the column-partial workspace [tiles, D] of dgamma."""
+    t = ctypes.c_int(0)
+    _call("coda_colstat_num_partials", int(rows), ctypes.byref(t))
+    return t.value
+
+
+def _opt_bf16(t, name):
+    return ctypes.c_void_p(None) if t is None else _bf16(t, name)
+
+
+def coda_rowdot_stat(dy, y, d, s=None, stream=None):
+    """s[m] = (1/d) sum_j dy[m, j] y[m, j] (the statistic from the output side)."""
+    torch = _torch()
+    M, N = dy.shape
+    if y.shape != (M, N):
+        raise ValueError("coda_rowdot_stat: inconsistent shapes")
+    s = _empty((M,), torch.float32, dy) if s is None else s
+    _call("coda_rowdot_stat", _bf16(dy, "dy"), _bf16(y, "y"), M, N, int(d), _f32(s, "s"), _stream(stream))
+    return s
+
+
+def coda_colsum_reduce(partials, out=None, stream=None):
+    """out[n] = sum_t partials[t, n] in the order t = 0, 1, ..."""
+    torch = _torch()
+    T, W = partials.shape
+    out = _empty((W,), torch.float32, partials) if out is None else out
+    _call("coda_colsum_reduce", _f32(partials, "partials"), T, W, _f32(out, "out"), _stream(stream))
+    return out
+
+
+def coda_gemm_rmsnorm_bwd_dx(dy, w1, h1, gamma, r, s, g_res=None, dh1=None, dgamma_partials=None, stream=None):
+    """Grad GEMM dO = dy w1^T whose epilogue stores dh1 = r gamma dO - r^2 s h1 (+ g_res)
+    and the dgamma column partials. Returns (dh1, dgamma_partials)."""
+    torch = _torch()
+    M, N = dy.shape
+    D = w1.shape[0]
+    if w1.shape[1] != N or h1.shape != (M, D) or gamma.shape != (D,) or r.shape != (M,) or s.shape != (M,) \
+            or (g_res is not None and g_res.shape != (M, D)):
+        raise ValueError("coda_gemm_rmsnorm_bwd_dx: inconsistent shapes")
+    dh1 = _empty((M, D), torch.bfloat16, dy) if dh1 is None else dh1
+    dgamma_partials = _empty((num_row_tiles(M), D), torch.float32, dy) if dgamma_partials is None else dgamma_partials
+    _call("coda_gemm_rmsnorm_bwd_dx", _bf16(dy, "dy"), _bf16(w1, "w1"), _bf16(h1, "h1"), _bf16(gamma, "gamma"),
+          _f32(r, "r"), _f32(s, "s"), _opt_bf16(g_res, "g_res"), M, D, N, _bf16(dh1, "dh1"),
+          _f32(dgamma_partials, "dgamma_partials"), _stream(stream))
+    return dh1, dgamma_partials
+
+
+def coda_rmsnorm_bwd(dy, w1, h1, gamma, r, y, g_res=None, s=None, dh1=None, dgamma_partials=None, dgamma=None,
+                     stream=None):
+    """The rest of the RMSNorm backward: s from (dy, y), the grad GEMM with the
+    RMSNorm-backward epilogue, and dgamma. Returns (s, dh1, dgamma_partials, dgamma)."""
+    torch = _torch()
+    M, N = dy.shape
+    D = w1.shape[0]
+    if w1.shape[1] != N or h1.shape != (M, D) or gamma.shape != (D,) or r.shape != (M,) or y.shape != (M, N) \
+            or (g_res is not None and g_res.shape != (M, D)):
+        raise ValueError("coda_rmsnorm_bwd: inconsistent shapes")
+    s = _empty((M,), torch.float32, dy) if s is None else s
+    dh1 = _empty((M, D), torch.bfloat16, dy) if dh1 is None else dh1
+    dgamma_partials = _empty((num_row_tiles(M), D), torch.float32, dy) if dgamma_partials is None else dgamma_partials
+    dgamma = _empty((D,), torch.float32, dy) if dgamma is None else dgamma
+    _call("coda_rmsnorm_bwd", _bf16(dy, "dy"), _bf16(w1, "w1"), _bf16(h1, "h1"), _bf16(gamma, "gamma"),
+          _f32(r, "r"), _bf16(y, "y"), _opt_bf16(g_res, "g_res"), M, D, N, _f32(s, "s"), _bf16(dh1, "dh1"),
+          _f32(dgamma_partials, "dgamma_partials"), _f32(dgamma, "dgamma"), _stream(stream))
+    return s, dh1, dgamma_partials, dgamma
 
 
 # ------------------------------------------------------------------- unfused baselines

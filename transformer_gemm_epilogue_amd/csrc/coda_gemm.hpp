@@ -413,63 +413,103 @@ __device__ __forceinline__ char* stage_base(const LdsRing& lds, int wave) {
 
 // Walk a wave's accumulators row-major: op.row(r, v, pre) gets wave-local row r
 // (0..127), this lane's 4 fp32 values at features col4() .. col4() + 3, and what
-// op.fetch(r) loaded for that row. Side-input loads are issued before any staging: for
-// all 32 rows of the lane at once when a row's input is at most 8 bytes, else per half
-// of 16 rows. Their latency then overlaps the LDS traffic, and no load queues behind
-// earlier output stores (the vector-memory counter waits on stores and loads alike).
+// op.fetch(r) loaded for that row; it returns the row's statistic (kRowStat) and, for
+// ops with kColStat, adds its per-feature contribution into a column accumulator kept
+// here (returned: the sum over this lane's 32 rows). When a row's input is at most 8 bytes, the loads for
+// all 32 rows of the lane are issued before any staging, so their latency overlaps the
+// LDS traffic; larger inputs are fetched one quarter (8 rows per lane) ahead of the
+// quarter being walked, which bounds the registers they hold. Either way a row's loads
+// are issued before the output stores that precede its use, so none queues behind them
+// (the vector-memory counter waits on stores and loads alike).
 typedef f32x16_t AccTile[kNI][kMJ];
 
 template <class Op>
-__device__ __forceinline__ void epilogue_rows(AccTile& acc, const LdsRing& lds, const EpiLane& L, Op& op) {
+__device__ __forceinline__ f32x4_t epilogue_rows(AccTile& acc, const LdsRing& lds, const EpiLane& L, Op& op) {
+  f32x4_t col = {0.f, 0.f, 0.f, 0.f};  // column statistic of ops with kColStat (sum over this lane's rows)
   const uint32_t sb = lds_addr(stage_base(lds, L.wave));
   const int cq = L.lane & 15, rq = L.lane >> 4;
-  constexpr bool kFetchAll = sizeof(typename Op::Pre) <= 8;
-  typename Op::Pre pre2[2][16];
-  if constexpr (kFetchAll) {
+  typedef typename Op::Pre Pre;
+  // stage accumulator block j (32 tokens) at staging rows row0 .. row0 + 31
+  auto stage = [&](int j, int row0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int i = 0; i < kNI; ++i)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) pre2[h][q] = op.fetch(kStgRows * h + 32 * (q >> 3) + 8 * rq + (q & 7));
-  }
+      for (int g = 0; g < 4; ++g) {
+        const f32x16_t& a = acc[i][j];
+        f32x4_t v;
+        v.x = a[4 * g];
+        v.y = a[4 * g + 1];
+        v.z = a[4 * g + 2];
+        v.w = a[4 * g + 3];
+        *(lds_f32x4_ptr)(uintptr_t)(sb + stg_off(row0 + (L.lane & 31), 8 * i + 2 * g + (L.lane >> 5))) = v;
+      }
+  };
+  // rows row0 + 8 rq + it (it = 0..7) of the staging area are wave rows r0 + 8 rq + it
+  auto walk8 = [&](int row0, int r0, const Pre (&pre)[8], float (&stat)[8]) {
+    constexpr int kRd = sizeof(Pre) <= 8 ? 8 : 4;  // rows whose LDS reads are in flight together
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    typename Op::Pre(&pre)[16] = pre2[h];
-    if constexpr (!kFetchAll) {
+    for (int b = 0; b < 8 / kRd; ++b) {
+      f32x4_t v[kRd];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) pre[q] = op.fetch(kStgRows * h + 32 * (q >> 3) + 8 * rq + (q & 7));
+      for (int q = 0; q < kRd; ++q) v[q] = *(lds_f32x4_ptr)(uintptr_t)(sb + stg_off(row0 + 8 * rq + kRd * b + q, cq));
+#pragma unroll
+      for (int q = 0; q < kRd; ++q) {
+        const int r = r0 + 8 * rq + kRd * b + q;
+        if constexpr (Op::kColStat)
+          stat[kRd * b + q] = op.row(r, v[q], pre[kRd * b + q], col);
+        else
+          stat[kRd * b + q] = op.row(r, v[q], pre[kRd * b + q]);
+      }
     }
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-      for (int i = 0; i < kNI; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x16_t& a = acc[i][2 * h + jj];
-          f32x4_t v;
-          v.x = a[4 * g];
-          v.y = a[4 * g + 1];
-          v.z = a[4 * g + 2];
-          v.w = a[4 * g + 3];
-          *(lds_f32x4_ptr)(uintptr_t)(sb + stg_off(32 * jj + (L.lane & 31), 8 * i + 2 * g + (L.lane >> 5))) = v;
-        }
-    float stat[16];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      f32x4_t v[8];  // 8 rows' reads in flight together
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = *(lds_f32x4_ptr)(uintptr_t)(sb + stg_off(32 * b + 8 * rq + q, cq));
-#pragma unroll
-      for (int q = 0; q < 8; ++q) stat[8 * b + q] = op.row(kStgRows * h + 32 * b + 8 * rq + q, v[q], pre[8 * b + q]);
-    }
+  };
+  auto record = [&](int r0, const float (&stat)[8]) {
     if constexpr (Op::kRowStat) {
       // lane 0 of each 16-lane row group records the wave's total of its rows
       if (cq == 0) {
-        float* red = lds.red + (L.wm * kWavesN + L.wn) * 128 + kStgRows * h + 8 * rq;
+        float* red = lds.red + (L.wm * kWavesN + L.wn) * 128 + r0 + 8 * rq;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) red[32 * (q >> 3) + (q & 7)] = stat[q];
+        for (int it = 0; it < 8; ++it) red[it] = stat[it];
       }
     }
+  };
+  if constexpr (sizeof(Pre) <= 8) {
+    // small side inputs: all 32 rows of the lane are fetched before any staging, then
+    // the block is walked in two halves of 64 staged tokens
+    Pre pre[4][8];
+#pragma unroll
+    for (int j = 0; j < kMJ; ++j)
+#pragma unroll
+      for (int it = 0; it < 8; ++it) pre[j][it] = op.fetch(32 * j + 8 * rq + it);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      stage(2 * h, 0);
+      stage(2 * h + 1, 32);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        float stat[8];
+        walk8(32 * jj, 64 * h + 32 * jj, pre[2 * h + jj], stat);
+        record(64 * h + 32 * jj, stat);
+      }
+    }
+  } else {
+    // larger side inputs: quarters of 32 tokens, each staged on its own; the next
+    // quarter's fetches are in flight while this one is walked
+    Pre pre[2][8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) pre[0][it] = op.fetch(8 * rq + it);
+#pragma unroll
+    for (int j = 0; j < kMJ; ++j) {
+      stage(j, 0);
+      if (j + 1 < kMJ) {
+#pragma unroll
+        for (int it = 0; it < 8; ++it) pre[(j + 1) & 1][it] = op.fetch(32 * (j + 1) + 8 * rq + it);
+      }
+      float stat[8];
+      walk8(0, 32 * j, pre[j & 1], stat);
+      record(32 * j, stat);
+    }
   }
+  return col;
 }
 
 struct NoPre {};
@@ -512,6 +552,37 @@ __device__ __forceinline__ u32x2_t load_bf16x4(const uint16_t* __restrict__ base
   if (ok) v = *(const u32x2_t*)(base + idx);
   return v;
 }
+
+// Side inputs of the row-major walk are read through raw buffer descriptors over the
+// wave's own 128 rows: rows past M fall outside the range and read as zero, and a lane
+// whose features lie past the width uses an out-of-range offset, so the loads need no
+// branches (branch-wrapped loads leave the compiler only full vector-memory waits).
+struct WaveRowsBf16 {  // [M, ld] bf16, this lane's 4 features at column n
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t pitch, coff;
+  __device__ __forceinline__ WaveRowsBf16(const uint16_t* base, const EpiLane& L, int M, int ld, int n, bool nok) {
+    const int r0 = L.m0 + L.wm * 128;
+    const int rows = base ? max(0, min(128, M - r0)) : 0;  // 128 * 2^22 * 2 bytes < 2^31
+    rs = make_rsrc(base ? base + (size_t)max(r0, 0) * ld : base, (uint32_t)rows * (uint32_t)ld * 2u);
+    pitch = (uint32_t)ld * 2u;
+    coff = nok ? (uint32_t)n * 2u : kOutOfRange;
+  }
+  __device__ __forceinline__ u32x2_t load4(int r) const {
+    return __builtin_amdgcn_raw_buffer_load_b64(rs, coff == kOutOfRange ? kOutOfRange : (uint32_t)r * pitch + coff, 0,
+                                                0);
+  }
+};
+struct WaveRowsF32 {  // [M] fp32, one value per row
+  __amdgpu_buffer_rsrc_t rs;
+  __device__ __forceinline__ WaveRowsF32(const float* base, const EpiLane& L, int M) {
+    const int r0 = L.m0 + L.wm * 128;
+    const int rows = base ? max(0, min(128, M - r0)) : 0;
+    rs = make_rsrc(base ? base + max(r0, 0) : base, (uint32_t)rows * 4u);
+  }
+  __device__ __forceinline__ float load(int r) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)r * 4u, 0, 0));
+  }
+};
 __device__ __forceinline__ void store_bf16x4(uint16_t* __restrict__ base, size_t idx, float a, float b, float c,
                                              float d) {
   u32x2_t v;
@@ -530,6 +601,7 @@ struct EpiStore {
     const Args& a;
     int M, N, n;
     static constexpr bool kRowStat = false;
+    static constexpr bool kColStat = false;
     typedef NoPre Pre;
     __device__ __forceinline__ Pre fetch(int) const { return Pre{}; }
     __device__ __forceinline__ float row(int r, const f32x4_t& v, const Pre&) {
@@ -565,12 +637,11 @@ struct EpiResidualRmsPartials {
     int M, N, n;
     bool nok;
     float g0, g1, g2, g3;
+    WaveRowsBf16 z;
     static constexpr bool kRowStat = true;
+    static constexpr bool kColStat = false;
     typedef u32x2_t Pre;
-    __device__ __forceinline__ Pre fetch(int r) const {
-      const int m = L.token(r);
-      return load_bf16x4(a.z, (size_t)m * N + n, nok && m < M);
-    }
+    __device__ __forceinline__ Pre fetch(int r) const { return z.load4(r); }
     __device__ __forceinline__ float row(int r, const f32x4_t& v, const Pre& zz) {
       const int m = L.token(r);
       const bool ok = nok && m < M;
@@ -590,7 +661,8 @@ struct EpiResidualRmsPartials {
     const int n = L.col4();
     const bool nok = n < p.N;
     const u32x2_t gg = load_bf16x4(a.gamma, (size_t)n, nok);
-    Op op{L, lds, a, p.M, p.N, n, nok, bf16_lo(gg.x), bf16_hi(gg.x), bf16_lo(gg.y), bf16_hi(gg.y)};
+    Op op{L, lds, a, p.M, p.N, n, nok, bf16_lo(gg.x), bf16_hi(gg.x), bf16_lo(gg.y), bf16_hi(gg.y),
+          WaveRowsBf16(a.z, L, p.M, p.N, n, nok)};
     epilogue_rows(acc, lds, L, op);
     store_row_partials(lds, L, a.partials, a.nb, p.M);
   }
@@ -606,12 +678,11 @@ struct EpiRowScale {
     const EpiLane& L;
     const Args& a;
     int M, N, n;
+    WaveRowsF32 rv;
     static constexpr bool kRowStat = false;
+    static constexpr bool kColStat = false;
     typedef float Pre;
-    __device__ __forceinline__ Pre fetch(int r) const {
-      const int m = L.token(r);
-      return m < M ? a.r[m] : 0.f;
-    }
+    __device__ __forceinline__ Pre fetch(int r) const { return rv.load(r); }
     __device__ __forceinline__ float row(int r, const f32x4_t& v, const Pre& s) {
       const int m = L.token(r);
       if (m < M && n < N) store_bf16x4(a.y, (size_t)m * N + n, s * v.x, s * v.y, s * v.z, s * v.w);
@@ -621,7 +692,7 @@ struct EpiRowScale {
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
     const EpiLane L(m0, n0);
-    Op op{L, a, p.M, p.N, L.col4()};
+    Op op{L, a, p.M, p.N, L.col4(), WaveRowsF32(a.r, L, p.M)};
     epilogue_rows(acc, lds, L, op);
   }
 };
@@ -645,21 +716,20 @@ struct EpiRope {
     int M, N, n, half, pp, pos0;
     bool rot;
     static constexpr bool kRowStat = false;
+    static constexpr bool kColStat = false;
     struct Pre {
       float2 c, s;
     };
     __device__ __forceinline__ Pre fetch(int r) const {
+      // (m + pos_offset) mod seq_len from the wave's first token: r < 128 steps on. The
+      // index is a valid table entry for every lane and row (also rows past M and
+      // unrotated columns, whose values are not used), so the loads need no branch.
+      int pos = pos0 + r;
+      const int S = a.seq_len;
+      if (pos >= S) pos = pos - S < S ? pos - S : pos % S;
       Pre t;
-      t.c = make_float2(1.f, 1.f);
-      t.s = make_float2(0.f, 0.f);
-      if (rot && L.token(r) < M) {
-        // (m + pos_offset) mod seq_len from the wave's first token: r < 128 steps on
-        int pos = pos0 + r;
-        const int S = a.seq_len;
-        if (pos >= S) pos = pos - S < S ? pos - S : pos % S;
-        t.c = *(const float2*)(a.cos_t + (size_t)pos * half + pp);
-        t.s = *(const float2*)(a.sin_t + (size_t)pos * half + pp);
-      }
+      t.c = *(const float2*)(a.cos_t + (size_t)pos * half + pp);
+      t.s = *(const float2*)(a.sin_t + (size_t)pos * half + pp);
       return t;
     }
     __device__ __forceinline__ float row(int r, const f32x4_t& v, const Pre& t) {
@@ -702,6 +772,7 @@ struct EpiSwiGLU {
     const Args& a;
     int M, N, n;
     static constexpr bool kRowStat = false;
+    static constexpr bool kColStat = false;
     typedef NoPre Pre;
     __device__ __forceinline__ Pre fetch(int) const { return Pre{}; }
     __device__ __forceinline__ float row(int r, const f32x4_t& v, const Pre&) {
@@ -736,12 +807,11 @@ struct EpiDotRowPartials {
     const Args& a;
     int M, N, n;
     bool nok;
+    WaveRowsBf16 hv;
     static constexpr bool kRowStat = true;
+    static constexpr bool kColStat = false;
     typedef u32x2_t Pre;
-    __device__ __forceinline__ Pre fetch(int r) const {
-      const int m = L.token(r);
-      return load_bf16x4(a.h2, (size_t)m * N + n, nok && m < M);
-    }
+    __device__ __forceinline__ Pre fetch(int r) const { return hv.load4(r); }
     __device__ __forceinline__ float row(int r, const f32x4_t& v, const Pre& hh) {
       const int m = L.token(r);
       const bool ok = nok && m < M;
@@ -755,7 +825,7 @@ struct EpiDotRowPartials {
                                                const LdsRing& lds) {
     const EpiLane L(m0, n0);
     const int n = L.col4();
-    Op op{L, lds, a, p.M, p.N, n, n < p.N};
+    Op op{L, lds, a, p.M, p.N, n, n < p.N, WaveRowsBf16(a.h2, L, p.M, p.N, n, n < p.N)};
     epilogue_rows(acc, lds, L, op);
     store_row_partials(lds, L, a.partials, a.nb, p.M);
   }
