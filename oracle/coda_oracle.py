@@ -50,6 +50,16 @@ the design notes of the repository):
       dh1 = r gamma dO - r^2 s h1 with s = (1/d) sum_cols(dO * o), plus the gradient
       g_res that reaches h1 through the residual stream; dgamma = sum_rows(dO r h1).
       Column partials of dgamma are sums over 256-row tiles, like R2's row partials.
+  R9  SwiGLU backward ([notes] key design 2, last item; [pith] Fig. 7: the backward
+      maps one incoming gradient into gradients for both paired inputs): the grad GEMM
+      dOut = dY W_down^T (W_down [F, Dm] is the forward down projection) meets the
+      saved interleaved pre-activations h = [G_0, U_0, G_1, U_1, ...]; out =
+      silu(G) U gives dG = dOut U silu'(G), dU = dOut silu(G) with
+      silu'(g) = s(g) (1 + g (1 - s(g))), s the logistic function; dh is interleaved
+      like h.
+  R10 RoPE backward: the rotation is orthogonal, so the gradient through it is the
+      rotation by the negated angle (R5 with -pos); fused into the GEMM that produces
+      the gradient of the rotated Q and K, it is that GEMM's epilogue.
 """
 from __future__ import annotations
 
@@ -69,6 +79,9 @@ __all__ = [
     "gemm_swiglu",
     "gemm_rmsnorm_bwd_stats",
     "rmsnorm_bwd",
+    "silu_grad",
+    "gemm_swiglu_bwd",
+    "gemm_rope_bwd",
     "flops_gemm_rmsnorm_fwd",
 ]
 
@@ -298,6 +311,42 @@ def rmsnorm_bwd(h1, gamma, w1, dy, eps: float, g_res=None, rows=None, cols=None,
     parts = np.stack([contrib[t * tile_m:(t + 1) * tile_m].sum(axis=0) for t in range(nt)])
     return dict(r=r, y=y, dO=dO, s=s, s_out=s_out, dh1=dh1, dgamma=contrib.sum(axis=0),
                 dgamma_partials=parts, cols=c)
+
+
+def silu_grad(g: np.ndarray) -> np.ndarray:
+    """d/dg of g / (1 + exp(-g)) = s(g) + g s(g) (1 - s(g)), s the logistic function."""
+    sig = 1.0 / (1.0 + np.exp(-g))
+    return sig * (1.0 + g * (1.0 - sig))
+
+
+def gemm_swiglu_bwd(dy, w_down, h, rows=None) -> dict:
+    """SwiGLU backward through the grad GEMM of the down projection (reading R9).
+
+    dOut = dY W_down^T (dY [M, Dm], W_down [F, Dm]); with G = h[:, 0::2], U = h[:, 1::2]
+    the saved pre-activations, dG = dOut U silu'(G) and dU = dOut silu(G), returned
+    interleaved as dh [M, 2F] (dh[:, 2j] = dG_j, dh[:, 2j+1] = dU_j).
+    """
+    dout = matmul(_take_rows(_as_f64(dy), rows), _as_f64(w_down).T)
+    H = _take_rows(_as_f64(h), rows)
+    if H.shape[1] != 2 * dout.shape[1]:
+        raise ValueError("h must be [M, 2F] for dOut [M, F]")
+    G = H[:, 0::2]
+    U = H[:, 1::2]
+    dh = np.empty_like(H)
+    dh[:, 0::2] = dout * U * silu_grad(G)
+    dh[:, 1::2] = dout * silu(G)
+    return dict(dout=dout, dh=dh)
+
+
+def gemm_rope_bwd(x, w, n_q: int, n_k: int, n_v: int, head_dim: int, seq_len: int,
+                  pos_offset: int = 0, theta: float = 10000.0, rows=None) -> np.ndarray:
+    """The GEMM x W followed by the RoPE backward on Q and K (reading R10): each pair is
+    rotated by -pos * theta_p, the transpose of the forward rotation; V is unchanged."""
+    M = np.asarray(x).shape[0]
+    idx = np.arange(M) if rows is None else np.asarray(rows)
+    h = matmul(_take_rows(_as_f64(x), rows), w)
+    pos = (idx + pos_offset) % seq_len
+    return rope_rotate(h, -pos, n_q, n_k, n_v, head_dim, theta)
 
 
 def flops_gemm_rmsnorm_fwd(M: int, K: int, D: int, N1: int) -> int:

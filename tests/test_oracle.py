@@ -423,3 +423,84 @@ def test_planted_rmsnorm_bwd_mistakes_fail_pin():
     for name, bad in planted.items():
         assert rel(bad, dh1) > 1e-3, name
     assert rel((dO * H1).sum(axis=0), dg) > 1e-3          # dgamma without r
+
+
+# ------------------------------------------------------- SwiGLU and RoPE backward (R9, R10)
+def _swiglu_bwd_case(seed=40, M=24, Dm=20, F=18):
+    rng = np.random.default_rng(seed)
+    return (normal_bf16(rng, (M, Dm), 0.1), normal_bf16(rng, (F, Dm), 1 / math.sqrt(F)),
+            normal_bf16(rng, (M, 2 * F), 1.0))
+
+
+def _swiglu_autograd(dy, w_down, h):
+    # torch's silu (a library routine): out = silu(G) U, then the down projection
+    H = torch.from_numpy(O.decode_bf16(h)).requires_grad_(True)
+    out = torch.nn.functional.silu(H[:, 0::2]) * H[:, 1::2]
+    y = out @ torch.from_numpy(O.decode_bf16(w_down))
+    y.backward(torch.from_numpy(O.decode_bf16(dy)))
+    return H.grad.numpy()
+
+
+def test_swiglu_bwd_matches_autograd():
+    dy, w_down, h = _swiglu_bwd_case()
+    res = O.gemm_swiglu_bwd(dy, w_down, h)
+    assert rel(res["dh"], _swiglu_autograd(dy, w_down, h)) < 1e-13
+
+
+def test_silu_grad_pins():
+    g = np.array([-30.0, -2.5, -1e-3, 0.0, 1e-3, 0.7, 3.0, 30.0])
+    # central difference of scipy's logistic-based silu
+    e = 1e-6
+    fd = ((g + e) * scipy.special.expit(g + e) - (g - e) * scipy.special.expit(g - e)) / (2 * e)
+    assert np.allclose(O.silu_grad(g), fd, rtol=1e-7, atol=1e-9)
+    assert O.silu_grad(np.array([0.0]))[0] == 0.5        # s(0) = 1/2
+    assert abs(O.silu_grad(np.array([40.0]))[0] - 1.0) < 1e-12 and abs(O.silu_grad(np.array([-40.0]))[0]) < 1e-12
+
+
+def test_swiglu_bwd_rows_and_planted_mistakes():
+    dy, w_down, h = _swiglu_bwd_case(seed=41, M=30)
+    full = O.gemm_swiglu_bwd(dy, w_down, h)
+    rows = np.array([0, 7, 29])
+    sub = O.gemm_swiglu_bwd(dy, w_down, h, rows=rows)
+    assert np.allclose(sub["dh"], full["dh"][rows], rtol=1e-13, atol=0)
+    want = _swiglu_autograd(dy, w_down, h)
+    G, U = O.decode_bf16(h)[:, 0::2], O.decode_bf16(h)[:, 1::2]
+    d = full["dout"]
+    sig = scipy.special.expit(G)
+    for name, dG, dU in (("silu' = s(g) only", d * U * sig, d * G * sig),
+                         ("gate and up swapped", d * G * O.silu_grad(U), d * O.silu(U))):
+        bad = np.empty_like(full["dh"])
+        bad[:, 0::2], bad[:, 1::2] = dG, dU
+        assert rel(bad, want) > 1e-3, name
+
+
+def _torch_rope(h, pos, head_dim, theta):
+    # RoPE as a complex multiplication built from torch.polar (library routines)
+    M, W_ = h.shape
+    half = head_dim // 2
+    inv = theta ** (-2.0 * torch.arange(half, dtype=torch.float64) / head_dim)
+    ang = torch.from_numpy(pos.astype(np.float64))[:, None] * inv[None, :]
+    rot = torch.polar(torch.ones_like(ang), ang)                      # e^{i a}
+    z = torch.view_as_complex(h.reshape(M, W_ // head_dim, half, 2).contiguous())
+    return torch.view_as_real(z * rot[:, None, :]).reshape(M, W_)
+
+
+def test_rope_bwd_matches_autograd_and_inverts_forward():
+    rng = np.random.default_rng(42)
+    M, hd, nq, nk, nv = 9, 8, 16, 8, 8
+    h = rng.standard_normal((M, nq + nk + nv))
+    pos = (np.arange(M) + 3) % 7
+    H = torch.from_numpy(h).requires_grad_(True)
+    qk = _torch_rope(H[:, :nq + nk], pos, hd, 10000.0)
+    g = torch.from_numpy(rng.standard_normal((M, nq + nk + nv)))
+    (torch.cat([qk, H[:, nq + nk:]], dim=1) * g).sum().backward()
+    # the oracle's backward with the identity as GEMM operand reproduces autograd
+    got = O.gemm_rope_bwd(f32_to_bf16_bits(np.eye(M, dtype=np.float32)), g.numpy(), nq, nk, nv, hd, seq_len=7,
+                          pos_offset=3)
+    assert rel(got, H.grad.numpy()) < 1e-13
+    # backward after forward is the identity on every pair (an orthogonal rotation)
+    fwd = O.rope_rotate(h, pos, nq, nk, nv, hd, 10000.0)
+    assert rel(O.rope_rotate(fwd, -pos, nq, nk, nv, hd, 10000.0), h) < 1e-14
+    # planted: the forward sign in the backward is rejected
+    wrong = O.rope_rotate(g.numpy(), pos, nq, nk, nv, hd, 10000.0)
+    assert rel(wrong, H.grad.numpy()) > 1e-2

@@ -154,6 +154,32 @@ def rmsnorm_bwd_full(seed: int = 5, M: int = 8192, D: int = 4096, N: int = 6144)
                     dict(M=M, D=D, N=N, eps=1e-5))
 
 
+def swiglu_bwd(seed: int = 6, M: int = 8192, Dm: int = 8192, F: int = 4096) -> Workload:
+    """SwiGLU backward through the down projection's grad GEMM: saved interleaved
+    pre-activations h[M, 2F] ~ N(0,1); W_down[F, Dm] ~ N(0,1/F); dY[M, Dm] ~ N(0,1e-2),
+    drawn in that order."""
+    rng = _rng(seed)
+    h = normal_bf16(rng, (M, 2 * F), 1.0)
+    w_down = normal_bf16(rng, (F, Dm), 1.0 / np.sqrt(F))
+    dy = normal_bf16(rng, (M, Dm), 0.1)
+    return Workload(f"gemm_swiglu_bwd_M{M}_Dm{Dm}_F{F}", seed, dict(h=h, w_down=w_down, dy=dy),
+                    dict(M=M, Dm=Dm, F=F))
+
+
+def rope_bwd(seed: int = 7, M: int = 4096, K: int = 4096, n_q: int = 4096, n_k: int = 4096,
+             n_v: int = 4096, head_dim: int = 128, seq_len: int = 4096, pos_offset: int = 0,
+             theta: float = 10000.0) -> Workload:
+    """RoPE backward in the epilogue of the GEMM producing the rotated Q/K/V gradient, at
+    the RoPE workload's shapes: a[M,K] ~ N(0,1e-2); W[K, n_q+n_k+n_v] ~ N(0,1/K)."""
+    rng = _rng(seed)
+    N = n_q + n_k + n_v
+    x = normal_bf16(rng, (M, K), 0.1)
+    w = normal_bf16(rng, (K, N), 1.0 / np.sqrt(K))
+    return Workload(f"gemm_rope_bwd_M{M}_K{K}_N{N}", seed, dict(x=x, w=w),
+                    dict(M=M, K=K, n_q=n_q, n_k=n_k, n_v=n_v, head_dim=head_dim,
+                         seq_len=seq_len, pos_offset=pos_offset, theta=theta))
+
+
 # The five workloads at their stated sizes (seed i for workload i).
 WORKLOADS = {
     "tiny_fwd": tiny_fwd,
