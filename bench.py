@@ -326,6 +326,45 @@ def other_paths(coda, torch, reps):
         "unfused": unfused,
         "hipblaslt": lambda: torch.matmul(dy, w1t)}, reps)
     out["rmsnorm_bwd_dx_dgamma_8192x4096x6144"] = path_record(t, fl)
+    del dy, w1, h1, g, gres, hf, r, y, sv, dh1, pg, dg, dO, w1t
+    torch.cuda.empty_cache()
+    # SwiGLU backward on the down projection's grad GEMM
+    wl = W.swiglu_bwd()
+    dy, wd, h = (to_dev(wl[k]) for k in ("dy", "w_down", "h"))
+    M, Dm, F = wl["M"], wl["Dm"], wl["F"]
+    dh = torch.empty((M, 2 * F), dtype=torch.bfloat16, device="cuda")
+    dout = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    wdt = wd.t().contiguous()
+
+    def swiglu_bwd_unfused():
+        coda.coda_baseline_gemm(dy, wd, b_kn=False, c=dout)
+        d = dout.float()
+        gg, uu = h[:, 0::2].float(), h[:, 1::2].float()
+        sg = torch.sigmoid(gg)
+        return torch.stack((d * uu * sg * (1 + gg * (1 - sg)), d * gg * sg), dim=2).reshape(M, 2 * F).to(torch.bfloat16)
+
+    t = time_interleaved({
+        "fused": lambda: coda.coda_gemm_swiglu_bwd(dy, wd, h, dh=dh),
+        "unfused": swiglu_bwd_unfused,
+        "hipblaslt": lambda: torch.matmul(dy, wdt)}, reps)
+    out["gemm_swiglu_bwd_8192x8192x4096"] = path_record(t, 2.0 * M * Dm * F)
+    del dy, wd, h, dh, dout, wdt
+    torch.cuda.empty_cache()
+    # RoPE backward (inverse rotation) in the epilogue of the GEMM producing dQKV
+    wl = W.rope_bwd()
+    x, w = to_dev(wl["x"]), to_dev(wl["w"])
+    c, sn = coda.coda_rope_tables(wl["seq_len"], wl["head_dim"], wl["theta"])
+    sneg = (-sn).contiguous()
+    M, K, N = wl["M"], wl["K"], wl["n_q"] + wl["n_k"] + wl["n_v"]
+    q = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    hh = torch.empty_like(q)
+    args = (wl["n_q"], wl["n_k"], wl["n_v"], wl["head_dim"], wl["seq_len"], 0)
+    t = time_interleaved({
+        "fused": lambda: coda.coda_gemm_rope_bwd(x, w, c, sn, *args, out=q),
+        # the separate rotation kernel with a negated sine table is the same inverse rotation
+        "unfused": lambda: (coda.coda_baseline_gemm(x, w, c=hh), coda.coda_baseline_rope(hh, c, sneg, *args, out=q)),
+        "hipblaslt": lambda: torch.matmul(x, w)}, reps)
+    out["gemm_rope_bwd_4096x12288x4096"] = path_record(t, 2.0 * M * K * N)
     return out
 
 

@@ -144,6 +144,28 @@ int coda_gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t,
 int coda_gemm_swiglu(const uint16_t* x, const uint16_t* w, int M, int K, int F,
                      uint16_t* out, void* stream);
 
+/* RoPE backward ([notes] key design 2; [pith] Fig. 7; the rotation is orthogonal, so its
+ * gradient is the rotation by the negated angle): same arguments, layouts and rules as
+ * coda_gemm_rope, with every Q and K pair of out = x W rotated by -pos * theta_p. It is
+ * the epilogue of the GEMM that produces the gradient of the rotated Q and K. */
+int coda_gemm_rope_bwd(const uint16_t* x, const uint16_t* w, const float* cos_t,
+                       const float* sin_t, int M, int K, int n_q, int n_k, int n_v,
+                       int head_dim, int seq_len, int pos_offset, uint16_t* out,
+                       void* stream);
+
+/* SwiGLU backward pairwise map ([notes] key design 2, last item; [pith] Fig. 7: one
+ * incoming gradient becomes the gradients of both paired inputs), in the epilogue of the
+ * down projection's grad GEMM:
+ *   dOut = dy W_down^T          (dy [M,Dm] bf16, w_down [F,Dm] bf16: the forward's
+ *                                down-projection weight, read as W_down^T; not stored)
+ *   dh[m, 2j]   = dOut U silu'(G),  dh[m, 2j+1] = dOut silu(G)
+ * with G = h[m, 2j], U = h[m, 2j+1] the saved interleaved pre-activations h [M,2F] bf16
+ * and silu'(g) = s (1 + g (1 - s)), s = 1/(1 + exp(-g)). dh [M,2F] bf16 output.
+ * Rules: Dm % 8 == 0 (>= 8), F % 8 == 0 (>= 8); 16-byte aligned pointers. One launch;
+ * M == 0 is a no-op. */
+int coda_gemm_swiglu_bwd(const uint16_t* dy, const uint16_t* w_down, const uint16_t* h,
+                         int M, int Dm, int F, uint16_t* dh, void* stream);
+
 /* ---------------------------------------------------------------------------------
  * RMSNorm-backward row statistic from the grad GEMM's epilogue ([notes] key design 3):
  *   dh2 = dy W1^T                              (dy [M,N] bf16, w1 [D,N] bf16 -> dh2 [M,D])

@@ -1,0 +1,124 @@
+"""Parity of the pairwise backward epilogues (SwiGLU backward on the down projection's
+grad GEMM, RoPE backward as the inverse rotation) with the fp64 oracle, through the C
+ABI: small ragged cases element by element, the full-size workloads on sampled rows."""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_util import assert_close, bf16_bits, log, sample_rows, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def coda():
+    import torch
+    import transformer_gemm_epilogue_amd as c
+    assert torch.cuda.is_available()
+    c.lib()
+    return c
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def dec(t):
+    return O.decode_bf16(bf16_bits(t))
+
+
+# ----------------------------------------------------------------------- SwiGLU backward
+def run_swiglu_bwd(coda, wl):
+    dh = coda.coda_gemm_swiglu_bwd(to_dev_bf16(wl["dy"]), to_dev_bf16(wl["w_down"]), to_dev_bf16(wl["h"]))
+    sync()
+    return dec(dh)
+
+
+@pytest.mark.parametrize("shape", [(333, 200, 136), (256, 256, 128), (5, 64, 8), (700, 328, 264)])
+def test_swiglu_bwd_small_full_compare(coda, shape):
+    M, Dm, F = shape
+    log(f"swiglu_bwd M={M} Dm={Dm} F={F}")
+    wl = W.swiglu_bwd(seed=70 + M % 13, M=M, Dm=Dm, F=F)
+    got = run_swiglu_bwd(coda, wl)
+    ref = O.gemm_swiglu_bwd(wl["dy"], wl["w_down"], wl["h"])["dh"]
+    assert_close("dG", got[:, 0::2], ref[:, 0::2])
+    assert_close("dU", got[:, 1::2], ref[:, 1::2])
+
+
+def test_swiglu_bwd_saturated_gates(coda):
+    # gates far into both tails of the logistic (|G| up to ~40): finite, and still the oracle's values
+    wl = W.swiglu_bwd(seed=77, M=300, Dm=64, F=128)
+    h = O.decode_bf16(wl["h"]) * 12.0
+    from workloads import f32_to_bf16_bits
+    hb = f32_to_bf16_bits(h.astype(np.float32))
+    wl2 = dict(dy=wl["dy"], w_down=wl["w_down"], h=hb)
+    got = run_swiglu_bwd(coda, wl2)
+    ref = O.gemm_swiglu_bwd(wl2["dy"], wl2["w_down"], wl2["h"])["dh"]
+    assert np.all(np.isfinite(got))
+    assert_close("dh", got, ref)
+
+
+def test_swiglu_bwd_full_size_sampled(coda):
+    wl = W.swiglu_bwd()
+    log(f"swiglu_bwd {wl.name}")
+    got = run_swiglu_bwd(coda, wl)
+    rows = sample_rows(wl["M"], 40, seed=6)
+    ref = O.gemm_swiglu_bwd(wl["dy"], wl["w_down"], wl["h"], rows=rows)["dh"]
+    assert_close("dh", got[rows], ref)
+
+
+# ------------------------------------------------------------------------- RoPE backward
+def run_rope_bwd(coda, wl):
+    c, s = coda.coda_rope_tables(wl["seq_len"], wl["head_dim"], wl["theta"])
+    out = coda.coda_gemm_rope_bwd(to_dev_bf16(wl["x"]), to_dev_bf16(wl["w"]), c, s, wl["n_q"], wl["n_k"], wl["n_v"],
+                                  wl["head_dim"], wl["seq_len"], wl["pos_offset"])
+    sync()
+    return dec(out)
+
+
+def oracle_rope_bwd(wl, rows=None):
+    return O.gemm_rope_bwd(wl["x"], wl["w"], wl["n_q"], wl["n_k"], wl["n_v"], wl["head_dim"], wl["seq_len"],
+                           wl["pos_offset"], wl["theta"], rows=rows)
+
+
+@pytest.mark.parametrize("case", [
+    dict(M=600, K=200, n_q=256, n_k=128, n_v=128, head_dim=128, seq_len=300, pos_offset=7),
+    dict(M=70, K=64, n_q=64, n_k=64, n_v=64, head_dim=64, seq_len=70, pos_offset=5),
+])
+def test_rope_bwd_small_full_compare(coda, case):
+    log(f"rope_bwd {case}")
+    wl = W.rope_bwd(seed=13, **case)
+    assert_close("dqkv", run_rope_bwd(coda, wl), oracle_rope_bwd(wl))
+
+
+def test_rope_bwd_full_size_sampled(coda):
+    wl = W.rope_bwd()
+    log(f"rope_bwd {wl.name}")
+    got = run_rope_bwd(coda, wl)
+    rows = sample_rows(wl["M"], 48, seed=7)
+    ref = oracle_rope_bwd(wl, rows)
+    nqk = wl["n_q"] + wl["n_k"]
+    assert_close("dq", got[rows][:, :wl["n_q"]], ref[:, :wl["n_q"]])
+    assert_close("dk", got[rows][:, wl["n_q"]:nqk], ref[:, wl["n_q"]:nqk])
+    assert_close("dv", got[rows][:, nqk:], ref[:, nqk:])
+
+
+def test_rope_bwd_rotation_properties(coda):
+    # the forward and backward epilogues of the same GEMM: both keep every pair's norm,
+    # and they differ (the angle's sign)
+    wl = W.rope_bwd(seed=14, M=256, K=64, n_q=128, n_k=128, n_v=0, head_dim=64, seq_len=256, pos_offset=3)
+    import transformer_gemm_epilogue_amd as c
+    cos_t, sin_t = c.coda_rope_tables(wl["seq_len"], wl["head_dim"], wl["theta"])
+    x, w = to_dev_bf16(wl["x"]), to_dev_bf16(wl["w"])
+    args = (wl["n_q"], wl["n_k"], wl["n_v"], wl["head_dim"], wl["seq_len"], wl["pos_offset"])
+    fwd = dec(c.coda_gemm_rope(x, w, cos_t, sin_t, *args))
+    bwd = dec(c.coda_gemm_rope_bwd(x, w, cos_t, sin_t, *args))
+    plain = O.matmul(wl["x"], wl["w"])
+    # each pair keeps its norm under both rotations
+    for out in (fwd, bwd):
+        n_out = out[:, 0::2] ** 2 + out[:, 1::2] ** 2
+        n_ref = plain[:, 0::2] ** 2 + plain[:, 1::2] ** 2
+        assert np.allclose(n_out, n_ref, rtol=2e-2, atol=1e-4)
+    assert not np.allclose(fwd, bwd, atol=1e-3)

@@ -59,6 +59,8 @@ SIGNATURES = {
     "coda_rope_tables": [_P, _P, _I, _I, _D, _P],
     "coda_gemm_rope": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P],
     "coda_gemm_swiglu": [_P, _P, _I, _I, _I, _P, _P],
+    "coda_gemm_rope_bwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P],
+    "coda_gemm_swiglu_bwd": [_P, _P, _P, _I, _I, _I, _P, _P],
     "coda_gemm_rmsnorm_bwd_stats": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
     "coda_colstat_num_partials": [_I, _P],
     "coda_rowdot_stat": [_P, _P, _I, _I, _I, _P, _P],
@@ -218,16 +220,27 @@ def coda_rope_tables(seq_len, head_dim, theta=10000.0, device="cuda", stream=Non
     return cos_t, sin_t
 
 
-def coda_gemm_rope(x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset=0, out=None, stream=None):
+def _gemm_rope(name, x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, stream):
     torch = _torch()
     M, K = x.shape
     N = n_q + n_k + n_v
     if w.shape != (K, N):
-        raise ValueError("coda_gemm_rope: w must be [K, n_q + n_k + n_v]")
+        raise ValueError(f"{name}: w must be [K, n_q + n_k + n_v]")
     out = _empty((M, N), torch.bfloat16, x) if out is None else out
-    _call("coda_gemm_rope", _bf16(x, "x"), _bf16(w, "w"), _f32(cos_t, "cos_t"), _f32(sin_t, "sin_t"), M, K,
+    _call(name, _bf16(x, "x"), _bf16(w, "w"), _f32(cos_t, "cos_t"), _f32(sin_t, "sin_t"), M, K,
           n_q, n_k, n_v, head_dim, seq_len, pos_offset, _bf16(out, "out"), _stream(stream))
     return out
+
+
+def coda_gemm_rope(x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset=0, out=None, stream=None):
+    return _gemm_rope("coda_gemm_rope", x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out,
+                      stream)
+
+
+def coda_gemm_rope_bwd(x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset=0, out=None, stream=None):
+    """x w with every Q and K pair rotated by the negated angle (the RoPE backward)."""
+    return _gemm_rope("coda_gemm_rope_bwd", x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out,
+                      stream)
 
 
 def coda_gemm_swiglu(x, w, out=None, stream=None):
@@ -239,6 +252,20 @@ def coda_gemm_swiglu(x, w, out=None, stream=None):
     out = _empty((M, F), torch.bfloat16, x) if out is None else out
     _call("coda_gemm_swiglu", _bf16(x, "x"), _bf16(w, "w"), M, K, F, _bf16(out, "out"), _stream(stream))
     return out
+
+
+def coda_gemm_swiglu_bwd(dy, w_down, h, dh=None, stream=None):
+    """dOut = dy w_down^T mapped in the epilogue to the interleaved (gate, up) gradients
+    of the saved pre-activations h [M, 2F]. Returns dh [M, 2F]."""
+    torch = _torch()
+    M, Dm = dy.shape
+    F = w_down.shape[0]
+    if w_down.shape[1] != Dm or h.shape != (M, 2 * F):
+        raise ValueError("coda_gemm_swiglu_bwd: inconsistent shapes")
+    dh = _empty((M, 2 * F), torch.bfloat16, dy) if dh is None else dh
+    _call("coda_gemm_swiglu_bwd", _bf16(dy, "dy"), _bf16(w_down, "w_down"), _bf16(h, "h"), M, Dm, F,
+          _bf16(dh, "dh"), _stream(stream))
+    return dh
 
 
 def coda_gemm_rmsnorm_bwd_stats(dy, w1, h2, dh2=None, partials=None, s=None, stream=None):

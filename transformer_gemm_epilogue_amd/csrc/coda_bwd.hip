@@ -1,6 +1,7 @@
-// C-ABI entry points of the rest of the RMSNorm backward (declared in coda.h): the row
-// statistic from the output side, the grad GEMM with the RMSNorm-backward epilogue, and
-// the column reduction of the gamma-gradient partials.
+// C-ABI entry points of the backward epilogue programs (declared in coda.h): the rest of
+// the RMSNorm backward (the row statistic from the output side, the grad GEMM with the
+// RMSNorm-backward epilogue, the column reduction of the gamma-gradient partials) and
+// the SwiGLU backward pairwise map on the down projection's grad GEMM.
 #include "coda_abi.hpp"
 #include "coda_bwd.hpp"
 
@@ -164,6 +165,28 @@ int coda_rmsnorm_bwd(const uint16_t* dy, const uint16_t* w1, const uint16_t* h1,
     CODA_TRY(launch_dx(dy, w1, h1, gamma, r, s, g_res, M, D, N, dh1, dgamma_partials, st));
   }
   return launch_colsum(dgamma_partials, row_tiles(M), D, dgamma, st);
+}
+
+int coda_gemm_swiglu_bwd(const uint16_t* dy, const uint16_t* w_down, const uint16_t* h, int M, int Dm, int F,
+                         uint16_t* dh, void* stream) {
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(Dm));
+  if (F < 8 || F % 8 != 0 || 2LL * F > kMaxDim) return CODA_ERR_SHAPE;
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(dy);
+  CODA_NONNULL(w_down);
+  CODA_NONNULL(h);
+  CODA_NONNULL(dh);
+  CODA_ALIGN16(dy);
+  CODA_ALIGN16(w_down);
+  CODA_ALIGN16(h);
+  CODA_ALIGN16(dh);
+  // dy [M, Dm] times W_down^T: depth = Dm, output width = F; W_down [F, Dm] is the NK layout.
+  const GemmProblem p{dy, w_down, M, F, Dm};
+  const EpiSwiGLUBwd::Args ea{h, dh};
+  hipLaunchKernelGGL((gemm_epilogue_kernel<false, EpiSwiGLUBwd>), dim3(gemm_grid(M, F)), dim3(kThreads), 0,
+                     as_stream(stream), p, ea);
+  return launch_status();
 }
 
 }  // extern "C"

@@ -103,4 +103,55 @@ struct EpiRmsNormBwd {
 };
 static_assert(kRedFloats * 4 + kBM * 8 + 2 * kBN * 4 <= kSlotBytes, "row tables fit in the last slot");
 
+// ------------------------------------------------------------------------------------
+// SwiGLU backward ([notes] key design 2, last item; [pith] Fig. 7): the grad GEMM of the
+// down projection gives dOut = dY W_down^T, one gradient per SwiGLU output; the epilogue
+// maps each into the gradients of its (gate, up) pair from the saved interleaved
+// pre-activations h = [G_0, U_0, G_1, U_1, ...]:
+//   dG = dOut U silu'(G),  dU = dOut silu(G),  silu'(g) = s (1 + g (1 - s)), s = 1/(1+e^-g)
+// and stores them interleaved like h. A lane's 4 outputs j .. j+3 use and produce the 8
+// interleaved columns 2j .. 2j+7: one 16-byte load of h and one 16-byte store of dh.
+struct EpiSwiGLUBwd {
+  struct Args {
+    const uint16_t* h;  // [M, 2F] saved pre-activations (F = this GEMM's output width)
+    uint16_t* dh;       // [M, 2F]
+  };
+  __device__ __forceinline__ static uint32_t pair_grad(float d, uint32_t gu) {
+    const float g = bf16_lo(gu), u = bf16_hi(gu);
+    const float sg = 1.0f / (1.0f + __expf(-g));
+    return pack_bf16x2(d * u * (sg * (1.0f + g * (1.0f - sg))), d * (g * sg));
+  }
+  struct Op {
+    const EpiLane& L;
+    const Args& a;
+    int M, N, n;
+    bool nok;
+    WaveRowsBf16 hv;
+    static constexpr bool kRowStat = false;
+    static constexpr bool kColStat = false;
+    typedef u32x4_t Pre;
+    __device__ __forceinline__ Pre fetch(int r) const { return hv.load8(r); }
+    __device__ __forceinline__ float row(int r, const f32x4_t& v, const Pre& t) const {
+      const int m = L.token(r);
+      if (nok && m < M) {
+        u32x4_t o;
+        o.x = pair_grad(v.x, t.x);
+        o.y = pair_grad(v.y, t.y);
+        o.z = pair_grad(v.z, t.z);
+        o.w = pair_grad(v.w, t.w);
+        *(u32x4_t*)(a.dh + (size_t)m * (2 * (size_t)N) + 2 * n) = o;
+      }
+      return 0.f;
+    }
+  };
+  __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
+                                               const LdsRing& lds) {
+    const EpiLane L(m0, n0);
+    const int n = L.col4();
+    const bool nok = n < p.N;
+    Op op{L, a, p.M, p.N, n, nok, WaveRowsBf16(a.h, L, p.M, 2 * p.N, 2 * n, nok)};
+    epilogue_rows(acc, lds, L, op);
+  }
+};
+
 }  // namespace coda

@@ -125,9 +125,10 @@ int coda_gemm_rmsnorm_fwd(const uint16_t* x, const uint16_t* w0, const uint16_t*
   return run_gemm2(h2, w1, r, M, D, N1, y, s);
 }
 
-int coda_gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K,
-                   int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset, uint16_t* out,
-                   void* stream) {
+namespace {
+int gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K, int n_q,
+              int n_k, int n_v, int head_dim, int seq_len, int pos_offset, uint16_t* out, int inverse,
+              hipStream_t stream) {
   CODA_TRY(check_rows(M));
   CODA_TRY(check_depth_or_width(K));
   if (head_dim < 8 || head_dim % 8 != 0 || head_dim > kMaxDim) return CODA_ERR_SHAPE;
@@ -146,8 +147,23 @@ int coda_gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, con
   CODA_ALIGN16(out);
   if (!aligned(cos_t, 8) || !aligned(sin_t, 8)) return CODA_ERR_ALIGN;
   const GemmProblem p{x, w, M, (int)N, K};
-  const EpiRope::Args ea{cos_t, sin_t, out, n_q + n_k, head_dim, seq_len, pos_offset};
-  return launch_gemm<true, EpiRope>(p, ea, as_stream(stream));
+  const EpiRope::Args ea{cos_t, sin_t, out, n_q + n_k, head_dim, seq_len, pos_offset, inverse};
+  return launch_gemm<true, EpiRope>(p, ea, stream);
+}
+}  // namespace
+
+int coda_gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K,
+                   int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset, uint16_t* out,
+                   void* stream) {
+  return gemm_rope(x, w, cos_t, sin_t, M, K, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, 0,
+                   as_stream(stream));
+}
+
+int coda_gemm_rope_bwd(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K,
+                       int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset, uint16_t* out,
+                       void* stream) {
+  return gemm_rope(x, w, cos_t, sin_t, M, K, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, 1,
+                   as_stream(stream));
 }
 
 int coda_gemm_swiglu(const uint16_t* x, const uint16_t* w, int M, int K, int F, uint16_t* out, void* stream) {

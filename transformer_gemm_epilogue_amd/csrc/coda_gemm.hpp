@@ -571,6 +571,10 @@ struct WaveRowsBf16 {  // [M, ld] bf16, this lane's 4 features at column n
     return __builtin_amdgcn_raw_buffer_load_b64(rs, coff == kOutOfRange ? kOutOfRange : (uint32_t)r * pitch + coff, 0,
                                                 0);
   }
+  __device__ __forceinline__ u32x4_t load8(int r) const {  // 8 features starting at column n
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, coff == kOutOfRange ? kOutOfRange : (uint32_t)r * pitch + coff,
+                                                 0, 0);
+  }
 };
 struct WaveRowsF32 {  // [M] fp32, one value per row
   __amdgpu_buffer_rsrc_t rs;
@@ -699,7 +703,9 @@ struct EpiRowScale {
 
 // ------------------------------------------------------- QKV projection + RoPE on Q, K
 // A lane's 4 features are two (even, odd) pairs of one head (4 | head_dim), rotated by
-// the angles of pair indices pp, pp + 1 at the token's position.
+// the angles of pair indices pp, pp + 1 at the token's position. With `inverse` set the
+// rotation is by the negated angle: the RoPE backward, applied in the epilogue of the
+// GEMM that produces the gradient of the rotated Q and K.
 struct EpiRope {
   struct Args {
     const float* cos_t;
@@ -709,6 +715,7 @@ struct EpiRope {
     int head_dim;
     int seq_len;
     int pos_offset;
+    int inverse;  // 0: forward rotation, 1: rotation by the negated angle
   };
   struct Op {
     const EpiLane& L;
@@ -737,7 +744,8 @@ struct EpiRope {
       if (!(m < M && n < N)) return 0.f;
       float e0 = v.x, o0 = v.y, e1 = v.z, o1 = v.w;
       if (rot) {
-        const float2 c = t.c, s = t.s;
+        const float2 c = t.c;
+        const float2 s = a.inverse ? make_float2(-t.s.x, -t.s.y) : t.s;
         const float re0 = e0 * c.x - o0 * s.x, ro0 = e0 * s.x + o0 * c.x;
         const float re1 = e1 * c.y - o1 * s.y, ro1 = e1 * s.y + o1 * c.y;
         e0 = re0;
