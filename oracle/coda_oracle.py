@@ -60,6 +60,13 @@ the design notes of the repository):
   R10 RoPE backward: the rotation is orthogonal, so the gradient through it is the
       rotation by the negated angle (R5 with -pos); fused into the GEMM that produces
       the gradient of the rotated Q and K, it is that GEMM's epilogue.
+  R11 GEMM + cross-entropy ([notes] method overview: the cross-entropy log-sum-exp is a
+      cross-tile statistic produced as tile partials and reduced by an auxiliary
+      kernel; the five primitives, (5) stateful transforms such as an online
+      log-sum-exp): logits = x W are never stored; each 256-column tile yields, per row,
+      the log-sum-exp of its columns; the auxiliary step merges them,
+      lse = log sum_t exp(lse_t), and loss = lse - logits[label]. A label outside
+      [0, V) marks an ignored row: loss 0.
 """
 from __future__ import annotations
 
@@ -82,6 +89,8 @@ __all__ = [
     "silu_grad",
     "gemm_swiglu_bwd",
     "gemm_rope_bwd",
+    "logsumexp_rows",
+    "gemm_cross_entropy",
     "flops_gemm_rmsnorm_fwd",
 ]
 
@@ -347,6 +356,33 @@ def gemm_rope_bwd(x, w, n_q: int, n_k: int, n_v: int, head_dim: int, seq_len: in
     h = matmul(_take_rows(_as_f64(x), rows), w)
     pos = (idx + pos_offset) % seq_len
     return rope_rotate(h, -pos, n_q, n_k, n_v, head_dim, theta)
+
+
+def logsumexp_rows(z: np.ndarray) -> np.ndarray:
+    """log sum_j exp(z[i, j]) per row, shifted by the row maximum (exact in fp64 for the
+    ranges here); rows of -inf only give -inf."""
+    mx = z.max(axis=1)
+    safe = np.where(np.isfinite(mx), mx, 0.0)
+    return safe + np.log(np.exp(z - safe[:, None]).sum(axis=1))
+
+
+def gemm_cross_entropy(x, w, labels, rows=None, tile_n: int = PARTIAL_TILE_N) -> dict:
+    """Cross-entropy of the logits x W against integer labels (reading R11).
+
+    Returns, for the selected rows: the per-tile log-sum-exp partials [rows, nb] over
+    256-column tiles, the full lse, the target logit (0 for ignored rows), and
+    loss = lse - target (0 for ignored rows: label outside [0, V)).
+    """
+    z = matmul(_take_rows(_as_f64(x), rows), w)
+    V = z.shape[1]
+    lab = _take_rows(np.asarray(labels).astype(np.int64), rows)
+    nb = (V + tile_n - 1) // tile_n
+    tile_lse = np.stack([logsumexp_rows(z[:, t * tile_n:(t + 1) * tile_n]) for t in range(nb)], axis=1)
+    lse = logsumexp_rows(z)
+    valid = (lab >= 0) & (lab < V)
+    target = np.where(valid, z[np.arange(z.shape[0]), np.clip(lab, 0, V - 1)], 0.0)
+    loss = np.where(valid, lse - target, 0.0)
+    return dict(tile_lse=tile_lse, lse=lse, target=target, loss=loss, valid=valid)
 
 
 def flops_gemm_rmsnorm_fwd(M: int, K: int, D: int, N1: int) -> int:

@@ -504,3 +504,57 @@ def test_rope_bwd_matches_autograd_and_inverts_forward():
     # planted: the forward sign in the backward is rejected
     wrong = O.rope_rotate(g.numpy(), pos, nq, nk, nv, hd, 10000.0)
     assert rel(wrong, H.grad.numpy()) > 1e-2
+
+
+# ------------------------------------------------------------- GEMM + cross-entropy (R11)
+def _ce_case(seed=50, M=30, K=24, V=600):
+    rng = np.random.default_rng(seed)
+    x = normal_bf16(rng, (M, K), 1.0)
+    w = normal_bf16(rng, (K, V), 1 / math.sqrt(K))
+    labels = rng.integers(0, V, size=M).astype(np.int32)
+    labels[3] = -1          # ignored
+    labels[4] = V           # out of range: ignored
+    return x, w, labels
+
+
+def test_cross_entropy_matches_torch_and_scipy():
+    x, w, labels = _ce_case()
+    res = O.gemm_cross_entropy(x, w, labels)
+    z = O.matmul(x, w)
+    assert rel(res["lse"], scipy.special.logsumexp(z, axis=1)) < 1e-14
+    lab = torch.from_numpy(labels.astype(np.int64))
+    want = torch.nn.functional.cross_entropy(torch.from_numpy(z), lab.clamp(0, z.shape[1] - 1), reduction="none")
+    valid = (labels >= 0) & (labels < z.shape[1])
+    assert rel(res["loss"][valid], want.numpy()[valid]) < 1e-14
+    assert np.all(res["loss"][~valid] == 0) and np.all(res["target"][~valid] == 0)
+
+
+def test_cross_entropy_tile_partials_merge_and_closed_forms():
+    x, w, labels = _ce_case(seed=51, M=12, V=600)   # 3 tiles of 256, the last ragged (88)
+    res = O.gemm_cross_entropy(x, w, labels)
+    assert res["tile_lse"].shape == (12, 3)
+    z = O.matmul(x, w)
+    for t, (a, b) in enumerate(((0, 256), (256, 512), (512, 600))):
+        assert rel(res["tile_lse"][:, t], scipy.special.logsumexp(z[:, a:b], axis=1)) < 1e-14
+    assert rel(scipy.special.logsumexp(res["tile_lse"], axis=1), res["lse"]) < 1e-14
+    # constant logits c over V columns: lse = c + log V, loss = log V
+    const = np.full((2, 600), 3.25)
+    assert np.allclose(O.logsumexp_rows(const), 3.25 + math.log(600), rtol=1e-15)
+    # row sampling equals slicing
+    sub = O.gemm_cross_entropy(x, w, labels, rows=np.array([0, 5, 11]))
+    assert np.allclose(sub["loss"], res["loss"][[0, 5, 11]], rtol=1e-13, atol=0)
+
+
+def test_planted_cross_entropy_mistakes_fail_pin():
+    x, w, labels = _ce_case(seed=52)
+    z = O.matmul(x, w)
+    valid = (labels >= 0) & (labels < z.shape[1])
+    lab = torch.from_numpy(np.clip(labels, 0, z.shape[1] - 1).astype(np.int64))
+    want = torch.nn.functional.cross_entropy(torch.from_numpy(z), lab, reduction="none").numpy()[valid]
+    res = O.gemm_cross_entropy(x, w, labels)
+    idx = np.arange(z.shape[0])
+    off_by_one = res["lse"] - z[idx, np.clip(labels + 1, 0, z.shape[1] - 1)]
+    no_log = np.exp(res["lse"]) - res["target"]
+    tiles_summed = res["tile_lse"].sum(axis=1) - res["target"]      # adding tile lse instead of merging
+    for bad in (off_by_one, no_log, tiles_summed):
+        assert rel(bad[valid], want) > 1e-3

@@ -180,6 +180,20 @@ def rope_bwd(seed: int = 7, M: int = 4096, K: int = 4096, n_q: int = 4096, n_k: 
                          seq_len=seq_len, pos_offset=pos_offset, theta=theta))
 
 
+def cross_entropy(seed: int = 8, M: int = 4096, K: int = 4096, V: int = 32768, ignore_every: int = 0) -> Workload:
+    """GEMM + cross-entropy at the pages' M x vocab x K shapes: hidden x[M,K] ~ N(0,1);
+    W[K,V] ~ N(0,1/K) (logits ~ N(0,1)); labels uniform in [0, V); with ignore_every = k,
+    every k-th row's label is -1 (ignored). Drawn in that order."""
+    rng = _rng(seed)
+    x = normal_bf16(rng, (M, K), 1.0)
+    w = normal_bf16(rng, (K, V), 1.0 / np.sqrt(K))
+    labels = rng.integers(0, V, size=M, dtype=np.int64).astype(np.int32)
+    if ignore_every:
+        labels[::ignore_every] = -1
+    return Workload(f"gemm_cross_entropy_M{M}_K{K}_V{V}", seed, dict(x=x, w=w, labels=labels),
+                    dict(M=M, K=K, V=V))
+
+
 # The five workloads at their stated sizes (seed i for workload i).
 WORKLOADS = {
     "tiny_fwd": tiny_fwd,
