@@ -365,6 +365,30 @@ def other_paths(coda, torch, reps):
         "unfused": lambda: (coda.coda_baseline_gemm(x, w, c=hh), coda.coda_baseline_rope(hh, c, sneg, *args, out=q)),
         "hipblaslt": lambda: torch.matmul(x, w)}, reps)
     out["gemm_rope_bwd_4096x12288x4096"] = path_record(t, 2.0 * M * K * N)
+    del x, w, c, sn, sneg, q, hh
+    torch.cuda.empty_cache()
+    # GEMM + cross-entropy at the pages' two shapes (M x vocab x K); logits never stored
+    for M_, K_ in ((4096, 4096), (8192, 8192)):
+        wl = W.cross_entropy(M=M_, K=K_, ignore_every=97)
+        x, w = to_dev(wl["x"]), to_dev(wl["w"])
+        lab = torch.from_numpy(wl["labels"]).cuda()
+        lab64 = lab.long()
+        M, K, V = wl["M"], wl["K"], wl["V"]
+        tl = torch.empty((M, coda.num_partials(V)), dtype=torch.float32, device="cuda")
+        tg, ls, lo = (torch.empty((M,), dtype=torch.float32, device="cuda") for _ in range(3))
+        logits = torch.empty((M, V), dtype=torch.bfloat16, device="cuda")
+
+        def ce_unfused():
+            coda.coda_baseline_gemm(x, w, c=logits)
+            return torch.nn.functional.cross_entropy(logits.float(), lab64, reduction="none", ignore_index=-1)
+
+        t = time_interleaved({
+            "fused": lambda: coda.coda_gemm_cross_entropy(x, w, lab, tile_lse=tl, target=tg, lse=ls, loss=lo),
+            "unfused": ce_unfused,
+            "hipblaslt": lambda: torch.matmul(x, w)}, reps)
+        out[f"gemm_cross_entropy_{M}x{V}x{K}"] = path_record(t, 2.0 * M * K * V)
+        del x, w, lab, lab64, tl, tg, ls, lo, logits
+        torch.cuda.empty_cache()
     return out
 
 

@@ -230,6 +230,28 @@ int coda_rmsnorm_bwd(const uint16_t* dy, const uint16_t* w1, const uint16_t* h1,
                      float* dgamma_partials, float* dgamma, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * GEMM + cross-entropy ([notes] method overview: the cross-entropy log-sum-exp is a
+ * cross-tile statistic emitted as tile partials and merged by an auxiliary kernel; the
+ * five epilogue primitives, (5) stateful transforms such as an online log-sum-exp):
+ *   z = x W                         (x [M,K] bf16, w [K,V] bf16; z is never stored)
+ *   tile_lse[m, t] = log sum over the columns of 256-column tile t of exp(z[m, .])
+ *   target[m] = z[m, labels[m]]     (fp32, from the accumulator)
+ *   lse[m] = log sum_t exp(tile_lse[m, t])   (auxiliary merge, order t = 0, 1, ...)
+ *   loss[m] = lse[m] - target[m]
+ * labels [M] int32; a label outside [0, V) marks an ignored row: loss = target = 0 there.
+ * tile_lse [M, nb] fp32 workspace/output with nb = coda_rowstat_num_partials(V); target,
+ * lse, loss [M] fp32 outputs. Rules: K % 8 == 0, V % 8 == 0 (both >= 8); x, w 16-byte
+ * aligned, the rest 4-byte aligned. Two launches on `stream`; M == 0 is a no-op.
+ * ------------------------------------------------------------------------------- */
+int coda_gemm_cross_entropy(const uint16_t* x, const uint16_t* w, const int32_t* labels,
+                            int M, int K, int V, float* tile_lse, float* target, float* lse,
+                            float* loss, void* stream);
+/* The auxiliary merge alone (tile_lse and target from the epilogue above). nb must equal
+ * coda_rowstat_num_partials(V). */
+int coda_lse_reduce(const float* tile_lse, const int32_t* labels, int M, int nb, int V,
+                    float* target, float* lse, float* loss, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Unfused baselines, for measurement and numerics comparison only (not the fused
  * path): the same MFMA main loop with a plain store, and separate HBM-bound kernels
  * for what the fused epilogues do (the standard operator-by-operator path).

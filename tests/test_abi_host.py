@@ -186,3 +186,23 @@ def test_rmsnorm_bwd_validation(L):
     assert L.coda_rmsnorm_bwd(*bad) == ALIGN
     bad = list(full); bad[8] = 20        # D % 8
     assert L.coda_rmsnorm_bwd(*bad) == SHAPE
+
+
+def test_cross_entropy_validation(L):
+    #        x  w  labels M   K   V  tile target lse loss stream
+    good = [P, P, P, 64, 64, 64, P, P, P, P, None]
+    names = ["x", "w", "labels", "M", "K", "V", "tile_lse", "target", "lse", "loss", "stream"]
+    def ce(**kw):
+        a = list(good)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return L.coda_gemm_cross_entropy(*a)
+    assert ce(V=12) == SHAPE and ce(K=4) == SHAPE and ce(M=-1) == SHAPE
+    for k in ("x", "w", "labels", "tile_lse", "target", "lse", "loss"):
+        assert ce(**{k: None}) == NULL, k
+    assert ce(x=P + 8) == ALIGN and ce(labels=P + 2) == ALIGN and ce(loss=P + 1) == ALIGN
+    assert ce(M=0, x=None, w=None, labels=None, tile_lse=None, target=None, lse=None, loss=None) == OK
+    # the merge alone: nb must match the vocabulary's tile count
+    assert L.coda_lse_reduce(P, P, 64, 3, 512, P, P, P, None) == SHAPE
+    assert L.coda_lse_reduce(None, P, 64, 2, 512, P, P, P, None) == NULL
+    assert L.coda_lse_reduce(P, P, 0, 2, 512, None, None, None, None) == OK

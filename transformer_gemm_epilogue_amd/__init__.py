@@ -61,6 +61,8 @@ SIGNATURES = {
     "coda_gemm_swiglu": [_P, _P, _I, _I, _I, _P, _P],
     "coda_gemm_rope_bwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P],
     "coda_gemm_swiglu_bwd": [_P, _P, _P, _I, _I, _I, _P, _P],
+    "coda_gemm_cross_entropy": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P],
+    "coda_lse_reduce": [_P, _P, _I, _I, _I, _P, _P, _P, _P],
     "coda_gemm_rmsnorm_bwd_stats": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
     "coda_colstat_num_partials": [_I, _P],
     "coda_rowdot_stat": [_P, _P, _I, _I, _I, _P, _P],
@@ -266,6 +268,38 @@ def coda_gemm_swiglu_bwd(dy, w_down, h, dh=None, stream=None):
     _call("coda_gemm_swiglu_bwd", _bf16(dy, "dy"), _bf16(w_down, "w_down"), _bf16(h, "h"), M, Dm, F,
           _bf16(dh, "dh"), _stream(stream))
     return dh
+
+
+def _i32(t, name):
+    return _dev(t, _torch().int32, name)
+
+
+def coda_gemm_cross_entropy(x, w, labels, tile_lse=None, target=None, lse=None, loss=None, stream=None):
+    """Cross-entropy of the logits x w (never stored) against int32 labels (outside
+    [0, V): ignored, loss 0). Returns (loss, lse, target, tile_lse)."""
+    torch = _torch()
+    M, K = x.shape
+    V = w.shape[1]
+    if w.shape[0] != K or labels.shape != (M,):
+        raise ValueError("coda_gemm_cross_entropy: inconsistent shapes")
+    tile_lse = _empty((M, num_partials(V)), torch.float32, x) if tile_lse is None else tile_lse
+    target = _empty((M,), torch.float32, x) if target is None else target
+    lse = _empty((M,), torch.float32, x) if lse is None else lse
+    loss = _empty((M,), torch.float32, x) if loss is None else loss
+    _call("coda_gemm_cross_entropy", _bf16(x, "x"), _bf16(w, "w"), _i32(labels, "labels"), M, K, V,
+          _f32(tile_lse, "tile_lse"), _f32(target, "target"), _f32(lse, "lse"), _f32(loss, "loss"), _stream(stream))
+    return loss, lse, target, tile_lse
+
+
+def coda_lse_reduce(tile_lse, labels, V, target, lse=None, loss=None, stream=None):
+    """The auxiliary merge of per-tile log-sum-exp partials. Returns (loss, lse)."""
+    torch = _torch()
+    M, nb = tile_lse.shape
+    lse = _empty((M,), torch.float32, tile_lse) if lse is None else lse
+    loss = _empty((M,), torch.float32, tile_lse) if loss is None else loss
+    _call("coda_lse_reduce", _f32(tile_lse, "tile_lse"), _i32(labels, "labels"), M, nb, int(V),
+          _f32(target, "target"), _f32(lse, "lse"), _f32(loss, "loss"), _stream(stream))
+    return loss, lse
 
 
 def coda_gemm_rmsnorm_bwd_stats(dy, w1, h2, dh2=None, partials=None, s=None, stream=None):

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libcoda.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["coda_gemm.hip", "coda_aux.hip", "coda_bwd.hip"]
+SOURCES = ["coda_gemm.hip", "coda_aux.hip", "coda_bwd.hip", "coda_ce.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,93 @@
+// C-ABI entry points of GEMM + cross-entropy (declared in coda.h): the GEMM whose
+// epilogue emits per-tile log-sum-exp partials and the label logit, and the auxiliary
+// merge into lse and the loss.
+#include "coda_abi.hpp"
+#include "coda_ce.hpp"
+
+using namespace coda;
+
+namespace {
+
+// One thread per row: lse = M + log sum_t exp(lse_t - M) with M = max_t lse_t, the sum
+// in the order t = 0, 1, ..., nb-1; loss = lse - target for a label in [0, V), else 0
+// (and target is set to 0 for such an ignored row).
+constexpr int kLseThreads = 256;
+
+__global__ __launch_bounds__(kLseThreads) void lse_reduce_kernel(const float* __restrict__ P, const int32_t* labels,
+                                                                 int M, int nb, int V, float* __restrict__ target,
+                                                                 float* __restrict__ lse, float* __restrict__ loss) {
+  const int m = blockIdx.x * kLseThreads + threadIdx.x;
+  if (m >= M) return;
+  const float* row = P + (size_t)m * nb;
+  float mx = row[0];
+  for (int t = 1; t < nb; ++t) mx = fmaxf(mx, row[t]);
+  float s = 0.f;
+  for (int t = 0; t < nb; ++t) s += expf(row[t] - mx);
+  const float l = mx + logf(s);
+  const int lab = labels[m];
+  const bool valid = lab >= 0 && lab < V;
+  lse[m] = l;
+  if (valid) {
+    loss[m] = l - target[m];
+  } else {
+    loss[m] = 0.f;
+    target[m] = 0.f;
+  }
+}
+
+int check_ce_outputs(const int32_t* labels, float* target, float* lse, float* loss) {
+  CODA_NONNULL(labels);
+  CODA_NONNULL(target);
+  CODA_NONNULL(lse);
+  CODA_NONNULL(loss);
+  if (!aligned(labels, 4) || !aligned(target, 4) || !aligned(lse, 4) || !aligned(loss, 4)) return CODA_ERR_ALIGN;
+  return CODA_OK;
+}
+
+int launch_lse(const float* P, const int32_t* labels, int M, int nb, int V, float* target, float* lse, float* loss,
+               hipStream_t st) {
+  hipLaunchKernelGGL(lse_reduce_kernel, dim3((M + kLseThreads - 1) / kLseThreads), dim3(kLseThreads), 0, st, P,
+                     labels, M, nb, V, target, lse, loss);
+  return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int coda_lse_reduce(const float* tile_lse, const int32_t* labels, int M, int nb, int V, float* target, float* lse,
+                    float* loss, void* stream) {
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(V));
+  if (nb != (V + kBN - 1) / kBN) return CODA_ERR_SHAPE;
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(tile_lse);
+  if (!aligned(tile_lse, 4)) return CODA_ERR_ALIGN;
+  CODA_TRY(check_ce_outputs(labels, target, lse, loss));
+  return launch_lse(tile_lse, labels, M, nb, V, target, lse, loss, as_stream(stream));
+}
+
+int coda_gemm_cross_entropy(const uint16_t* x, const uint16_t* w, const int32_t* labels, int M, int K, int V,
+                            float* tile_lse, float* target, float* lse, float* loss, void* stream) {
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(K));
+  CODA_TRY(check_depth_or_width(V));
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(x);
+  CODA_NONNULL(w);
+  CODA_NONNULL(tile_lse);
+  CODA_ALIGN16(x);
+  CODA_ALIGN16(w);
+  if (!aligned(tile_lse, 4)) return CODA_ERR_ALIGN;
+  const int nb = (V + kBN - 1) / kBN;
+  CODA_TRY(check_ce_outputs(labels, target, lse, loss));
+  const hipStream_t st = as_stream(stream);
+  const GemmProblem p{x, w, M, V, K};
+  const EpiCrossEntropy::Args ea{labels, tile_lse, target, nb};
+  hipLaunchKernelGGL((gemm_epilogue_kernel<true, EpiCrossEntropy>), dim3(gemm_grid(M, V)), dim3(kThreads), 0, st, p,
+                     ea);
+  CODA_TRY(launch_status());
+  return launch_lse(tile_lse, labels, M, nb, V, target, lse, loss, st);
+}
+
+}  // extern "C"

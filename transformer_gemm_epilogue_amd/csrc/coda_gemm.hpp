@@ -44,6 +44,8 @@
 // never make an MFMA wait for reads issued after its operands.
 #pragma once
 
+#include <type_traits>
+
 #include "coda_common.hpp"
 
 namespace coda {
@@ -423,12 +425,23 @@ __device__ __forceinline__ char* stage_base(const LdsRing& lds, int wave) {
 // (the vector-memory counter waits on stores and loads alike).
 typedef f32x16_t AccTile[kNI][kMJ];
 
+// Type of an op's row statistic: Op::Stat if it declares one, else float.
+template <class Op, class = void>
+struct StatOf {
+  typedef float type;
+};
+template <class Op>
+struct StatOf<Op, std::void_t<typename Op::Stat>> {
+  typedef typename Op::Stat type;
+};
+
 template <class Op>
 __device__ __forceinline__ f32x4_t epilogue_rows(AccTile& acc, const LdsRing& lds, const EpiLane& L, Op& op) {
   f32x4_t col = {0.f, 0.f, 0.f, 0.f};  // column statistic of ops with kColStat (sum over this lane's rows)
   const uint32_t sb = lds_addr(stage_base(lds, L.wave));
   const int cq = L.lane & 15, rq = L.lane >> 4;
   typedef typename Op::Pre Pre;
+  typedef typename StatOf<Op>::type Stat;
   // stage accumulator block j (32 tokens) at staging rows row0 .. row0 + 31
   auto stage = [&](int j, int row0) {
 #pragma unroll
@@ -445,7 +458,7 @@ __device__ __forceinline__ f32x4_t epilogue_rows(AccTile& acc, const LdsRing& ld
       }
   };
   // rows row0 + 8 rq + it (it = 0..7) of the staging area are wave rows r0 + 8 rq + it
-  auto walk8 = [&](int row0, int r0, const Pre (&pre)[8], float (&stat)[8]) {
+  auto walk8 = [&](int row0, int r0, const Pre (&pre)[8], Stat (&stat)[8]) {
     constexpr int kRd = sizeof(Pre) <= 8 ? 8 : 4;  // rows whose LDS reads are in flight together
 #pragma unroll
     for (int b = 0; b < 8 / kRd; ++b) {
@@ -462,11 +475,11 @@ __device__ __forceinline__ f32x4_t epilogue_rows(AccTile& acc, const LdsRing& ld
       }
     }
   };
-  auto record = [&](int r0, const float (&stat)[8]) {
+  auto record = [&](int r0, const Stat (&stat)[8]) {
     if constexpr (Op::kRowStat) {
-      // lane 0 of each 16-lane row group records the wave's total of its rows
+      // lane 0 of each 16-lane row group records the wave's statistic of its rows
       if (cq == 0) {
-        float* red = lds.red + (L.wm * kWavesN + L.wn) * 128 + r0 + 8 * rq;
+        Stat* red = (Stat*)lds.red + (L.wm * kWavesN + L.wn) * 128 + r0 + 8 * rq;
 #pragma unroll
         for (int it = 0; it < 8; ++it) red[it] = stat[it];
       }
@@ -486,7 +499,7 @@ __device__ __forceinline__ f32x4_t epilogue_rows(AccTile& acc, const LdsRing& ld
       stage(2 * h + 1, 32);
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
-        float stat[8];
+        Stat stat[8];
         walk8(32 * jj, 64 * h + 32 * jj, pre[2 * h + jj], stat);
         record(64 * h + 32 * jj, stat);
       }
@@ -504,7 +517,7 @@ __device__ __forceinline__ f32x4_t epilogue_rows(AccTile& acc, const LdsRing& ld
 #pragma unroll
         for (int it = 0; it < 8; ++it) pre[(j + 1) & 1][it] = op.fetch(32 * (j + 1) + 8 * rq + it);
       }
-      float stat[8];
+      Stat stat[8];
       walk8(0, 32 * j, pre[j & 1], stat);
       record(32 * j, stat);
     }
