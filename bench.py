@@ -10,8 +10,11 @@ inputs with fp32 accumulation, synthetic seeded data already resident in HBM.
 Prints ONE JSON line. `value` is the algorithmic TFLOP/s of the step (2MKD + 2MDN1 per
 step) over the synchronize-bracketed wall time of `--steps` steps. Per-kernel durations
 come from HIP events recorded on the stream the kernels run on. The other fused paths
-(GEMM+RoPE, GEMM+SwiGLU, the backward statistic) and the unfused baselines are timed
-after the headline and reported under "paths" (context, not the headline).
+(GEMM+RoPE at 4096 and 8192 under both schedules, GEMM+SwiGLU, the backward statistic,
+the rest of the RMSNorm backward, the SwiGLU and RoPE backward maps, GEMM+cross-entropy)
+and the unfused baselines are timed after the headline and reported under "paths"
+(context, not the headline); so is the register-only MFMA rate the chip sustains on
+Gaussian operands under its power limit ("mfma_power_ceiling").
 """
 from __future__ import annotations
 
@@ -241,10 +244,15 @@ def unfused_fwd(coda, torch, b, reps):
 
 # ------------------------------------------------------------------ other fused paths
 def path_record(t, fl):
-    return dict(fused_us=round(t["fused"] * 1e3, 1), tflops=round(fl / (t["fused"] * 1e-3) / 1e12, 1),
-                unfused_us=round(t["unfused"] * 1e3, 1), speedup_vs_unfused=round(t["unfused"] / t["fused"], 3),
-                hipblaslt_gemm_only_us=round(t["hipblaslt"] * 1e3, 1),
-                hipblaslt_gemm_only_tflops=round(fl / (t["hipblaslt"] * 1e-3) / 1e12, 1))
+    rec = dict(fused_us=round(t["fused"] * 1e3, 1), tflops=round(fl / (t["fused"] * 1e-3) / 1e12, 1),
+               unfused_us=round(t["unfused"] * 1e3, 1), speedup_vs_unfused=round(t["unfused"] / t["fused"], 3),
+               hipblaslt_gemm_only_us=round(t["hipblaslt"] * 1e3, 1),
+               hipblaslt_gemm_only_tflops=round(fl / (t["hipblaslt"] * 1e-3) / 1e12, 1))
+    if "persistent" in t:  # the same fused computation under the persistent schedule
+        rec.update(persistent_us=round(t["persistent"] * 1e3, 1),
+                   persistent_tflops=round(fl / (t["persistent"] * 1e-3) / 1e12, 1),
+                   persistent_vs_per_tile=round(t["fused"] / t["persistent"], 3))
+    return rec
 
 
 def other_paths(coda, torch, reps):
@@ -260,11 +268,30 @@ def other_paths(coda, torch, reps):
     args = (wl["n_q"], wl["n_k"], wl["n_v"], wl["head_dim"], wl["seq_len"], 0)
     t = time_interleaved({
         "fused": lambda: coda.coda_gemm_rope(x, w, c, s, *args, out=qkv),
+        "persistent": lambda: coda.coda_gemm_rope_persistent(x, w, c, s, *args, out=qkv),
         "unfused": lambda: (coda.coda_baseline_gemm(x, w, c=h), coda.coda_baseline_rope(h, c, s, *args, out=qkv)),
         "hipblaslt": lambda: torch.matmul(x, w)}, reps)
     fl = 2.0 * M * K * N
     out["gemm_rope_qkv_4096x12288x4096"] = path_record(t, fl)
     del x, w, qkv, h
+    torch.cuda.empty_cache()
+    # GEMM + RoPE at the 8192 class (M = K = 8192, QKV width 3 x 8192), both schedules
+    log("paths: rope 8192 (generating inputs) ...")
+    wl = W.rope_qkv_8k()
+    x, w = to_dev(wl["x"]), to_dev(wl["w"])
+    c, s = coda.coda_rope_tables(wl["seq_len"], wl["head_dim"], wl["theta"])
+    M, K, N = wl["M"], wl["K"], wl["n_q"] + wl["n_k"] + wl["n_v"]
+    qkv = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    h = torch.empty_like(qkv)
+    args = (wl["n_q"], wl["n_k"], wl["n_v"], wl["head_dim"], wl["seq_len"], 0)
+    t = time_interleaved({
+        "fused": lambda: coda.coda_gemm_rope(x, w, c, s, *args, out=qkv),
+        "persistent": lambda: coda.coda_gemm_rope_persistent(x, w, c, s, *args, out=qkv),
+        "unfused": lambda: (coda.coda_baseline_gemm(x, w, c=h), coda.coda_baseline_rope(h, c, s, *args, out=qkv)),
+        "hipblaslt": lambda: torch.matmul(x, w)}, reps)
+    out["gemm_rope_qkv_8192x24576x8192"] = path_record(t, 2.0 * M * K * N)
+    del x, w, qkv, h, wl
+    torch.cuda.empty_cache()
     # GEMM + SwiGLU
     wl = W.swiglu()
     x, w = to_dev(wl["x"]), to_dev(wl["w"])
@@ -392,6 +419,31 @@ def other_paths(coda, torch, reps):
     return out
 
 
+def mfma_ceiling(coda, torch):
+    """Register-only MFMA rate (no memory traffic; the GEMM's per-wave shape and
+    occupancy) with operands drawn like the workloads' data (bf16 N(0,1)) and with
+    constant operands: under its power limit the chip's clock, and so the MFMA rate,
+    depends on how much the operands toggle. The Gaussian figure is the practical
+    ceiling for the headline workload beside the nominal peak."""
+    import workloads as W
+    rng = np.random.default_rng(17)
+    ops = {"gaussian": to_dev(W.normal_bf16(rng, (1 << 20, 8), 1.0)),
+           "constant_1.0": torch.ones((1 << 20) * 8, dtype=torch.bfloat16, device="cuda")}
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid, iters = 4 * cus, 5000
+    out = torch.empty((grid * 512,), dtype=torch.float32, device="cuda")
+    fl = grid * 8.0 * iters * 16 * 32768
+    res = {}
+    for name, o in ops.items():
+        t_end = time.perf_counter() + 0.5  # clock settle under this load
+        while time.perf_counter() < t_end:
+            coda.coda_baseline_mfma_loop(o, iters, grid, out=out)
+            torch.cuda.synchronize()
+        t = time_reps(lambda: coda.coda_baseline_mfma_loop(o, iters, grid, out=out), reps=5, warmup=1)
+        res[f"{name}_tflops"] = round(fl / (t["median_ms"] * 1e-3) / 1e12, 1)
+    return res
+
+
 def aux_reduce_sweep(coda, torch, reps):
     """Bandwidth of the auxiliary row reduction on partial buffers far above the 256 MiB
     Infinity Cache (at the forward workload the buffer is 0.5 MiB and latency-bound)."""
@@ -485,6 +537,10 @@ def main():
         torch.cuda.empty_cache()
         res["paths"] = other_paths(coda, torch, args.reps)
         torch.cuda.empty_cache()
+        res["mfma_power_ceiling"] = mfma_ceiling(coda, torch)
+        g = res["mfma_power_ceiling"]["gaussian_tflops"]
+        res["roofline"]["practical_peak_gaussian_operands"] = g
+        res["roofline"]["frac_of_practical_peak"] = round(res["roofline"]["achieved"] / g, 4)
         # the same sweep before any GEMM ran and after the GEMM paths (sustained MFMA load
         # leaves the GPU in a lower power state that also slows pure streaming kernels)
         res["aux_reduce_sweep"] = dict(before_gemms=aux_cool, after_gemms=aux_reduce_sweep(coda, torch, args.reps))

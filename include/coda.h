@@ -137,6 +137,18 @@ int coda_gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t,
                    const float* sin_t, int M, int K, int n_q, int n_k, int n_v, int head_dim,
                    int seq_len, int pos_offset, uint16_t* out, void* stream);
 
+/* coda_gemm_rope under the persistent schedule ([notes] main experiment table, "主实验":
+ * GEMM + RoPE measured at M = N = K = 4096 and 8192 with a 3N QKV width; a schedule
+ * variant of the same computation): min(tiles, CUs) workgroups walk the output
+ * tiles, and the last depth steps of a tile load the first two of the next, so their
+ * latency hides under the epilogue and no workgroup launch separates tiles. Same
+ * arguments, rules, errors and bit-identical output as coda_gemm_rope (K < 128 runs the
+ * one-workgroup-per-tile kernel). CODA_ERR_HIP also if the CU count cannot be read. */
+int coda_gemm_rope_persistent(const uint16_t* x, const uint16_t* w, const float* cos_t,
+                              const float* sin_t, int M, int K, int n_q, int n_k, int n_v,
+                              int head_dim, int seq_len, int pos_offset, uint16_t* out,
+                              void* stream);
+
 /* GEMM + SwiGLU ([notes] key design 2; [pith] Fig. 7): h = x W with x [M,K] bf16 and
  * w [K, 2F] bf16 whose columns interleave gate and up (even column 2j = G_j, odd
  * column 2j+1 = U_j); out [M,F] bf16 = silu(G) * U with silu(g) = g / (1 + exp(-g)).
@@ -275,6 +287,15 @@ int coda_baseline_rowdot(const uint16_t* a, const uint16_t* b, int M, int D, flo
                          void* stream);
 /* dst = src, `bytes` a positive multiple of 16: a plain copy kernel of known traffic. */
 int coda_baseline_copy(const void* src, void* dst, int64_t bytes, void* stream);
+/* Measurement probe (no step of the method): `grid` workgroups of 512 threads; thread g
+ * reads fragments 12 g .. 12 g + 11 (mod n_frag) of operands [n_frag, 8] bf16 once, then
+ * each wave runs `iters` rounds of 16 v_mfma_f32_32x32x16_bf16 on registers only;
+ * out [grid * 512] fp32 receives each thread's accumulator sum. FLOPs =
+ * grid * 8 * iters * 16 * 32768. With operands drawn like the workloads' data it gives
+ * the MFMA rate sustained under the chip's power limit (the practical ceiling beside the
+ * nominal peak). Rules: n_frag, iters >= 1; 1 <= grid <= 65535; operands 16-byte aligned. */
+int coda_baseline_mfma_loop(const uint16_t* operands, int n_frag, int iters, int grid,
+                            float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,6 +28,7 @@ __all__ = [
     "coda_rowstat_reduce",
     "coda_rope_tables",
     "coda_gemm_rope",
+    "coda_gemm_rope_persistent",
     "coda_gemm_swiglu",
     "coda_gemm_rmsnorm_bwd_stats",
     "coda_baseline_gemm",
@@ -58,6 +59,7 @@ SIGNATURES = {
     "coda_rowstat_reduce": [_P, _I, _I, _I, _F, _I, _P, _P],
     "coda_rope_tables": [_P, _P, _I, _I, _D, _P],
     "coda_gemm_rope": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P],
+    "coda_gemm_rope_persistent": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P],
     "coda_gemm_swiglu": [_P, _P, _I, _I, _I, _P, _P],
     "coda_gemm_rope_bwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P],
     "coda_gemm_swiglu_bwd": [_P, _P, _P, _I, _I, _I, _P, _P],
@@ -75,6 +77,7 @@ SIGNATURES = {
     "coda_baseline_swiglu": [_P, _I, _I, _P, _P],
     "coda_baseline_rowdot": [_P, _P, _I, _I, _P, _P],
     "coda_baseline_copy": [_P, _P, _I64, _P],
+    "coda_baseline_mfma_loop": [_P, _I, _I, _I, _P, _P],
 }
 
 
@@ -237,6 +240,13 @@ def _gemm_rope(name, x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_o
 def coda_gemm_rope(x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset=0, out=None, stream=None):
     return _gemm_rope("coda_gemm_rope", x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out,
                       stream)
+
+
+def coda_gemm_rope_persistent(x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset=0, out=None,
+                              stream=None):
+    """coda_gemm_rope under the persistent schedule (same output, bit for bit)."""
+    return _gemm_rope("coda_gemm_rope_persistent", x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset,
+                      out, stream)
 
 
 def coda_gemm_rope_bwd(x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset=0, out=None, stream=None):
@@ -444,3 +454,15 @@ def coda_baseline_copy(src, dst, stream=None):
     _call("coda_baseline_copy", ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
           src.numel() * src.element_size(), _stream(stream))
     return dst
+
+
+def coda_baseline_mfma_loop(operands, iters, grid, out=None, stream=None):
+    """Register-only MFMA loop over bf16 `operands` (numel a multiple of 8); returns the
+    per-thread sums [grid * 512] fp32. FLOPs = grid * 8 * iters * 16 * 32768."""
+    torch = _torch()
+    if operands.numel() % 8:
+        raise ValueError("coda_baseline_mfma_loop: operands must hold whole 8-element fragments")
+    out = _empty((grid * 512,), torch.float32, operands) if out is None else out
+    _call("coda_baseline_mfma_loop", _bf16(operands, "operands"), operands.numel() // 8, int(iters), int(grid),
+          _f32(out, "out"), _stream(stream))
+    return out

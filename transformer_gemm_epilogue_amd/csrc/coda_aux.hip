@@ -175,6 +175,52 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4_t* __restrict__ s
 
 inline unsigned blocks_for(long long n, int per_block) { return (unsigned)((n + per_block - 1) / per_block); }
 
+// Register-only MFMA loop, a measurement probe: each thread reads 12 operand fragments
+// once, then every wave runs `iters` rounds of 16 v_mfma_f32_32x32x16_bf16 on 8
+// independent accumulators (the GEMM's per-wave shape, 8 waves per workgroup, two per
+// SIMD) with no memory traffic in between. Fed with operands drawn like the workloads'
+// data, it shows the MFMA rate the chip sustains under its power limit.
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void mfma_loop_kernel(const bf16x8_t* __restrict__ ops, int n_frag, int iters, float* __restrict__ out) {
+  const long long gt = (long long)blockIdx.x * 512 + threadIdx.x;
+  bf16x8_t a[2], b[4], c[2], d[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    a[i] = ops[(gt * 12 + i) % n_frag];
+    c[i] = ops[(gt * 12 + 6 + i) % n_frag];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    b[j] = ops[(gt * 12 + 2 + j) % n_frag];
+    d[j] = ops[(gt * 12 + 8 + j) % n_frag];
+  }
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c[i], d[j], acc[i][j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s += acc[i][j][v];
+  out[gt] = s;
+}
+
 }  // namespace
 
 // Shared with the GEMM entry points (no argument checks: callers have checked).
@@ -296,6 +342,17 @@ int coda_baseline_copy(const void* src, void* dst, int64_t bytes, void* stream) 
   const unsigned grid = (unsigned)std::min<long long>(blocks_for(n16, 256), 256LL * 16);
   hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, as_stream(stream), (const u32x4_t*)src, (u32x4_t*)dst,
                      n16);
+  return launch_status();
+}
+
+int coda_baseline_mfma_loop(const uint16_t* operands, int n_frag, int iters, int grid, float* out, void* stream) {
+  if (n_frag < 1 || iters < 1 || grid < 1 || grid > 65535) return CODA_ERR_SHAPE;
+  CODA_NONNULL(operands);
+  CODA_NONNULL(out);
+  CODA_ALIGN16(operands);
+  if (!aligned(out, 4)) return CODA_ERR_ALIGN;
+  hipLaunchKernelGGL(mfma_loop_kernel, dim3(grid), dim3(512), 0, as_stream(stream), (const bf16x8_t*)operands, n_frag,
+                     iters, out);
   return launch_status();
 }
 

@@ -68,11 +68,11 @@ struct EpiRmsNormBwd {
   };
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
-    const EpiLane L(m0, n0);
+    const EpiLane L(m0, n0, lds.tid);
     const int M = p.M, N = p.N;
     float2* tab = (float2*)(lds.red + kRedFloats);   // 2 KiB after the row-partial area
     float* colred = lds.red + kRedFloats + 2 * kBM;  // [2][256] column sums of the two token-waves
-    const int t = threadIdx.x;
+    const int t = lds.tid;
     if (t < kBM) {
       const int m = m0 + t;
       const float rr = m < M ? a.r[m] : 0.f;
@@ -146,7 +146,7 @@ struct EpiSwiGLUBwd {
   };
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
-    const EpiLane L(m0, n0);
+    const EpiLane L(m0, n0, lds.tid);
     const int n = L.col4();
     const bool nok = n < p.N;
     Op op{L, a, p.M, p.N, n, nok, WaveRowsBf16(a.h, L, p.M, 2 * p.N, 2 * n, nok)};

@@ -53,13 +53,13 @@ struct EpiCrossEntropy {
   };
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
-    const EpiLane L(m0, n0);
+    const EpiLane L(m0, n0, lds.tid);
     const int n = L.col4();
     Op op{L, a, p.M, p.N, n, n < p.N, WaveRowsF32((const float*)a.labels, L, p.M)};
     epilogue_rows(acc, lds, L, op);
     __syncthreads();
     // merge the four feature-waves of each row in the order wn = 0, 1, 2, 3
-    const int t = threadIdx.x;
+    const int t = lds.tid;
     if (t < kBM) {
       const int wm = t >> 7, r = t & 127;
       const float2* st = (const float2*)lds.red + wm * kWavesN * 128 + r;

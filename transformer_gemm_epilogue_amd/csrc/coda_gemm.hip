@@ -16,6 +16,22 @@ int launch_gemm(const GemmProblem& p, const typename Epi::Args& ea, hipStream_t 
   return launch_status();
 }
 
+// Persistent schedule: min(tiles, CUs of the current device) workgroups walk the tiles
+// (one workgroup fills a CU's LDS); below the minimum depth the per-tile kernel runs
+// instead. Both give bit-identical results.
+template <bool kWKN, class Epi>
+int launch_gemm_persistent(const GemmProblem& p, const typename Epi::Args& ea, hipStream_t stream) {
+  if ((p.K + kBK - 1) / kBK < kPersistMinSteps) return launch_gemm<kWKN, Epi>(p, ea, stream);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus < 1)
+    return CODA_ERR_HIP;
+  const int tiles = gemm_grid(p.M, p.N);
+  const int grid = tiles < cus ? tiles : cus;
+  hipLaunchKernelGGL((gemm_persistent_kernel<kWKN, Epi>), dim3(grid), dim3(kThreads), 0, stream, p, ea);
+  return launch_status();
+}
+
 // Shape rules first; an empty batch (M == 0) needs no buffers at all, so pointers are
 // checked only when there is work to do.
 int check_gemm1(const uint16_t* x, const uint16_t* w0, const uint16_t* z, const uint16_t* gamma, int M,
@@ -128,7 +144,7 @@ int coda_gemm_rmsnorm_fwd(const uint16_t* x, const uint16_t* w0, const uint16_t*
 namespace {
 int gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K, int n_q,
               int n_k, int n_v, int head_dim, int seq_len, int pos_offset, uint16_t* out, int inverse,
-              hipStream_t stream) {
+              bool persistent, hipStream_t stream) {
   CODA_TRY(check_rows(M));
   CODA_TRY(check_depth_or_width(K));
   if (head_dim < 8 || head_dim % 8 != 0 || head_dim > kMaxDim) return CODA_ERR_SHAPE;
@@ -148,6 +164,7 @@ int gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, const fl
   if (!aligned(cos_t, 8) || !aligned(sin_t, 8)) return CODA_ERR_ALIGN;
   const GemmProblem p{x, w, M, (int)N, K};
   const EpiRope::Args ea{cos_t, sin_t, out, n_q + n_k, head_dim, seq_len, pos_offset, inverse};
+  if (persistent) return launch_gemm_persistent<true, EpiRope>(p, ea, stream);
   return launch_gemm<true, EpiRope>(p, ea, stream);
 }
 }  // namespace
@@ -155,14 +172,21 @@ int gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, const fl
 int coda_gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K,
                    int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset, uint16_t* out,
                    void* stream) {
-  return gemm_rope(x, w, cos_t, sin_t, M, K, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, 0,
+  return gemm_rope(x, w, cos_t, sin_t, M, K, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, 0, false,
+                   as_stream(stream));
+}
+
+int coda_gemm_rope_persistent(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M,
+                              int K, int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset,
+                              uint16_t* out, void* stream) {
+  return gemm_rope(x, w, cos_t, sin_t, M, K, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, 0, true,
                    as_stream(stream));
 }
 
 int coda_gemm_rope_bwd(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K,
                        int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset, uint16_t* out,
                        void* stream) {
-  return gemm_rope(x, w, cos_t, sin_t, M, K, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, 1,
+  return gemm_rope(x, w, cos_t, sin_t, M, K, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, 1, false,
                    as_stream(stream));
 }
 

@@ -64,10 +64,11 @@ constexpr int kXJ = 16 / kWaves;  // 1 KiB DMA instructions per wave per operand
 constexpr int kLoadsPerStep = 2 * kXJ;  // 16-byte DMA loads per thread per step
 constexpr int kTileBytes = kBM * kBK * 2;  // one operand tile per stage: 16 KiB
 constexpr int kSlotBytes = 2 * kTileBytes;  // one stage: X tile + W tile
-constexpr int kStgRows = 64;                // tokens a wave re-lays out at a time
-constexpr int kStgWaveBytes = kStgRows * kWaveN * 4;  // fp32: 16 KiB per wave
+constexpr int kStgRows = 32;                // tokens a wave re-lays out at a time
+constexpr int kStgWaveBytes = kStgRows * kWaveN * 4;  // fp32: 8 KiB per wave
 constexpr int kRedFloats = 2 * kWavesN * 128;
-static_assert(kWaves * kStgWaveBytes + 4 * kRedFloats <= kStages * kSlotBytes, "staging and red reuse the slots");
+static_assert(4 * kStgWaveBytes == kSlotBytes, "four waves' staging areas fill one slot");
+static_assert(4 * kRedFloats <= kSlotBytes, "the row exchange fits in one slot");
 static_assert(kStages * kSlotBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
 static_assert(kWaves == 2 * kWavesN && kWavesN * kWaveN == kBN, "wave layout covers the tile");
 
@@ -75,13 +76,17 @@ struct GemmProblem {
   const uint16_t* x;  // [M, K]
   const uint16_t* w;  // [K, N] (KN) or [N, K] (NK)
   int M, N, K;
+  int group_m = 0;    // token-tiles per raster group; 0: chosen from the shape (raster_group_m)
 };
 
-// LDS of one workgroup: five stage slots. After the main loop, slots 0..3 hold the eight
-// waves' epilogue staging areas and slot 4 the row-partial exchange area.
+// LDS of one workgroup: five stage slots (in the main loop's order), and the epilogue's
+// areas in three of them: staging of waves 0-3 (stg[0]) and 4-7 (stg[1]), and the
+// row-statistic exchange (red). tid is the thread index the epilogue works from.
 struct LdsRing {
   char* slot[kStages];
   float* red;
+  char* stg[2];
+  int tid;
 };
 
 // Swizzle of the four 16-byte chunks of a depth-contiguous 64-byte row (X and NK-W
@@ -102,29 +107,41 @@ __device__ __forceinline__ uint32_t nrow_off(int row, int chunk) {
   return ((uint32_t)row << 9) | (((uint32_t)chunk ^ swz_n(row)) << 4);
 }
 
-// Workgroup -> output tile: groups of 2 token-tiles walked feature-tile by feature-tile.
-// Consecutive workgroups go round-robin to the 8 XCDs, so each XCD receives tiles of one
-// token-tile parity and every fourth feature-tile: 8 X panels and 4 W panels shared by
-// its 32 concurrent tiles, which the XCD's L2 serves. (Measured on MI355X against other
-// groupings and an explicit XCD-contiguous remap; this order was the fastest.)
-constexpr int kGroupM = 2;
-__device__ __forceinline__ void tile_coords(int M, int N, int& m0, int& n0) {
+// Workgroup -> output tile: groups of G token-tiles walked feature-tile by feature-tile
+// (token tile fastest within a group). Consecutive workgroups go round-robin to the 8
+// XCDs. With G = 2 each XCD receives tiles of one token-tile parity and every fourth
+// feature-tile (8 X panels and 4 W panels shared by its 32 concurrent tiles, which its
+// L2 serves), and the 256 concurrent tiles cover 16 token-tiles x all features when the
+// width is 16 tiles: the best order measured on MI355X for weights that fit the 256 MiB
+// Infinity Cache (also against an explicit XCD-contiguous remap). A weight larger than
+// that would then be streamed from HBM again by every wave of 256 tiles; with G = 32
+// each wave instead covers up to 8192 tokens x 8 feature-tiles (an XCD: 4 X and 8 W
+// panels), the token rows stay cache-resident across waves and the weight is streamed
+// once (measured: GEMM + RoPE 8192 x 24576 x 8192 +11%, 8192 x 32768 x 8192 +16%,
+// 4096 x 32768 x 4096 +8%; no gain below the cache size).
+__host__ __device__ inline int raster_group_m(int M, int N, int K) {
+  const long long w_bytes = 2LL * N * K;
+  const long long x_group_bytes = 2LL * (M < 32 * kBM ? M : 32 * kBM) * K;
+  return (w_bytes > (192LL << 20) && x_group_bytes <= (160LL << 20)) ? 32 : 2;
+}
+__device__ __forceinline__ void tile_coords(int M, int N, int K, int group_m, int t, int& m0, int& n0) {
   const int mt = (M + kBM - 1) / kBM;
   const int nt = (N + kBN - 1) / kBN;
-  const int t = blockIdx.x;
-  const int group = t / (kGroupM * nt);
-  const int first_m = group * kGroupM;
-  const int gm = min(mt - first_m, kGroupM);
-  const int rem = t - group * kGroupM * nt;
+  const int G = group_m > 0 ? group_m : raster_group_m(M, N, K);
+  const int group = t / (G * nt);
+  const int first_m = group * G;
+  const int gm = min(mt - first_m, G);
+  const int rem = t - group * G * nt;
   m0 = (first_m + rem % gm) * kBM;
   n0 = (rem / gm) * kBN;
 }
 
-// Depth step a workgroup starts at: the K loop of each block is rotated by an eighth of
-// K per XCD (blockIdx % 8), so the XCDs stream different depth ranges of the shared
-// panels at any moment instead of all hitting the same addresses. The tile's sum covers
-// the same products; only the (fixed, deterministic) accumulation order changes.
-__device__ __forceinline__ int k_rotation(int KT) { return (int)((blockIdx.x % 8) * (KT / 8)); }
+// Depth step tile t starts at: the K loop is rotated by an eighth of K per XCD (t % 8,
+// the XCD that workgroup t, or a persistent workgroup t mod 8k, runs on), so the XCDs
+// stream different depth ranges of the shared panels at any moment instead of all
+// hitting the same addresses. The tile's sum covers the same products; only the
+// (fixed, deterministic) accumulation order changes, and it depends on t alone.
+__device__ __forceinline__ int k_rotation(int t, int KT) { return (t % 8) * (KT / 8); }
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -168,23 +185,33 @@ __device__ __forceinline__ void wait_vmcnt() {
 typedef __attribute__((address_space(3))) const bf16x8_t* lds_b128_ptr;
 typedef __attribute__((address_space(3))) i16x4_t* lds_tr_ptr;
 
+// DMA sources of one output tile: descriptors of its X rows and (NK) W rows, which of
+// this lane's KN-W chunks lie inside the width, and the tile's rotated first depth step.
+struct TileSrc {
+  i32x4_t xrs, wrs_nk;
+  int n0, kstart;
+  bool w_col_ok[kXJ];
+};
+
+typedef f32x16_t AccTile[kNI][kMJ];
+
 template <bool kWKN>
 struct Mainloop {
-  i32x4_t xrs, wrs_nk;    // descriptors of the tile's X rows and (NK) W rows
   uint32_t wave_u;        // wave index, wave-uniform
   uint32_t x_off[kXJ];    // byte offsets of this lane's X chunks (depth 0 of the tile)
   uint32_t x_kchunk[kXJ]; // logical depth chunk (0..3) of each X load
   uint32_t w_off[kXJ];    // KN: offset within the stage's depth rows; NK: like x_off
   uint32_t w_kchunk[kXJ];
-  bool w_col_ok[kXJ];
+  uint32_t w_col[kXJ];    // KN: first feature, within the tile, of this lane's chunk
+  const uint16_t* xbase;
   const uint16_t* wbase;
-  int M, N, K, m0, n0;
-  int KT, kstart;           // depth steps and the rotated first step
+  int M, N, K, KT;          // KT: depth steps
   uint32_t xr_off[2];       // operand read offsets within a slot, per k16 sub-step
   uint32_t wr_off[2][kNI][2];
 
-  __device__ __forceinline__ void init(const GemmProblem& p, int m0_, int n0_) {
-    const int tid = threadIdx.x, lane = tid & 63;
+  // Everything that does not depend on the output tile; tid is the thread index.
+  __device__ __forceinline__ void init(const GemmProblem& p, int tid) {
+    const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / kWavesN, wn = wave % kWavesN;
     wave_u = (uint32_t)wave;
@@ -192,13 +219,9 @@ struct Mainloop {
     N = p.N;
     K = p.K;
     KT = (K + kBK - 1) / kBK;
-    kstart = k_rotation(KT);
-    m0 = m0_;
-    n0 = n0_;
+    xbase = p.x;
     wbase = p.w;
     const uint32_t kb = (uint32_t)K * 2u;
-    xrs = rsrc_words(p.x + (size_t)m0 * K, (uint32_t)min(kBM, M - m0) * kb);
-    wrs_nk = kWKN ? rsrc_words(p.w, 0u) : rsrc_words(p.w + (size_t)n0 * K, (uint32_t)min(kBN, N - n0) * kb);
 #pragma unroll
     for (int j = 0; j < kXJ; ++j) {
       // X (and NK-W): instruction j of wave w fills rows (kXJ w + j)*16 .. +15 of the tile
@@ -210,13 +233,13 @@ struct Mainloop {
         // KN-W: instruction j of wave w fills depth rows (kXJ w + j)*2 .. +1
         const int wrow = (wave * kXJ + j) * 2 + (lane >> 5);
         const uint32_t wc = (uint32_t)(lane & 31) ^ swz_n(wrow);
-        w_col_ok[j] = n0 + 8 * (int)wc < N;
+        w_col[j] = 8u * wc;
         w_off[j] = ((uint32_t)wrow * (uint32_t)N + 8u * wc) * 2u;
         w_kchunk[j] = (uint32_t)wrow;
       } else {
         w_off[j] = x_off[j];
         w_kchunk[j] = c;
-        w_col_ok[j] = true;
+        w_col[j] = 0u;
       }
     }
     const int r32 = lane & 31, hs = lane >> 5;
@@ -246,34 +269,47 @@ struct Mainloop {
     }
   }
 
-  // DMA load number j (0 .. kLoadsPerStep-1) of the kt-th depth step (rotated) into
-  // `slot`. Steps past the end (kt >= KT) issue out-of-range loads that only zero-fill
-  // a slot nobody reads.
-  __device__ __forceinline__ void issue_one(char* slot, int kt, int j) const {
-    const int ksr = kt + kstart;
+  // Sources of tile number t at (m0, n0).
+  __device__ __forceinline__ TileSrc src(int t, int m0, int n0) const {
+    TileSrc s;
+    const uint32_t kb = (uint32_t)K * 2u;
+    s.xrs = rsrc_words(xbase + (size_t)m0 * K, (uint32_t)min(kBM, M - m0) * kb);
+    s.wrs_nk = kWKN ? rsrc_words(wbase, 0u) : rsrc_words(wbase + (size_t)n0 * K, (uint32_t)min(kBN, N - n0) * kb);
+    s.n0 = n0;
+    s.kstart = k_rotation(t, KT);
+#pragma unroll
+    for (int j = 0; j < kXJ; ++j) s.w_col_ok[j] = !kWKN || n0 + (int)w_col[j] < N;
+    return s;
+  }
+
+  // DMA load number j (0 .. kLoadsPerStep-1) of the tile's kt-th depth step (rotated)
+  // into `slot`. Steps past the end (kt >= KT) issue out-of-range loads that only
+  // zero-fill a slot nobody reads.
+  __device__ __forceinline__ void issue_one(const TileSrc& s, char* slot, int kt, int j) const {
+    const int ksr = kt + s.kstart;
     const int k0 = (kt >= KT) ? K : (ksr >= KT ? ksr - KT : ksr) * kBK;
     if (j < kXJ) {
       const uint32_t xs = lds_addr(slot) + wave_u * (kXJ * 1024u);
       const bool ok = k0 + 8 * (int)x_kchunk[j] < K;
-      dma16(xrs, xs + j * 1024u, ok ? x_off[j] + (uint32_t)k0 * 2u : kOutOfRange);
+      dma16(s.xrs, xs + j * 1024u, ok ? x_off[j] + (uint32_t)k0 * 2u : kOutOfRange);
     } else {
       const int jj = j - kXJ;
       const uint32_t ws = lds_addr(slot) + (uint32_t)kTileBytes + wave_u * (kXJ * 1024u);
       if constexpr (kWKN) {
         const int krows = max(0, min(kBK, K - k0));
-        const i32x4_t wrs = rsrc_words(wbase + (size_t)min(k0, K - 1) * N + n0,
-                                       krows ? ((uint32_t)krows * (uint32_t)N - (uint32_t)n0) * 2u : 0u);
-        dma16(wrs, ws + jj * 1024u, w_col_ok[jj] ? w_off[jj] : kOutOfRange);
+        const i32x4_t wrs = rsrc_words(wbase + (size_t)min(k0, K - 1) * N + s.n0,
+                                       krows ? ((uint32_t)krows * (uint32_t)N - (uint32_t)s.n0) * 2u : 0u);
+        dma16(wrs, ws + jj * 1024u, s.w_col_ok[jj] ? w_off[jj] : kOutOfRange);
       } else {
         const bool ok = k0 + 8 * (int)w_kchunk[jj] < K;
-        dma16(wrs_nk, ws + jj * 1024u, ok ? w_off[jj] + (uint32_t)k0 * 2u : kOutOfRange);
+        dma16(s.wrs_nk, ws + jj * 1024u, ok ? w_off[jj] + (uint32_t)k0 * 2u : kOutOfRange);
       }
     }
   }
 
-  __device__ __forceinline__ void issue(char* slot, int kt) const {
+  __device__ __forceinline__ void issue(const TileSrc& s, char* slot, int kt) const {
 #pragma unroll
-    for (int j = 0; j < kLoadsPerStep; ++j) issue_one(slot, kt, j);
+    for (int j = 0; j < kLoadsPerStep; ++j) issue_one(s, slot, kt, j);
   }
 
   __device__ __forceinline__ void read(const char* slot, int ks, bf16x8_t (&a)[kNI], bf16x8_t (&b)[kMJ]) const {
@@ -297,11 +333,58 @@ struct Mainloop {
   }
 };
 
+// Field-wise choice between two tiles' sources on a wave-uniform condition (kept in
+// registers; a reference chosen at run time would put both structs in scratch memory).
+__device__ __forceinline__ TileSrc pick(bool second, const TileSrc& a, const TileSrc& b) {
+  TileSrc s;
+  s.xrs.x = second ? b.xrs.x : a.xrs.x;
+  s.xrs.y = second ? b.xrs.y : a.xrs.y;
+  s.xrs.z = second ? b.xrs.z : a.xrs.z;
+  s.xrs.w = second ? b.xrs.w : a.xrs.w;
+  s.wrs_nk.x = second ? b.wrs_nk.x : a.wrs_nk.x;
+  s.wrs_nk.y = second ? b.wrs_nk.y : a.wrs_nk.y;
+  s.wrs_nk.z = second ? b.wrs_nk.z : a.wrs_nk.z;
+  s.wrs_nk.w = second ? b.wrs_nk.w : a.wrs_nk.w;
+  s.n0 = second ? b.n0 : a.n0;
+  s.kstart = second ? b.kstart : a.kstart;
+#pragma unroll
+  for (int j = 0; j < kXJ; ++j) s.w_col_ok[j] = second ? b.w_col_ok[j] : a.w_col_ok[j];
+  return s;
+}
+
+// Prologue: steps 0, 1, 2 and the X half of step 3 in flight; wait for step 0.
 template <bool kWKN>
-__device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int n0, const LdsRing& lds,
-                                              f32x16_t (&acc)[kNI][kMJ]) {
-  Mainloop<kWKN> ml;
-  ml.init(p, m0, n0);
+__device__ __forceinline__ void mainloop_prologue(const Mainloop<kWKN>& ml, const TileSrc& src, const LdsRing& lds) {
+#pragma unroll
+  for (int s = 0; s < 3; ++s) ml.issue(src, lds.slot[s], s);
+  ml.issue_one(src, lds.slot[3], 3, 0);
+  ml.issue_one(src, lds.slot[3], 3, 1);
+  wait_vmcnt<10>();
+  __builtin_amdgcn_s_barrier();
+}
+
+// Depth steps of the next tile that a persistent workgroup loads during the last steps
+// of the current one (into the slots the current tile has finished with); the other
+// three slots hold the epilogue's staging and row-exchange areas meanwhile.
+constexpr int kNextSteps = 2;
+
+// Start of a persistent workgroup's next tile, after its epilogue and a barrier: steps
+// 0 and 1 are already in LDS; put step 2 and the X half of step 3 in flight.
+template <bool kWKN>
+__device__ __forceinline__ void mainloop_resume(const Mainloop<kWKN>& ml, const TileSrc& src, const LdsRing& lds) {
+  ml.issue(src, lds.slot[2], 2);
+  ml.issue_one(src, lds.slot[3], 3, 0);
+  ml.issue_one(src, lds.slot[3], 3, 1);
+}
+
+// The depth loop of one tile, after its prologue (or resume). With kPersist and a next
+// tile, the loads of steps KT and KT+1 of the schedule are that tile's steps 0 and 1
+// (this needs KT >= 4, so that all of them fall inside this loop); otherwise loads past
+// the end zero-fill free slots. Returns once every load has landed and every wave is
+// done reading operands.
+template <bool kWKN, bool kPersist>
+__device__ __forceinline__ void mainloop_body(const Mainloop<kWKN>& ml, const TileSrc& cur, const TileSrc& nxt,
+                                              bool has_next, const LdsRing& lds, AccTile& acc) {
 #pragma unroll
   for (int i = 0; i < kNI; ++i)
 #pragma unroll
@@ -312,20 +395,24 @@ __device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int 
   const int KT = ml.KT;
   constexpr int kReads = kMJ + (kWKN ? 2 * kNI : kNI);  // LDS read instructions per k16 sub-step
   constexpr int kMfma = kNI * kMJ;                      // MFMAs per k16 sub-step
-  constexpr int L = kLoadsPerStep;
 
-  // prologue: steps 0, 1, 2 and the X half of step 3 in flight; wait for step 0
-#pragma unroll
-  for (int s = 0; s < 3; ++s) ml.issue(lds.slot[s], s);
-  ml.issue_one(lds.slot[3], 3, 0);
-  ml.issue_one(lds.slot[3], 3, 1);
-  wait_vmcnt<10>();
-  __builtin_amdgcn_s_barrier();
+  // load j of schedule step kk: in a tail step (kTail) of a persistent workgroup it may
+  // be a step of the next tile; elsewhere it is this tile's (or a zero fill)
+  auto issue_at = [&](char* slot, int kk, int j, auto tail) {
+    if constexpr (kPersist && decltype(tail)::value) {
+      const bool nx = has_next && kk >= KT && kk < KT + kNextSteps;
+      ml.issue_one(pick(nx, cur, nxt), slot, nx ? kk - KT : kk, j);
+    } else {
+      ml.issue_one(cur, slot, kk, j);
+    }
+  };
+  const std::false_type steady;
+  const std::true_type tail;
 
   bf16x8_t a0[kNI], b0[kMJ], a1[kNI], b1[kMJ];
   ml.read(lds.slot[0], 0, a0, b0);
 
-  auto step = [&](const int S, const int kt) {
+  auto step = [&](const int S, const int kt, auto kind) {
     ml.read(lds.slot[S], 1, a1, b1);
 #pragma unroll
     for (int i = 0; i < kNI; ++i)
@@ -334,8 +421,8 @@ __device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int 
     __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);  // sub-step-1 reads first
     __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);   // then the sub-step-0 MFMAs
     // W half of step kt+3 into the slot of kt-2 (free since the previous barrier)
-    ml.issue_one(lds.slot[(S + 3) % kStages], kt + 3, 2);
-    ml.issue_one(lds.slot[(S + 3) % kStages], kt + 3, 3);
+    issue_at(lds.slot[(S + 3) % kStages], kt + 3, 2, kind);
+    issue_at(lds.slot[(S + 3) % kStages], kt + 3, 3, kind);
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<8>();  // this thread's loads of step kt+1 have landed
     __builtin_amdgcn_s_barrier();
@@ -347,7 +434,7 @@ __device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int 
       const int i = r / kMJ, j = r % kMJ;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
       // X half of step kt+4 into the slot of kt-1 (free since this step's barrier)
-      if (r < 2) ml.issue_one(lds.slot[(S + 4) % kStages], kt + 4, r);
+      if (r < 2) issue_at(lds.slot[(S + 4) % kStages], kt + 4, r, kind);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       if (r < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
     }
@@ -358,19 +445,50 @@ __device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int 
   };
 
   int kt = 0;
-  for (; kt + kStages <= KT; kt += kStages) {
-    step(0, kt);
-    step(1, kt + 1);
-    step(2, kt + 2);
-    step(3, kt + 3);
-    step(4, kt + 4);
+  // steady state; a persistent workgroup leaves the last 4 to 8 steps, whose loads
+  // reach past this tile, to the tail below
+  constexpr int kLook = kPersist ? 4 : 0;
+  for (; kt + kStages + kLook <= KT; kt += kStages) {
+    step(0, kt, steady);
+    step(1, kt + 1, steady);
+    step(2, kt + 2, steady);
+    step(3, kt + 3, steady);
+    step(4, kt + 4, steady);
   }
-  if (kt < KT) step(0, kt);
-  if (kt + 1 < KT) step(1, kt + 1);
-  if (kt + 2 < KT) step(2, kt + 2);
-  if (kt + 3 < KT) step(3, kt + 3);
-  wait_vmcnt<0>();  // trailing zero-fill loads land before the epilogue reuses LDS
-  __syncthreads();  // all operand reads are done before the slots hold staging data
+  if constexpr (kPersist) {
+    step(0, kt, tail);
+    step(1, kt + 1, tail);
+    step(2, kt + 2, tail);
+    step(3, kt + 3, tail);
+    if (kt + 4 < KT) step(4, kt + 4, tail);
+    if (kt + 5 < KT) step(0, kt + 5, tail);
+    if (kt + 6 < KT) step(1, kt + 6, tail);
+    if (kt + 7 < KT) step(2, kt + 7, tail);
+  } else {
+    if (kt < KT) step(0, kt, steady);
+    if (kt + 1 < KT) step(1, kt + 1, steady);
+    if (kt + 2 < KT) step(2, kt + 2, steady);
+    if (kt + 3 < KT) step(3, kt + 3, steady);
+  }
+  wait_vmcnt<0>();  // zero-fill loads (and the next tile's first steps) have landed
+  __syncthreads();  // all operand reads are done before the free slots hold epilogue data
+}
+
+// The LDS of one workgroup as a ring whose logical slot s is physical slot
+// (s + rot) mod 5, with the epilogue's areas in the three physical slots from e on
+// (mod 5): staging of waves 0-3, staging of waves 4-7, row exchange.
+__device__ __forceinline__ char* phys_slot(char* smem, int i) {
+  return smem + (i >= kStages ? i - kStages : i) * kSlotBytes;
+}
+__device__ __forceinline__ LdsRing make_ring(char* smem, int rot, int e, int tid) {
+  LdsRing r;
+  r.tid = tid;
+#pragma unroll
+  for (int s = 0; s < kStages; ++s) r.slot[s] = phys_slot(smem, s + rot);
+  r.stg[0] = phys_slot(smem, e);
+  r.stg[1] = phys_slot(smem, e + 1);
+  r.red = (float*)phys_slot(smem, e + 2);
+  return r;
 }
 
 // ------------------------------------------------------------------------------------
@@ -378,8 +496,8 @@ __device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int 
 //   n = n0 + wn*64 + 32 i + 8 g + 4 (lane >> 5) + e,  (register v = 4 g + e)
 // for the token m = m0 + wm*128 + 32 j + (lane & 31): one lane spans 32 tokens, which
 // makes direct loads of per-element side inputs 8-byte gathers from 32 rows. So each
-// wave first re-lays its 128 x 64 fp32 block out row-major through a private 16 KiB LDS
-// area (64 tokens at a time) and then walks it with 16 lanes per token, 4 features per
+// wave first re-lays its 128 x 64 fp32 block out row-major through a private 8 KiB LDS
+// area (32 tokens at a time) and then walks it with 16 lanes per token, 4 features per
 // lane: side inputs (residual, gamma, rotary tables, saved activations) are read and
 // outputs written as whole 128-byte row segments, and a row statistic is a 16-lane
 // reduction. No barrier is needed between a wave's own staging writes and reads (one
@@ -387,9 +505,8 @@ __device__ __forceinline__ void gemm_mainloop(const GemmProblem& p, int m0, int 
 // loop is the one that combines the row statistics of the four feature-waves.
 struct EpiLane {
   int lane, wave, wm, wn, m0, n0;
-  __device__ __forceinline__ EpiLane(int m0_, int n0_)
-      : lane(threadIdx.x & 63), wave(threadIdx.x >> 6), wm((threadIdx.x >> 6) / kWavesN),
-        wn((threadIdx.x >> 6) % kWavesN), m0(m0_), n0(n0_) {}
+  __device__ __forceinline__ EpiLane(int m0_, int n0_, int tid)
+      : lane(tid & 63), wave(tid >> 6), wm((tid >> 6) / kWavesN), wn((tid >> 6) % kWavesN), m0(m0_), n0(n0_) {}
   // first of the 4 features this lane holds in the row-major walk
   __device__ __forceinline__ int col4() const { return n0 + wn * kWaveN + 4 * (lane & 15); }
   // token of wave-local row r (0..127)
@@ -398,7 +515,7 @@ struct EpiLane {
 
 typedef __attribute__((address_space(3))) f32x4_t* lds_f32x4_ptr;
 
-// Staging address of (row r in 0..63, 16-byte chunk c in 0..15), rows of 256 bytes.
+// Staging address of (row r in 0..31, 16-byte chunk c in 0..15), rows of 256 bytes.
 // The accumulator writes put 8 consecutive rows at one chunk into each 8-lane group
 // (gfx950 serves ds_write_b128 8 lanes at a time over 32 banks), so XOR-ing the chunk
 // with r mod 8 makes them distinct; the row-major reads give rows r and r + 8 to the
@@ -409,8 +526,7 @@ __device__ __forceinline__ uint32_t stg_off(int r, int c) {
 }
 
 __device__ __forceinline__ char* stage_base(const LdsRing& lds, int wave) {
-  char* s = (wave >> 1) == 0 ? lds.slot[0] : (wave >> 1) == 1 ? lds.slot[1] : (wave >> 1) == 2 ? lds.slot[2] : lds.slot[3];
-  return s + (wave & 1) * kStgWaveBytes;
+  return (wave < 4 ? lds.stg[0] : lds.stg[1]) + (wave & 3) * kStgWaveBytes;
 }
 
 // Walk a wave's accumulators row-major: op.row(r, v, pre) gets wave-local row r
@@ -423,7 +539,6 @@ __device__ __forceinline__ char* stage_base(const LdsRing& lds, int wave) {
 // quarter being walked, which bounds the registers they hold. Either way a row's loads
 // are issued before the output stores that precede its use, so none queues behind them
 // (the vector-memory counter waits on stores and loads alike).
-typedef f32x16_t AccTile[kNI][kMJ];
 
 // Type of an op's row statistic: Op::Stat if it declares one, else float.
 template <class Op, class = void>
@@ -487,22 +602,18 @@ __device__ __forceinline__ f32x4_t epilogue_rows(AccTile& acc, const LdsRing& ld
   };
   if constexpr (sizeof(Pre) <= 8) {
     // small side inputs: all 32 rows of the lane are fetched before any staging, then
-    // the block is walked in two halves of 64 staged tokens
+    // the block is walked 32 staged tokens at a time
     Pre pre[4][8];
 #pragma unroll
     for (int j = 0; j < kMJ; ++j)
 #pragma unroll
       for (int it = 0; it < 8; ++it) pre[j][it] = op.fetch(32 * j + 8 * rq + it);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      stage(2 * h, 0);
-      stage(2 * h + 1, 32);
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        Stat stat[8];
-        walk8(32 * jj, 64 * h + 32 * jj, pre[2 * h + jj], stat);
-        record(64 * h + 32 * jj, stat);
-      }
+    for (int j = 0; j < kMJ; ++j) {
+      stage(j, 0);
+      Stat stat[8];
+      walk8(0, 32 * j, pre[j], stat);
+      record(32 * j, stat);
     }
   } else {
     // larger side inputs: quarters of 32 tokens, each staged on its own; the next
@@ -548,7 +659,7 @@ __device__ __forceinline__ float sum16(float x) {
 __device__ __forceinline__ void store_row_partials(const LdsRing& lds, const EpiLane& L, float* __restrict__ partials,
                                                    int nb, int M) {
   __syncthreads();
-  const int t = threadIdx.x;
+  const int t = lds.tid;
   if (t < kBM) {
     const int wm = t >> 7, r = t & 127;
     const int m = L.m0 + t;
@@ -629,7 +740,7 @@ struct EpiStore {
   };
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
-    const EpiLane L(m0, n0);
+    const EpiLane L(m0, n0, lds.tid);
     Op op{L, a, p.M, p.N, L.col4()};
     epilogue_rows(acc, lds, L, op);
   }
@@ -674,7 +785,7 @@ struct EpiResidualRmsPartials {
   };
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
-    const EpiLane L(m0, n0);
+    const EpiLane L(m0, n0, lds.tid);
     const int n = L.col4();
     const bool nok = n < p.N;
     const u32x2_t gg = load_bf16x4(a.gamma, (size_t)n, nok);
@@ -708,7 +819,7 @@ struct EpiRowScale {
   };
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
-    const EpiLane L(m0, n0);
+    const EpiLane L(m0, n0, lds.tid);
     Op op{L, a, p.M, p.N, L.col4(), WaveRowsF32(a.r, L, p.M)};
     epilogue_rows(acc, lds, L, op);
   }
@@ -772,7 +883,7 @@ struct EpiRope {
   };
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
-    const EpiLane L(m0, n0);
+    const EpiLane L(m0, n0, lds.tid);
     const int n = L.col4();
     const int pos0 = (int)(((long long)L.token(0) + a.pos_offset) % a.seq_len);
     Op op{L, a, p.M, p.N, n, a.head_dim >> 1, (n % a.head_dim) >> 1, pos0, n < a.n_rot};
@@ -808,7 +919,7 @@ struct EpiSwiGLU {
   };
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
-    const EpiLane L(m0, n0);
+    const EpiLane L(m0, n0, lds.tid);
     Op op{L, a, p.M, p.N, L.col4()};
     epilogue_rows(acc, lds, L, op);
   }
@@ -844,7 +955,7 @@ struct EpiDotRowPartials {
   };
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
-    const EpiLane L(m0, n0);
+    const EpiLane L(m0, n0, lds.tid);
     const int n = L.col4();
     Op op{L, lds, a, p.M, p.N, n, n < p.N, WaveRowsBf16(a.h2, L, p.M, p.N, n, n < p.N)};
     epilogue_rows(acc, lds, L, op);
@@ -852,19 +963,92 @@ struct EpiDotRowPartials {
   }
 };
 
+__host__ __device__ inline int gemm_grid(int M, int N) { return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN); }
+
+// One workgroup per output tile.
 template <bool kWKN, class Epi>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void gemm_epilogue_kernel(GemmProblem p, typename Epi::Args ea) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kSlotBytes];
-  const LdsRing lds{{smem, smem + kSlotBytes, smem + 2 * kSlotBytes, smem + 3 * kSlotBytes, smem + 4 * kSlotBytes},
-                    (float*)(smem + kWaves * kStgWaveBytes)};
+  const LdsRing lds = make_ring(smem, 0, 0, threadIdx.x);
+  const int t = blockIdx.x;
   int m0, n0;
-  tile_coords(p.M, p.N, m0, n0);
+  tile_coords(p.M, p.N, p.K, p.group_m, t, m0, n0);
+  Mainloop<kWKN> ml;
+  ml.init(p, threadIdx.x);
+  const TileSrc src = ml.src(t, m0, n0);
   AccTile acc;
-  gemm_mainloop<kWKN>(p, m0, n0, lds, acc);
+  mainloop_prologue(ml, src, lds);
+  mainloop_body<kWKN, false>(ml, src, src, false, lds, acc);
   Epi::apply(acc, ea, p, m0, n0, lds);
 }
 
-inline int gemm_grid(int M, int N) { return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN); }
+// Persistent form: one workgroup per CU walks tiles t = blockIdx.x, + gridDim.x, ...
+// (tile t stays on XCD t mod 8 when gridDim.x is a multiple of 8, as in the form
+// above). The DMA ring runs on across tiles: the last steps of a tile load the first
+// two depth steps of the next, whose latency the epilogue then covers, and no
+// workgroup launch separates the tiles. Needs K / 32 >= 4. Results are bit-identical
+// to the one-workgroup-per-tile form (same tile sums in the same order).
+template <bool kWKN, class Epi>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void gemm_persistent_kernel(GemmProblem p, typename Epi::Args ea) {
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kSlotBytes];
+  const int tiles = gemm_grid(p.M, p.N);
+  const int KT = (p.K + kBK - 1) / kBK;
+  const int adv = KT % kStages;  // ring advance per tile
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int t = blockIdx.x, rot = 0;
+  int m0, n0;
+  tile_coords(p.M, p.N, p.K, p.group_m, t, m0, n0);
+  bool first = true;
+  TileSrc cur;
+  while (true) {
+    // Every lane-dependent offset (the main loop's DMA and read offsets, the epilogue's
+    // staging addresses) is rebuilt for each tile from a thread index the compiler
+    // cannot hoist (the lane id from mbcnt in volatile asm): hoisted out of the tile
+    // loop, they would stay live across the main loop and push it past the register
+    // budget.
+    int lane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    const int tid = wave * 64 + lane;
+    Mainloop<kWKN> ml;
+    ml.init(p, tid);
+    if (first) {
+      cur = ml.src(t, m0, n0);
+      mainloop_prologue(ml, cur, make_ring(smem, 0, 0, tid));
+      first = false;
+    } else {
+      mainloop_resume(ml, cur, make_ring(smem, rot, 0, tid));
+    }
+    const int tn = t + (int)gridDim.x;
+    const bool has_next = tn < tiles;
+    int mn = m0, nn = n0;
+    int Mo = p.M, No = p.N;  // opaque copies: the division is redone per tile, not hoisted
+    asm volatile("" : "+s"(Mo), "+s"(No));
+    if (has_next) tile_coords(Mo, No, p.K, p.group_m, tn, mn, nn);
+    const TileSrc nxt = ml.src(has_next ? tn : t, mn, nn);
+    // the next tile's steps 0, 1 land in physical slots rot + KT, rot + KT + 1 (mod 5);
+    // the epilogue takes the three after them
+    int e = rot + adv + kNextSteps;  // at most 10
+    e = e >= kStages ? e - kStages : e;
+    e = e >= kStages ? e - kStages : e;
+    const LdsRing lds = make_ring(smem, rot, e, tid);
+    AccTile acc;
+    mainloop_body<kWKN, true>(ml, cur, nxt, has_next, lds, acc);
+    Epi::apply(acc, ea, p, m0, n0, lds);
+    if (!has_next) break;
+    t = tn;
+    m0 = mn;
+    n0 = nn;
+    cur = nxt;
+    rot += adv;
+    rot = rot >= kStages ? rot - kStages : rot;
+    __syncthreads();  // every wave is done with the epilogue's areas before steps 2, 3 land there
+  }
+}
+
+// Persistent launches need at least this many depth steps (the next tile's first two
+// steps are loaded by the last four of the current one).
+constexpr int kPersistMinSteps = 4;
 
 }  // namespace coda

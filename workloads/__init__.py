@@ -120,6 +120,12 @@ def rope_qkv(seed: int = 1, M: int = 4096, K: int = 4096, n_q: int = 4096, n_k: 
                          seq_len=seq_len, pos_offset=pos_offset, theta=theta))
 
 
+def rope_qkv_8k(seed: int = 9) -> Workload:
+    """The 8192-class GEMM + RoPE: M = K = 8192, QKV width 3 x 8192, head_dim 128, the
+    positions of one 8192-token sequence; same distributions as rope_qkv."""
+    return rope_qkv(seed=seed, M=8192, K=8192, n_q=8192, n_k=8192, n_v=8192, head_dim=128, seq_len=8192)
+
+
 def swiglu(seed: int = 2, M: int = 8192, K: int = 8192, F: int = 4096) -> Workload:
     """GEMM+SwiGLU: x[M,K] ~ N(0,1); W[K,2F] ~ N(0,1/K) with interleaved columns
     (even = gate, odd = up)."""
