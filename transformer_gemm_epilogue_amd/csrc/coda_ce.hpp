@@ -9,15 +9,11 @@
 
 namespace coda {
 
-// Maximum over the 16 lanes of a DPP row (same exchange pattern as sum16).
-__device__ __forceinline__ float max16(float x) {
-  x = fmaxf(x, dpp<0xB1>(x));
-  x = fmaxf(x, dpp<0x4E>(x));
-  x = fmaxf(x, dpp<0x141>(x));
-  x = fmaxf(x, dpp<0x140>(x));
-  return x;
-}
-
+// The epilogue works in the accumulator layout itself, with no row-major relayout: it has
+// no per-element side input and writes no tile, and a lane already holds 32 of a row's 64
+// wave-features (acc[i][j][4 g + e] is feature 32 i + 8 g + 4 (lane >> 5) + e of token
+// 32 j + (lane & 31)); the lane 32 away holds the other 32. So each row's maximum and sum
+// of exponentials reduce within the lane, then once across the lane pair.
 struct EpiCrossEntropy {
   struct Args {
     const int32_t* labels;  // [M]; outside [0, V) marks an ignored row
@@ -25,55 +21,95 @@ struct EpiCrossEntropy {
     float* target;          // [M] z[m, label[m]] (written by the tile that holds it)
     int nb;
   };
-  struct Op {
-    const EpiLane& L;
-    const Args& a;
-    int M, N, n;
-    bool nok;
-    WaveRowsF32 lab;  // labels, read as 32-bit words
-    static constexpr bool kRowStat = true;
-    static constexpr bool kColStat = false;
-    typedef float2 Stat;  // (max over the wave's 64 columns, sum of exp(z - max) over them)
-    typedef float Pre;    // the row's label bits
-    __device__ __forceinline__ Pre fetch(int r) const { return lab.load(r); }
-    __device__ __forceinline__ Stat row(int r, const f32x4_t& v, const Pre& lbits) const {
-      const float ninf = -__builtin_huge_valf();
-      const float z0 = nok ? v.x : ninf, z1 = nok ? v.y : ninf, z2 = nok ? v.z : ninf, z3 = nok ? v.w : ninf;
-      const float mx = max16(fmaxf(fmaxf(z0, z1), fmaxf(z2, z3)));
-      const float sh = mx == ninf ? 0.f : mx;  // a wave with no valid column contributes 0
-      const float se = sum16((__expf(z0 - sh) + __expf(z1 - sh)) + (__expf(z2 - sh) + __expf(z3 - sh)));
-      const int m = L.token(r);
-      const int label = __builtin_bit_cast(int, lbits);
-      if (nok && m < M && label >= n && label < n + 4) {
-        const int e = label - n;
-        a.target[m] = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+  // Per 32-token block j: the row's maximum and sum of exp(z - max) over this wave's 64
+  // columns (kFull: all of them inside the width, no column masks), recorded per
+  // (wave, row); the lane holding the label's column writes the target logit. The
+  // exponential is exp2 of one fused multiply-add; the label search runs only for the
+  // blocks where some lane of the wave can hold a label column (64 of V columns).
+  template <bool kFull>
+  __device__ __forceinline__ static void rows(AccTile& acc, const Args& a, const GemmProblem& p, const EpiLane& L,
+                                              int nbase, const int (&label)[kMJ], float2* red) {
+    const float ninf = -__builtin_huge_valf();
+    const float l2e = 1.4426950408889634f;
+    const int r32 = L.lane & 31;
+    // columns 32 i + 8 g .. + 3 of this lane are inside the width (N % 8 == 0)
+    bool ok[kNI][4];
+#pragma unroll
+    for (int i = 0; i < kNI; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) ok[i][g] = kFull || nbase + 32 * i + 8 * g < p.N;
+#pragma unroll
+    for (int j = 0; j < kMJ; ++j) {
+      float mx = ninf;
+#pragma unroll
+      for (int i = 0; i < kNI; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = ok[i][g] ? fmaxf(mx, acc[i][j][4 * g + e]) : mx;
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float shl = (mx == ninf ? 0.f : mx) * l2e;  // a wave with no valid column contributes 0
+      float se = 0.f;
+#pragma unroll
+      for (int i = 0; i < kNI; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            se += ok[i][g] ? __builtin_amdgcn_exp2f(fmaf(acc[i][j][4 * g + e], l2e, -shl)) : 0.f;
+      se += __shfl_xor(se, 32);
+      const int m = L.token(32 * j + r32);
+      const int rel = label[j] - nbase;  // this lane's column offset of the label
+      const bool maybe = (unsigned)rel < (unsigned)(2 * 32) && (rel & 4) == 0;
+      if (__builtin_amdgcn_ballot_w64(maybe) != 0) {  // wave-uniform
+        float tv = 0.f;
+        bool hit = false;
+#pragma unroll
+        for (int i = 0; i < kNI; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool here = ok[i][g] && rel == 32 * i + 8 * g + e;
+              tv = here ? acc[i][j][4 * g + e] : tv;
+              hit = hit || here;
+            }
+        if (hit && m < p.M) a.target[m] = tv;
       }
-      return make_float2(mx, se);
+      if (L.lane < 32) red[32 * j + r32] = make_float2(mx, se);
     }
-  };
+  }
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
     const EpiLane L(m0, n0, lds.tid);
-    const int n = L.col4();
-    Op op{L, a, p.M, p.N, n, n < p.N, WaveRowsF32((const float*)a.labels, L, p.M)};
-    epilogue_rows(acc, lds, L, op);
+    const int r32 = L.lane & 31;
+    const int nbase = n0 + L.wn * kWaveN + 4 * (L.lane >> 5);  // feature of acc[0][j][0]
+    const WaveRowsF32 lab((const float*)a.labels, L, p.M);
+    int label[kMJ];
+#pragma unroll
+    for (int j = 0; j < kMJ; ++j) label[j] = __builtin_bit_cast(int, lab.load(32 * j + r32));
+    float2* red = (float2*)lds.red + (L.wm * kWavesN + L.wn) * 128;
+    if (n0 + kBN <= p.N)  // wave-uniform: the whole tile lies inside the width
+      rows<true>(acc, a, p, L, nbase, label, red);
+    else
+      rows<false>(acc, a, p, L, nbase, label, red);
     __syncthreads();
     // merge the four feature-waves of each row in the order wn = 0, 1, 2, 3
     const int t = lds.tid;
     if (t < kBM) {
       const int wm = t >> 7, r = t & 127;
       const float2* st = (const float2*)lds.red + wm * kWavesN * 128 + r;
-      float mx = st[0].x;
+      float mxa = st[0].x;
 #pragma unroll
-      for (int w = 1; w < kWavesN; ++w) mx = fmaxf(mx, st[w * 128].x);
+      for (int w = 1; w < kWavesN; ++w) mxa = fmaxf(mxa, st[w * 128].x);
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < kWavesN; ++w) {
         const float2 q = st[w * 128];
-        s += q.y == 0.f ? 0.f : q.y * expf(q.x - mx);
+        s += q.y == 0.f ? 0.f : q.y * expf(q.x - mxa);
       }
       const int m = m0 + t;
-      if (m < p.M) a.tile_lse[(size_t)m * a.nb + n0 / kBN] = mx + logf(s);
+      if (m < p.M) a.tile_lse[(size_t)m * a.nb + n0 / kBN] = mxa + logf(s);
     }
   }
 };
