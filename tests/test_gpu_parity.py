@@ -138,6 +138,23 @@ def test_rowstat_reduce(coda, nb):
     assert_close("s", s.cpu().numpy(), O.rowstat_reduce(P, d, 0.0, "mean"), rel_fro=1e-6)
 
 
+@pytest.mark.parametrize("nb,M", [(4, 1), (4, 1031), (8, 777), (16, 8192), (16, 4099), (32, 300), (64, 1000),
+                                  (12, 513)])
+def test_rowstat_reduce_sum_order_is_sequential(coda, nb, M):
+    """Every load layout sums a row in the order t = 0, 1, ..., nb-1 in fp32 (the
+    contiguous-load form passes the running sum lane to lane): compared bit for bit with
+    that sequential fp32 sum, here on the host; ragged M past a block."""
+    rng = np.random.default_rng(100 + nb + M)
+    P = (rng.standard_normal((M, nb)) ** 2).astype(np.float32)
+    s = coda.coda_rowstat_reduce(to_dev_f32(P), 4096, 0.0, coda.ROWSTAT_MEAN)
+    sync()
+    acc = np.zeros(M, dtype=np.float32)
+    for t in range(nb):
+        acc = (acc + P[:, t]).astype(np.float32)
+    want = (acc / np.float32(4096)).astype(np.float32)
+    assert np.array_equal(s.cpu().numpy(), want)
+
+
 def test_rowstat_reduce_ragged_partial_buffer_offset(coda):
     """A partials view that is only 4-byte aligned takes the scalar-load path."""
     import torch
