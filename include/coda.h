@@ -132,7 +132,8 @@ int coda_rope_tables(float* cos_t, float* sin_t, int seq_len, int head_dim, doub
  *       out[2p] = h[2p] cos - h[2p+1] sin,   out[2p+1] = h[2p] sin + h[2p+1] cos,
  *   where cos/sin = cos_t/sin_t[pos, p] (from coda_rope_tables). V is stored unrotated.
  * Rules: head_dim % 8 == 0; n_q, n_k, n_v >= 0 multiples of head_dim with a positive
- * sum; seq_len >= 1; pos_offset >= 0. */
+ * sum; seq_len >= 1 (else CODA_ERR_ARG); seq_len * head_dim <= 2^29 (tables under 2^31
+ * bytes, else CODA_ERR_SHAPE); pos_offset >= 0. */
 int coda_gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t,
                    const float* sin_t, int M, int K, int n_q, int n_k, int n_v, int head_dim,
                    int seq_len, int pos_offset, uint16_t* out, void* stream);

@@ -152,6 +152,7 @@ int gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, const fl
   const long long N = (long long)n_q + n_k + n_v;
   if (N < 8 || N > kMaxDim) return CODA_ERR_SHAPE;
   if (seq_len < 1 || pos_offset < 0) return CODA_ERR_ARG;
+  if ((long long)seq_len * head_dim > (1LL << 29)) return CODA_ERR_SHAPE;  // each table stays < 2^31 bytes
   if (M == 0) return CODA_OK;
   CODA_NONNULL(x);
   CODA_NONNULL(w);

@@ -533,12 +533,11 @@ __device__ __forceinline__ char* stage_base(const LdsRing& lds, int wave) {
 // (0..127), this lane's 4 fp32 values at features col4() .. col4() + 3, and what
 // op.fetch(r) loaded for that row; it returns the row's statistic (kRowStat) and, for
 // ops with kColStat, adds its per-feature contribution into a column accumulator kept
-// here (returned: the sum over this lane's 32 rows). When a row's input is at most 8 bytes, the loads for
-// all 32 rows of the lane are issued before any staging, so their latency overlaps the
-// LDS traffic; larger inputs are fetched one quarter (8 rows per lane) ahead of the
-// quarter being walked, which bounds the registers they hold. Either way a row's loads
-// are issued before the output stores that precede its use, so none queues behind them
-// (the vector-memory counter waits on stores and loads alike).
+// here (returned: the sum over this lane's 32 rows). Side inputs are fetched one block
+// (8 rows per lane) ahead of the block being walked, which bounds the registers they
+// hold while the accumulators are still live; a row's loads are issued before the output
+// stores that precede its use, so none queues behind them (the vector-memory counter
+// waits on stores and loads alike).
 
 // Type of an op's row statistic: Op::Stat if it declares one, else float.
 template <class Op, class = void>
@@ -600,38 +599,21 @@ __device__ __forceinline__ f32x4_t epilogue_rows(AccTile& acc, const LdsRing& ld
       }
     }
   };
-  if constexpr (sizeof(Pre) <= 8) {
-    // small side inputs: all 32 rows of the lane are fetched before any staging, then
-    // the block is walked 32 staged tokens at a time
-    Pre pre[4][8];
+  // blocks of 32 tokens, each staged on its own; the next block's side-input loads are
+  // issued before this block's stores and are in flight while it is walked
+  Pre pre[2][8];
 #pragma unroll
-    for (int j = 0; j < kMJ; ++j)
+  for (int it = 0; it < 8; ++it) pre[0][it] = op.fetch(8 * rq + it);
 #pragma unroll
-      for (int it = 0; it < 8; ++it) pre[j][it] = op.fetch(32 * j + 8 * rq + it);
+  for (int j = 0; j < kMJ; ++j) {
+    stage(j, 0);
+    if (j + 1 < kMJ) {
 #pragma unroll
-    for (int j = 0; j < kMJ; ++j) {
-      stage(j, 0);
-      Stat stat[8];
-      walk8(0, 32 * j, pre[j], stat);
-      record(32 * j, stat);
+      for (int it = 0; it < 8; ++it) pre[(j + 1) & 1][it] = op.fetch(32 * (j + 1) + 8 * rq + it);
     }
-  } else {
-    // larger side inputs: quarters of 32 tokens, each staged on its own; the next
-    // quarter's fetches are in flight while this one is walked
-    Pre pre[2][8];
-#pragma unroll
-    for (int it = 0; it < 8; ++it) pre[0][it] = op.fetch(8 * rq + it);
-#pragma unroll
-    for (int j = 0; j < kMJ; ++j) {
-      stage(j, 0);
-      if (j + 1 < kMJ) {
-#pragma unroll
-        for (int it = 0; it < 8; ++it) pre[(j + 1) & 1][it] = op.fetch(32 * (j + 1) + 8 * rq + it);
-      }
-      Stat stat[8];
-      walk8(0, 32 * j, pre[j & 1], stat);
-      record(32 * j, stat);
-    }
+    Stat stat[8];
+    walk8(0, 32 * j, pre[j & 1], stat);
+    record(32 * j, stat);
   }
   return col;
 }
@@ -711,6 +693,34 @@ struct WaveRowsF32 {  // [M] fp32, one value per row
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)r * 4u, 0, 0));
   }
 };
+// Output rows of the wave's 128 tokens in an [M, ld] bf16 array, through a raw buffer
+// descriptor: rows past M lie outside its range, and a lane whose features lie past the
+// width starts from an out-of-range column offset (2^31; adding a row offset below 2^30
+// keeps it out of every range), so those stores are dropped by the hardware and the
+// stores need no branch. Outputs of the same shape share one row offset (row_off).
+struct WaveRowsOutBf16 {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t pitch, coff;
+  __device__ __forceinline__ WaveRowsOutBf16(uint16_t* base, const EpiLane& L, int M, int ld, int n, bool nok) {
+    const int r0 = L.m0 + L.wm * 128;
+    const int rows = max(0, min(128, M - r0));  // 128 * 2^22 * 2 bytes < 2^31
+    rs = make_rsrc(base + (size_t)max(r0, 0) * ld, (uint32_t)rows * (uint32_t)ld * 2u);
+    pitch = (uint32_t)ld * 2u;
+    coff = nok ? (uint32_t)n * 2u : kOutOfRange;
+  }
+  __device__ __forceinline__ uint32_t row_off(int r) const { return coff + (uint32_t)r * pitch; }
+  // bf16 of (a, b, c, d) at byte offset `off` (row_off of this or a same-shaped output)
+  __device__ __forceinline__ void store4_at(uint32_t off, float a, float b, float c, float d) const {
+    u32x2_t v;
+    v.x = pack_bf16x2(a, b);
+    v.y = pack_bf16x2(c, d);
+    __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, 0);
+  }
+  __device__ __forceinline__ void store4(int r, float a, float b, float c, float d) const {
+    store4_at(row_off(r), a, b, c, d);
+  }
+};
+
 __device__ __forceinline__ void store_bf16x4(uint16_t* __restrict__ base, size_t idx, float a, float b, float c,
                                              float d) {
   u32x2_t v;
@@ -725,23 +735,21 @@ struct EpiStore {
     uint16_t* out;
   };
   struct Op {
-    const EpiLane& L;
-    const Args& a;
-    int M, N, n;
+    WaveRowsOutBf16 out;
     static constexpr bool kRowStat = false;
     static constexpr bool kColStat = false;
     typedef NoPre Pre;
     __device__ __forceinline__ Pre fetch(int) const { return Pre{}; }
     __device__ __forceinline__ float row(int r, const f32x4_t& v, const Pre&) {
-      const int m = L.token(r);
-      if (m < M && n < N) store_bf16x4(a.out, (size_t)m * N + n, v.x, v.y, v.z, v.w);
+      out.store4(r, v.x, v.y, v.z, v.w);
       return 0.f;
     }
   };
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
     const EpiLane L(m0, n0, lds.tid);
-    Op op{L, a, p.M, p.N, L.col4()};
+    const int n = L.col4();
+    Op op{WaveRowsOutBf16(a.out, L, p.M, p.N, n, n < p.N)};
     epilogue_rows(acc, lds, L, op);
   }
 };
@@ -759,27 +767,19 @@ struct EpiResidualRmsPartials {
     int nb;
   };
   struct Op {
-    const EpiLane& L;
-    const LdsRing& lds;
-    const Args& a;
-    int M, N, n;
-    bool nok;
     float g0, g1, g2, g3;
     WaveRowsBf16 z;
+    WaveRowsOutBf16 h1o, h2o;
     static constexpr bool kRowStat = true;
     static constexpr bool kColStat = false;
     typedef u32x2_t Pre;
     __device__ __forceinline__ Pre fetch(int r) const { return z.load4(r); }
     __device__ __forceinline__ float row(int r, const f32x4_t& v, const Pre& zz) {
-      const int m = L.token(r);
-      const bool ok = nok && m < M;
-      const size_t idx = (size_t)m * N + n;
       const float h0 = v.x + bf16_lo(zz.x), h1 = v.y + bf16_hi(zz.x);
       const float h2 = v.z + bf16_lo(zz.y), h3 = v.w + bf16_hi(zz.y);
-      if (ok) {
-        store_bf16x4(a.h1, idx, h0, h1, h2, h3);
-        store_bf16x4(a.h2, idx, h0 * g0, h1 * g1, h2 * g2, h3 * g3);
-      }
+      const uint32_t off = h1o.row_off(r);  // h1 and h2 have the same shape
+      h1o.store4_at(off, h0, h1, h2, h3);
+      h2o.store4_at(off, h0 * g0, h1 * g1, h2 * g2, h3 * g3);
       return sum16((h0 * h0 + h1 * h1) + (h2 * h2 + h3 * h3));
     }
   };
@@ -789,8 +789,8 @@ struct EpiResidualRmsPartials {
     const int n = L.col4();
     const bool nok = n < p.N;
     const u32x2_t gg = load_bf16x4(a.gamma, (size_t)n, nok);
-    Op op{L, lds, a, p.M, p.N, n, nok, bf16_lo(gg.x), bf16_hi(gg.x), bf16_lo(gg.y), bf16_hi(gg.y),
-          WaveRowsBf16(a.z, L, p.M, p.N, n, nok)};
+    Op op{bf16_lo(gg.x), bf16_hi(gg.x), bf16_lo(gg.y), bf16_hi(gg.y), WaveRowsBf16(a.z, L, p.M, p.N, n, nok),
+          WaveRowsOutBf16(a.h1, L, p.M, p.N, n, nok), WaveRowsOutBf16(a.h2, L, p.M, p.N, n, nok)};
     epilogue_rows(acc, lds, L, op);
     store_row_partials(lds, L, a.partials, a.nb, p.M);
   }
@@ -803,24 +803,22 @@ struct EpiRowScale {
     uint16_t* y;
   };
   struct Op {
-    const EpiLane& L;
-    const Args& a;
-    int M, N, n;
     WaveRowsF32 rv;
+    WaveRowsOutBf16 out;
     static constexpr bool kRowStat = false;
     static constexpr bool kColStat = false;
     typedef float Pre;
     __device__ __forceinline__ Pre fetch(int r) const { return rv.load(r); }
     __device__ __forceinline__ float row(int r, const f32x4_t& v, const Pre& s) {
-      const int m = L.token(r);
-      if (m < M && n < N) store_bf16x4(a.y, (size_t)m * N + n, s * v.x, s * v.y, s * v.z, s * v.w);
+      out.store4(r, s * v.x, s * v.y, s * v.z, s * v.w);
       return 0.f;
     }
   };
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
     const EpiLane L(m0, n0, lds.tid);
-    Op op{L, a, p.M, p.N, L.col4(), WaveRowsF32(a.r, L, p.M)};
+    const int n = L.col4();
+    Op op{WaveRowsF32(a.r, L, p.M), WaveRowsOutBf16(a.y, L, p.M, p.N, n, n < p.N)};
     epilogue_rows(acc, lds, L, op);
   }
 };
@@ -841,10 +839,14 @@ struct EpiRope {
     int pos_offset;
     int inverse;  // 0: forward rotation, 1: rotation by the negated angle
   };
+  // kShort: seq_len < 128, so a wave's 128 rows may wrap the position more than once.
+  template <bool kShort>
   struct Op {
     const EpiLane& L;
     const Args& a;
-    int M, N, n, half, pp, pos0;
+    __amdgpu_buffer_rsrc_t ct, st;  // the cos and sin tables, [seq_len, head_dim / 2] fp32
+    WaveRowsOutBf16 out;
+    int half, pp, pos0;
     bool rot;
     static constexpr bool kRowStat = false;
     static constexpr bool kColStat = false;
@@ -852,42 +854,48 @@ struct EpiRope {
       float2 c, s;
     };
     __device__ __forceinline__ Pre fetch(int r) const {
-      // (m + pos_offset) mod seq_len from the wave's first token: r < 128 steps on. The
-      // index is a valid table entry for every lane and row (also rows past M and
-      // unrotated columns, whose values are not used), so the loads need no branch.
+      // (m + pos_offset) mod seq_len for wave row r: pos0 + r < pos0 + 128, so one
+      // subtraction wraps it when seq_len >= 128. Every lane and row reads a valid table
+      // entry (also rows past M and unrotated columns, whose values are not used).
       int pos = pos0 + r;
-      const int S = a.seq_len;
-      if (pos >= S) pos = pos - S < S ? pos - S : pos % S;
+      if constexpr (kShort) {
+        pos %= a.seq_len;
+      } else {
+        pos = pos >= a.seq_len ? pos - a.seq_len : pos;
+      }
+      const uint32_t off = (uint32_t)(pos * half + pp) * 4u;
       Pre t;
-      t.c = *(const float2*)(a.cos_t + (size_t)pos * half + pp);
-      t.s = *(const float2*)(a.sin_t + (size_t)pos * half + pp);
+      t.c = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(ct, off, 0, 0));
+      t.s = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(st, off, 0, 0));
       return t;
     }
     __device__ __forceinline__ float row(int r, const f32x4_t& v, const Pre& t) {
-      const int m = L.token(r);
-      if (!(m < M && n < N)) return 0.f;
-      float e0 = v.x, o0 = v.y, e1 = v.z, o1 = v.w;
-      if (rot) {
-        const float2 c = t.c;
-        const float2 s = a.inverse ? make_float2(-t.s.x, -t.s.y) : t.s;
-        const float re0 = e0 * c.x - o0 * s.x, ro0 = e0 * s.x + o0 * c.x;
-        const float re1 = e1 * c.y - o1 * s.y, ro1 = e1 * s.y + o1 * c.y;
-        e0 = re0;
-        o0 = ro0;
-        e1 = re1;
-        o1 = ro1;
-      }
-      store_bf16x4(a.out, (size_t)m * N + n, e0, o0, e1, o1);
+      const float2 c = t.c;
+      const float2 s = a.inverse ? make_float2(-t.s.x, -t.s.y) : t.s;
+      const float re0 = v.x * c.x - v.y * s.x, ro0 = v.x * s.x + v.y * c.x;
+      const float re1 = v.z * c.y - v.w * s.y, ro1 = v.z * s.y + v.w * c.y;
+      out.store4(r, rot ? re0 : v.x, rot ? ro0 : v.y, rot ? re1 : v.z, rot ? ro1 : v.w);
       return 0.f;
     }
   };
+  template <bool kShort>
+  __device__ __forceinline__ static void run(AccTile& acc, const Args& a, const GemmProblem& p, const EpiLane& L,
+                                             const LdsRing& lds) {
+    const int n = L.col4();
+    const int half = a.head_dim >> 1;
+    const int pos0 = (int)(((long long)L.token(0) + a.pos_offset) % a.seq_len);
+    const uint32_t tbytes = (uint32_t)a.seq_len * (uint32_t)half * 4u;
+    Op<kShort> op{L, a, make_rsrc(a.cos_t, tbytes), make_rsrc(a.sin_t, tbytes),
+                  WaveRowsOutBf16(a.out, L, p.M, p.N, n, n < p.N), half, (n % a.head_dim) >> 1, pos0, n < a.n_rot};
+    epilogue_rows(acc, lds, L, op);
+  }
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
     const EpiLane L(m0, n0, lds.tid);
-    const int n = L.col4();
-    const int pos0 = (int)(((long long)L.token(0) + a.pos_offset) % a.seq_len);
-    Op op{L, a, p.M, p.N, n, a.head_dim >> 1, (n % a.head_dim) >> 1, pos0, n < a.n_rot};
-    epilogue_rows(acc, lds, L, op);
+    if (a.seq_len >= 128)
+      run<false>(acc, a, p, L, lds);
+    else
+      run<true>(acc, a, p, L, lds);
   }
 };
 
