@@ -95,6 +95,13 @@ def test_rope_validation(L):
     assert call(off=-1) == ARG
     assert call(cos=P + 4) == ALIGN
     assert call(M=0) == OK
+    # each rotary table must stay below 2^31 bytes: seq_len * head_dim <= 2^29
+    assert call(hd=128, seq=(1 << 22) + 8, n_q=128, n_k=0, n_v=0) == SHAPE
+    assert call(hd=128, seq=(1 << 22), n_q=128, n_k=0, n_v=0, M=0) == OK
+    for name in ("coda_gemm_rope_persistent", "coda_gemm_rope_bwd"):
+        fn = getattr(L, name)
+        assert fn(P, P, P, P, 64, 64, 128, 0, 0, 128, (1 << 22) + 8, 0, P, None) == SHAPE
+        assert fn(P, P, None, P, 64, 64, 128, 128, 128, 128, 64, 0, P, None) == NULL
 
 
 def test_swiglu_validation(L):
