@@ -292,19 +292,19 @@ def other_paths(coda, torch, reps):
     out["gemm_rope_qkv_8192x24576x8192"] = path_record(t, 2.0 * M * K * N)
     del x, w, qkv, h, wl
     torch.cuda.empty_cache()
-    # GEMM + SwiGLU
-    wl = W.swiglu()
-    x, w = to_dev(wl["x"]), to_dev(wl["w"])
-    M, K, F = wl["M"], wl["K"], wl["F"]
-    o = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
-    h = torch.empty((M, 2 * F), dtype=torch.bfloat16, device="cuda")
-    t = time_interleaved({
-        "fused": lambda: coda.coda_gemm_swiglu(x, w, out=o),
-        "unfused": lambda: (coda.coda_baseline_gemm(x, w, c=h), coda.coda_baseline_swiglu(h, out=o)),
-        "hipblaslt": lambda: torch.matmul(x, w)}, reps)
-    fl = 2.0 * M * K * 2 * F
-    out["gemm_swiglu_8192x8192x8192"] = path_record(t, fl)
-    del x, w, o, h
+    # GEMM + SwiGLU at the pages' two shapes
+    for wl in (W.swiglu_4k(), W.swiglu()):
+        x, w = to_dev(wl["x"]), to_dev(wl["w"])
+        M, K, F = wl["M"], wl["K"], wl["F"]
+        o = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+        h = torch.empty((M, 2 * F), dtype=torch.bfloat16, device="cuda")
+        t = time_interleaved({
+            "fused": lambda: coda.coda_gemm_swiglu(x, w, out=o),
+            "unfused": lambda: (coda.coda_baseline_gemm(x, w, c=h), coda.coda_baseline_swiglu(h, out=o)),
+            "hipblaslt": lambda: torch.matmul(x, w)}, reps)
+        fl = 2.0 * M * K * 2 * F
+        out[f"gemm_swiglu_{M}x{2 * F}x{K}"] = path_record(t, fl)
+        del x, w, o, h
     # backward statistic
     wl = W.bwd_stats()
     dy, w1, h2 = to_dev(wl["dy"]), to_dev(wl["w1"]), to_dev(wl["h2"])

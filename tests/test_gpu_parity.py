@@ -235,6 +235,15 @@ def test_swiglu_full_size_sampled(coda):
     assert_close("swiglu", dec(out)[rows], O.gemm_swiglu(wl["x"], wl["w"], rows=rows))
 
 
+def test_swiglu_4096_full_size_sampled(coda):
+    wl = W.swiglu_4k()
+    log(f"swiglu {wl.name}")
+    out = coda.coda_gemm_swiglu(to_dev_bf16(wl["x"]), to_dev_bf16(wl["w"]))
+    sync()
+    rows = sample_rows(wl["M"], 40, seed=10)
+    assert_close("swiglu", dec(out)[rows], O.gemm_swiglu(wl["x"], wl["w"], rows=rows))
+
+
 # ----------------------------------------------------------------------- backward statistic
 def run_bwd(coda, wl):
     dh2, part, s = coda.coda_gemm_rmsnorm_bwd_stats(to_dev_bf16(wl["dy"]), to_dev_bf16(wl["w1"]),

@@ -135,6 +135,11 @@ def swiglu(seed: int = 2, M: int = 8192, K: int = 8192, F: int = 4096) -> Worklo
     return Workload(f"gemm_swiglu_M{M}_K{K}_F{F}", seed, dict(x=x, w=w), dict(M=M, K=K, F=F))
 
 
+def swiglu_4k(seed: int = 10) -> Workload:
+    """GEMM+SwiGLU at the pages' 4096 shape: M = K = 4096, interleaved width 2F = 4096."""
+    return swiglu(seed=seed, M=4096, K=4096, F=2048)
+
+
 def bwd_stats(seed: int = 4, M: int = 8192, D: int = 4096, N: int = 6144) -> Workload:
     """RMSNorm-backward statistic through the grad GEMM: h2[M,D] ~ N(0,1);
     W1[D,N] ~ N(0,1/D); dY[M,N] ~ N(0,1e-2), drawn in that order."""
