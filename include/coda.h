@@ -25,10 +25,11 @@
  *     nonzero status (nothing is written). A failed kernel launch returns
  *     CODA_ERR_HIP. Faults during execution surface at the caller's next
  *     synchronisation, as for any asynchronous HIP work.
- *   - Shapes: M (rows / tokens) may be any value >= 0 (M == 0 is a no-op returning
- *     CODA_OK). Depth K and every output width must be positive multiples of 8, and
- *     at most 4194304 (2^22). Any M is handled by row predication; ragged K and widths
- *     by zero-filled tails.
+ *   - Shapes: M (rows / tokens) may be any value from 0 to 16777216 (2^24; M == 0 is a
+ *     no-op returning CODA_OK). Depth K and every output width must be positive
+ *     multiples of 8, and at most 4194304 (2^22); so a GEMM has fewer than 2^30 output
+ *     tiles. Any M is handled by row predication; ragged K and widths by zero-filled
+ *     tails. Larger sizes return CODA_ERR_SHAPE.
  *   - Accumulation is fp32 on the MFMA units; epilogue math is fp32; only stores round.
  *   - Results are deterministic: no atomics, fixed summation orders.
  */

@@ -104,6 +104,20 @@ def test_rope_validation(L):
         assert fn(P, P, None, P, 64, 64, 128, 128, 128, 128, 64, 0, P, None) == NULL
 
 
+def test_row_count_bound(L):
+    """M above 2^24 rows is rejected by every GEMM entry point before anything is
+    enqueued (with widths <= 2^22 this keeps tile counts below 2^30)."""
+    big = (1 << 24) + 1
+    assert L.coda_baseline_gemm(P, P, big, 64, 256, 1, P, None) == SHAPE
+    assert L.coda_gemm_swiglu(P, P, big, 64, 128, P, None) == SHAPE
+    assert L.coda_gemm_rope(P, P, P, P, big, 64, 128, 128, 128, 128, 64, 0, P, None) == SHAPE
+    assert L.coda_gemm_rmsnorm_bwd_stats(P, P, P, big, 256, 256, P, P, P, None) == SHAPE
+    assert L.coda_rowstat_reduce(P, big, 16, 4096, 1e-5, 0, P, None) == SHAPE
+    assert L.coda_gemm_cross_entropy(P, P, P, big, 64, 256, P, P, P, P, None) == SHAPE
+    nb = ctypes.c_int(0)
+    assert L.coda_colstat_num_partials(big, ctypes.byref(nb)) == SHAPE
+
+
 def test_swiglu_validation(L):
     assert L.coda_gemm_swiglu(P, P, 64, 64, 12, P, None) == SHAPE
     assert L.coda_gemm_swiglu(P, P, 64, 64, 0, P, None) == SHAPE

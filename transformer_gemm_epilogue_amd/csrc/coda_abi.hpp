@@ -9,7 +9,8 @@
 
 namespace coda {
 
-constexpr int kMaxDim = 1 << 22;  // bound on K and output widths (keeps buffer ranges < 2^31)
+constexpr int kMaxDim = 1 << 22;   // bound on K and output widths (keeps buffer ranges < 2^31)
+constexpr int kMaxRows = 1 << 24;  // bound on M (with kMaxDim, fewer than 2^30 output tiles)
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -18,7 +19,7 @@ inline int check_depth_or_width(int v) {
   return CODA_OK;
 }
 
-inline int check_rows(int M) { return M < 0 ? CODA_ERR_SHAPE : CODA_OK; }
+inline int check_rows(int M) { return (M < 0 || M > kMaxRows) ? CODA_ERR_SHAPE : CODA_OK; }
 
 inline int launch_status() {
   const hipError_t e = hipGetLastError();

@@ -125,7 +125,7 @@ extern "C" {
 
 int coda_colstat_num_partials(int rows, int* tiles) {
   CODA_NONNULL(tiles);
-  if (rows < 0) return CODA_ERR_SHAPE;
+  CODA_TRY(check_rows(rows));
   *tiles = row_tiles(rows);
   return CODA_OK;
 }
