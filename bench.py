@@ -432,7 +432,7 @@ def mfma_ceiling(coda, torch):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     grid, iters = 4 * cus, 5000
     out = torch.empty((grid * 512,), dtype=torch.float32, device="cuda")
-    fl = grid * 8.0 * iters * 16 * 32768
+    fl = grid * 8.0 * iters * 32 * 16384
     res = {}
     for name, o in ops.items():
         t_end = time.perf_counter() + 0.5  # clock settle under this load

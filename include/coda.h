@@ -290,10 +290,10 @@ int coda_baseline_rowdot(const uint16_t* a, const uint16_t* b, int M, int D, flo
 /* dst = src, `bytes` a positive multiple of 16: a plain copy kernel of known traffic. */
 int coda_baseline_copy(const void* src, void* dst, int64_t bytes, void* stream);
 /* Measurement probe (no step of the method): `grid` workgroups of 512 threads; thread g
- * reads fragments 12 g .. 12 g + 11 (mod n_frag) of operands [n_frag, 8] bf16 once, then
- * each wave runs `iters` rounds of 16 v_mfma_f32_32x32x16_bf16 on registers only;
- * out [grid * 512] fp32 receives each thread's accumulator sum. FLOPs =
- * grid * 8 * iters * 16 * 32768. With operands drawn like the workloads' data it gives
+ * reads fragments 16 g .. 16 g + 15 (mod n_frag) of operands [n_frag, 8] bf16 once, then
+ * each wave runs `iters` rounds of 32 v_mfma_f32_16x16x32_bf16 (the GEMM's MFMA form and
+ * per-wave shape) on registers only; out [grid * 512] fp32 receives each thread's
+ * accumulator sum. FLOPs = grid * 8 * iters * 32 * 16384. With operands drawn like the workloads' data it gives
  * the MFMA rate sustained under the chip's power limit (the practical ceiling beside the
  * nominal peak). Rules: n_frag, iters >= 1; 1 <= grid <= 65535; operands 16-byte aligned. */
 int coda_baseline_mfma_loop(const uint16_t* operands, int n_frag, int iters, int grid,

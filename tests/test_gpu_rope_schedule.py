@@ -47,9 +47,12 @@ def oracle_rows(wl, rows):
                        wl["pos_offset"], wl["theta"], rows=rows)
 
 
-# More tiles than CUs, so persistent workgroups walk two or three tiles each: depth steps
-# 4 .. 9 cover every length of the tail that loads the next tile's first steps and every
-# ring advance per tile (K/32 mod 5); ragged M and N; K below the persistent minimum.
+# More tiles than CUs, so persistent workgroups walk two or three tiles each. The loop
+# runs ten depth steps per round and leaves 4 to 13 to the tail that loads the next
+# tile's first steps: depth steps 4 .. 14 cover every tail length, both parities of the
+# step that pairs the next tile's X loads (an odd count pairs across the two tiles) and
+# every ring advance per tile (K/32 mod 5); 17 steps add a nonzero (even) depth
+# rotation; ragged M and N; K below the persistent minimum.
 @pytest.mark.parametrize("case", [
     dict(M=8192, K=128, n_q=1536, n_k=1536, n_v=1536, head_dim=128, seq_len=8192, pos_offset=0),
     dict(M=8192, K=160, n_q=1536, n_k=1536, n_v=1536, head_dim=128, seq_len=4096, pos_offset=3),
@@ -57,6 +60,12 @@ def oracle_rows(wl, rows):
     dict(M=8192, K=224, n_q=2048, n_k=1024, n_v=1024, head_dim=128, seq_len=8192, pos_offset=0),
     dict(M=8192, K=256, n_q=1536, n_k=1536, n_v=1536, head_dim=128, seq_len=8192, pos_offset=0),
     dict(M=8000, K=288, n_q=1000, n_k=1000, n_v=1000, head_dim=8, seq_len=5000, pos_offset=11),
+    dict(M=8192, K=320, n_q=1536, n_k=1536, n_v=1536, head_dim=128, seq_len=8192, pos_offset=0),
+    dict(M=8192, K=352, n_q=1536, n_k=1536, n_v=1536, head_dim=128, seq_len=8192, pos_offset=5),
+    dict(M=8192, K=384, n_q=1536, n_k=1536, n_v=1536, head_dim=64, seq_len=8192, pos_offset=0),
+    dict(M=8100, K=416, n_q=1024, n_k=1024, n_v=1024, head_dim=128, seq_len=8192, pos_offset=0),
+    dict(M=8192, K=448, n_q=1536, n_k=1536, n_v=1536, head_dim=128, seq_len=8192, pos_offset=0),
+    dict(M=8192, K=544, n_q=1536, n_k=1536, n_v=1536, head_dim=128, seq_len=8192, pos_offset=1),
     dict(M=8192, K=64, n_q=1536, n_k=1536, n_v=1536, head_dim=128, seq_len=8192, pos_offset=0),
 ])
 def test_persistent_matches_per_tile_and_oracle(coda, case):
@@ -84,8 +93,8 @@ def test_rope_8192_full_size_sampled(coda):
 
 def test_mfma_probe_closed_form(coda):
     import torch
-    # every operand 1.0: each accumulator element sums 16 products twice per round, so a
-    # thread's 8 x 16 accumulator values add up to 8 * 16 * 32 * iters
+    # every operand 1.0: each accumulator element sums 32 products per round, so a
+    # thread's 32 x 4 accumulator values add up to 128 * 32 * iters
     ones = torch.full((4096 * 8,), 1.0, dtype=torch.bfloat16, device="cuda")
     for iters in (1, 3, 10):
         out = coda.coda_baseline_mfma_loop(ones, iters, 2)

@@ -458,7 +458,7 @@ def coda_baseline_copy(src, dst, stream=None):
 
 def coda_baseline_mfma_loop(operands, iters, grid, out=None, stream=None):
     """Register-only MFMA loop over bf16 `operands` (numel a multiple of 8); returns the
-    per-thread sums [grid * 512] fp32. FLOPs = grid * 8 * iters * 16 * 32768."""
+    per-thread sums [grid * 512] fp32. FLOPs = grid * 8 * iters * 32 * 16384."""
     torch = _torch()
     if operands.numel() % 8:
         raise ValueError("coda_baseline_mfma_loop: operands must hold whole 8-element fragments")

@@ -215,49 +215,44 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4_t* __restrict__ s
 
 inline unsigned blocks_for(long long n, int per_block) { return (unsigned)((n + per_block - 1) / per_block); }
 
-// Register-only MFMA loop, a measurement probe: each thread reads 12 operand fragments
-// once, then every wave runs `iters` rounds of 16 v_mfma_f32_32x32x16_bf16 on 8
-// independent accumulators (the GEMM's per-wave shape, 8 waves per workgroup, two per
-// SIMD) with no memory traffic in between. Fed with operands drawn like the workloads'
-// data, it shows the MFMA rate the chip sustains under its power limit.
+// Register-only MFMA loop, a measurement probe: each thread reads 16 operand fragments
+// once, then every wave runs `iters` rounds of 32 v_mfma_f32_16x16x32_bf16 on 32
+// independent accumulators (the GEMM's per-wave shape: 4 feature blocks x 8 token
+// blocks, 8 waves per workgroup, two per SIMD) with no memory traffic in between; the
+// token blocks 0..3 and 4..7 take different operand sets. Fed with operands drawn like
+// the workloads' data, it shows the MFMA rate the chip sustains under its power limit.
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void mfma_loop_kernel(const bf16x8_t* __restrict__ ops, int n_frag, int iters, float* __restrict__ out) {
   const long long gt = (long long)blockIdx.x * 512 + threadIdx.x;
-  bf16x8_t a[2], b[4], c[2], d[4];
+  bf16x8_t a[4], c[4], b[8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    a[i] = ops[(gt * 12 + i) % n_frag];
-    c[i] = ops[(gt * 12 + 6 + i) % n_frag];
+  for (int i = 0; i < 4; ++i) {
+    a[i] = ops[(gt * 16 + i) % n_frag];
+    c[i] = ops[(gt * 16 + 4 + i) % n_frag];
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    b[j] = ops[(gt * 12 + 2 + j) % n_frag];
-    d[j] = ops[(gt * 12 + 8 + j) % n_frag];
-  }
-  f32x16_t acc[2][4];
+  for (int j = 0; j < 8; ++j) b[j] = ops[(gt * 16 + 8 + j) % n_frag];
+  f32x4_t acc[4][8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.f;
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c[i], d[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 8; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(j < 4 ? a[i] : c[i], b[j], acc[i][j], 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s += acc[i][j][v];
+      for (int v = 0; v < 4; ++v) s += acc[i][j][v];
   out[gt] = s;
 }
 

@@ -10,10 +10,10 @@
 namespace coda {
 
 // The epilogue works in the accumulator layout itself, with no row-major relayout: it has
-// no per-element side input and writes no tile, and a lane already holds 32 of a row's 64
-// wave-features (acc[i][j][4 g + e] is feature 32 i + 8 g + 4 (lane >> 5) + e of token
-// 32 j + (lane & 31)); the lane 32 away holds the other 32. So each row's maximum and sum
-// of exponentials reduce within the lane, then once across the lane pair.
+// no per-element side input and writes no tile, and a lane already holds 16 of a row's 64
+// wave-features (acc[i][j][v] is feature 16 i + 4 (lane >> 4) + v of token
+// 16 j + (lane & 15)); the lanes 16, 32 and 48 away hold the other 48. So each row's
+// maximum and sum of exponentials reduce within the lane, then across those four lanes.
 struct EpiCrossEntropy {
   struct Args {
     const int32_t* labels;  // [M]; outside [0, V) marks an ignored row
@@ -21,7 +21,7 @@ struct EpiCrossEntropy {
     float* target;          // [M] z[m, label[m]] (written by the tile that holds it)
     int nb;
   };
-  // Per 32-token block j: the row's maximum and sum of exp(z - max) over this wave's 64
+  // Per 16-token block j: the row's maximum and sum of exp(z - max) over this wave's 64
   // columns (kFull: all of them inside the width, no column masks), recorded per
   // (wave, row); the lane holding the label's column writes the target logit. The
   // exponential is exp2 of one fused multiply-add; the label search runs only for the
@@ -31,63 +31,56 @@ struct EpiCrossEntropy {
                                               int nbase, const int (&label)[kMJ], float2* red) {
     const float ninf = -__builtin_huge_valf();
     const float l2e = 1.4426950408889634f;
-    const int r32 = L.lane & 31;
-    // columns 32 i + 8 g .. + 3 of this lane are inside the width (N % 8 == 0)
-    bool ok[kNI][4];
+    const int r16 = L.lane & 15;
+    // columns 16 i .. 16 i + 3 of this lane are inside the width (N % 8 == 0)
+    bool ok[kNI];
 #pragma unroll
-    for (int i = 0; i < kNI; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) ok[i][g] = kFull || nbase + 32 * i + 8 * g < p.N;
+    for (int i = 0; i < kNI; ++i) ok[i] = kFull || nbase + 16 * i < p.N;
 #pragma unroll
     for (int j = 0; j < kMJ; ++j) {
       float mx = ninf;
 #pragma unroll
       for (int i = 0; i < kNI; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) mx = ok[i][g] ? fmaxf(mx, acc[i][j][4 * g + e]) : mx;
+        for (int v = 0; v < 4; ++v) mx = ok[i] ? fmaxf(mx, acc[i][j][v]) : mx;
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float shl = (mx == ninf ? 0.f : mx) * l2e;  // a wave with no valid column contributes 0
       float se = 0.f;
 #pragma unroll
       for (int i = 0; i < kNI; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            se += ok[i][g] ? __builtin_amdgcn_exp2f(fmaf(acc[i][j][4 * g + e], l2e, -shl)) : 0.f;
+        for (int v = 0; v < 4; ++v) se += ok[i] ? __builtin_amdgcn_exp2f(fmaf(acc[i][j][v], l2e, -shl)) : 0.f;
+      se += __shfl_xor(se, 16);
       se += __shfl_xor(se, 32);
-      const int m = L.token(32 * j + r32);
+      const int m = L.token(16 * j + r16);
       const int rel = label[j] - nbase;  // this lane's column offset of the label
-      const bool maybe = (unsigned)rel < (unsigned)(2 * 32) && (rel & 4) == 0;
+      const bool maybe = (unsigned)rel < (unsigned)(4 * 16) && (rel & 12) == 0;
       if (__builtin_amdgcn_ballot_w64(maybe) != 0) {  // wave-uniform
         float tv = 0.f;
         bool hit = false;
 #pragma unroll
         for (int i = 0; i < kNI; ++i)
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bool here = ok[i][g] && rel == 32 * i + 8 * g + e;
-              tv = here ? acc[i][j][4 * g + e] : tv;
-              hit = hit || here;
-            }
+          for (int v = 0; v < 4; ++v) {
+            const bool here = ok[i] && rel == 16 * i + v;
+            tv = here ? acc[i][j][v] : tv;
+            hit = hit || here;
+          }
         if (hit && m < p.M) a.target[m] = tv;
       }
-      if (L.lane < 32) red[32 * j + r32] = make_float2(mx, se);
+      if (L.lane < 16) red[16 * j + r16] = make_float2(mx, se);
     }
   }
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
     const EpiLane L(m0, n0, lds.tid);
-    const int r32 = L.lane & 31;
-    const int nbase = n0 + L.wn * kWaveN + 4 * (L.lane >> 5);  // feature of acc[0][j][0]
+    const int r16 = L.lane & 15;
+    const int nbase = n0 + L.wn * kWaveN + 4 * (L.lane >> 4);  // feature of acc[0][j][0]
     const WaveRowsF32 lab((const float*)a.labels, L, p.M);
     int label[kMJ];
 #pragma unroll
-    for (int j = 0; j < kMJ; ++j) label[j] = __builtin_bit_cast(int, lab.load(32 * j + r32));
+    for (int j = 0; j < kMJ; ++j) label[j] = __builtin_bit_cast(int, lab.load(16 * j + r16));
     float2* red = (float2*)lds.red + (L.wm * kWavesN + L.wn) * 128;
     if (n0 + kBN <= p.N)  // wave-uniform: the whole tile lies inside the width
       rows<true>(acc, a, p, L, nbase, label, red);

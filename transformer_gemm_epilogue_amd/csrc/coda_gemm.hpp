@@ -6,17 +6,22 @@
 // projections) or [N, K] row-major ("NK", depth contiguous: the grad GEMM dY W1^T).
 //
 // Workgroup tile: 256 tokens x 256 features, 512 threads = 8 waves, two per SIMD, in a
-// 2 (tokens) x 4 (features) arrangement; each wave owns 128 tokens x 64 features = 2 x 4
-// blocks of v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane). While one wave of
-// a SIMD waits on a barrier or an LDS read, the other keeps the MFMA pipe busy.
+// 2 (tokens) x 4 (features) arrangement; each wave owns 128 tokens x 64 features = 4 x 8
+// blocks of v_mfma_f32_16x16x32_bf16 (128 fp32 accumulators per lane). While one wave of
+// a SIMD waits on a barrier or an LDS read, the other keeps the MFMA pipe busy. The
+// 16x16x32 form reads and writes a quarter of the accumulator bytes per flop of the
+// 32x32x16 one; on gfx950, whose clock is set by power on this loop, that buys a higher
+// clock (measured on MI355X, gaussian operands: +7% in a register-only loop, +4-8% for
+// this main loop together with the paired X loads below).
 //
 // Transposed MFMA formulation. The MFMA "A" operand (rows of the MFMA output) is the
 // W slice, so MFMA rows are FEATURES; the "B" operand is the X slice, so MFMA columns
-// are TOKENS. With the 32x32 output layout (lane l, register v holds row
-// 8*(v/4) + 4*(l/32) + v%4, column l%32), every lane holds, for one token, runs of 4
-// consecutive features. The epilogue keeps that property when it re-lays each wave's
-// block out row-major (16 lanes per token, 4 consecutive features per lane): the
-// (even, odd) feature pairs of RoPE and SwiGLU stay in one lane's registers.
+// are TOKENS. An operand lane l holds row l % 16 of its block at depth 8 (l / 16) .. +7;
+// in the 16x16 output layout lane l, register v holds row 4 (l / 16) + v, column l % 16,
+// so every lane holds, for one token, runs of 4 consecutive features. The epilogue keeps
+// that property when it re-lays each wave's block out row-major (16 lanes per token, 4
+// consecutive features per lane): the (even, odd) feature pairs of RoPE and SwiGLU stay
+// in one lane's registers.
 //
 // Data movement. Both operand tiles go from HBM straight into LDS with
 // buffer_load_dwordx4 ... lds (no register staging), through a ring of 5 LDS stages of
@@ -29,14 +34,19 @@
 // free of bank conflicts. Raw buffer descriptors make rows past M, depth past K and
 // columns past N read as zero, so ragged edges need no special path.
 //
-// Schedule of one depth-step S (two k16 sub-steps), per wave:
-//   read the sub-step-1 operands of S | 8 MFMAs of sub-step 0 of S, and the W half of
+// Schedule of one depth-step S (32 MFMAs per wave: 4 feature blocks x 8 token blocks),
+// per wave:
+//   read X blocks 4..7 of S | the 16 MFMAs on token blocks 0..3 of S, and the W half of
 //   the DMA of S+3 into the slot of S-2 | wait for this thread's loads of S+1, barrier
-//   (S+1 complete for every wave, S-1 no longer read by anyone) | 8 MFMAs of sub-step 1
-//   of S, interleaved one for one with the reads of sub-step 0 of S+1 and the X half of
-//   the DMA of S+4 into the slot of S-1.
+//   (S+1 complete for every wave, S-1 no longer read by anyone) | the 16 MFMAs on token
+//   blocks 4..7 of S, interleaved one for one with the reads of W and X blocks 0..3 of
+//   S+1, and, on odd steps, the X halves of the DMA of S+3 and S+4 (slots of S-2, S-1).
+// X loads go in pairs because a 32-deep X row is 64 bytes, half of a 128-byte vector-L1
+// line: issued back to back, the loads of steps 2p and 2p+1 share each line, where
+// loads a step apart fetched every line from L2 twice (measured on MI355X: L1 -> L2
+// requests 87.8 M -> 58.8 M per 8192 x 4096 x 14336 product, and less power).
 // A slot is written only after the barrier that follows its last reader's consumption,
-// and the load issue is spread over the whole step: on gfx950 the operand delivery is
+// and the load issue is spread over the steps: on gfx950 the operand delivery is
 // bounded by how many DMA loads are in flight (texture data path busy, waiting on L1),
 // and the fifth stage raises that bound from 8 to 12 loads per wave.
 // The order is pinned with scheduling barriers; the code is straight-line (the DMA of
@@ -57,9 +67,9 @@ constexpr int kStages = 5;      // LDS ring depth
 constexpr int kWaves = 8;       // two per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWavesN = 4;      // waves along features
-constexpr int kNI = 2;          // 32-feature MFMA blocks per wave
-constexpr int kMJ = 4;          // 32-token MFMA blocks per wave
-constexpr int kWaveN = 32 * kNI;  // features per wave (64)
+constexpr int kNI = 4;          // 16-feature MFMA blocks per wave
+constexpr int kMJ = 8;          // 16-token MFMA blocks per wave
+constexpr int kWaveN = 16 * kNI;  // features per wave (64)
 constexpr int kXJ = 16 / kWaves;  // 1 KiB DMA instructions per wave per operand per step
 constexpr int kLoadsPerStep = 2 * kXJ;  // 16-byte DMA loads per thread per step
 constexpr int kTileBytes = kBM * kBK * 2;  // one operand tile per stage: 16 KiB
@@ -93,16 +103,22 @@ struct LdsRing {
 // tiles). gfx950 serves a 64-lane ds_read_b128 in four groups of 16 lanes over 64
 // banks; measured with the LDS bank-conflict counter, a group is one 32-lane half split
 // by lane bit 4 XOR lane bit 2 (give or take lanes bits 0, 1, 3). The operand read has
-// lane l on row l % 32, chunk 2 ks + l / 32, so XOR-ing the chunk with row bits 2 and 3
-// spreads every such group over all 64 banks, whichever of those lane bits join in.
-__device__ __forceinline__ uint32_t swz_k(int row) { return (uint32_t)(((row >> 2) & 1) | (((row >> 3) & 1) << 1)); }
+// lane l on row l % 16, chunk l / 16, so XOR-ing the chunk with 2 on rows whose bit 3 is
+// set spreads every such group over all 64 banks, whichever of those lane bits join in
+// (row bit 2 must stay out: it follows lane bit 2). The DMA writes whole 64-byte rows
+// per 4 lanes, which any per-row permutation of the chunks keeps conflict-free.
+__device__ __forceinline__ uint32_t swz_k(int row) { return (uint32_t)(((row >> 3) & 1) << 1); }
 __device__ __forceinline__ uint32_t krow_off(int row, int chunk) {
   return ((uint32_t)row << 6) | (((uint32_t)chunk ^ swz_k(row)) << 4);
 }
-// Swizzle of the 32 chunks of a 512-byte KN-W row: a transposed read touches 4
-// consecutive depth rows x 2 (or 4) chunks; rows r = 0..3 (mod 4) XOR with 0, 6, 10,
-// 12, which spreads those 8 (16) chunks over distinct banks.
-__device__ __forceinline__ uint32_t swz_n(int row) { return (0xCA60u >> (4 * (row & 3))) & 0xFu; }
+// Swizzle of the 32 chunks of a 512-byte KN-W row: each 16-lane group of a transposed
+// read touches 4 consecutive depth rows x 2 chunks, and the two groups served together
+// (32 lanes, 256 bytes) read the same chunks 8 rows apart. Rows r = 0..3 (mod 4) XOR
+// with 0, 6, 10, 12, which spreads a group's 8 chunks over distinct banks, and rows with
+// bit 3 set XOR with 2 more, which moves the partner group onto the other 8.
+__device__ __forceinline__ uint32_t swz_n(int row) {
+  return ((0xCA60u >> (4 * (row & 3))) & 0xFu) ^ ((uint32_t)((row >> 3) & 1) << 1);
+}
 __device__ __forceinline__ uint32_t nrow_off(int row, int chunk) {
   return ((uint32_t)row << 9) | (((uint32_t)chunk ^ swz_n(row)) << 4);
 }
@@ -140,8 +156,10 @@ __device__ __forceinline__ void tile_coords(int M, int N, int K, int group_m, in
 // the XCD that workgroup t, or a persistent workgroup t mod 8k, runs on), so the XCDs
 // stream different depth ranges of the shared panels at any moment instead of all
 // hitting the same addresses. The tile's sum covers the same products; only the
-// (fixed, deterministic) accumulation order changes, and it depends on t alone.
-__device__ __forceinline__ int k_rotation(int t, int KT) { return (t % 8) * (KT / 8); }
+// (fixed, deterministic) accumulation order changes, and it depends on t alone. The
+// rotation is an even number of steps, so that paired X loads (steps 2p, 2p+1) still
+// share 128-byte lines.
+__device__ __forceinline__ int k_rotation(int t, int KT) { return (t % 8) * ((KT / 8) & ~1); }
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -193,7 +211,7 @@ struct TileSrc {
   bool w_col_ok[kXJ];
 };
 
-typedef f32x16_t AccTile[kNI][kMJ];
+typedef f32x4_t AccTile[kNI][kMJ];
 
 template <bool kWKN>
 struct Mainloop {
@@ -206,8 +224,8 @@ struct Mainloop {
   const uint16_t* xbase;
   const uint16_t* wbase;
   int M, N, K, KT;          // KT: depth steps
-  uint32_t xr_off[2];       // operand read offsets within a slot, per k16 sub-step
-  uint32_t wr_off[2][kNI][2];
+  uint32_t xr_off;          // operand read offsets within a slot: X block 0
+  uint32_t wr_off[2];       // W block 0 (KN: the two transposed halves)
 
   // Everything that does not depend on the output tile; tid is the thread index.
   __device__ __forceinline__ void init(const GemmProblem& p, int tid) {
@@ -242,30 +260,27 @@ struct Mainloop {
         w_col[j] = 0u;
       }
     }
-    const int r32 = lane & 31, hs = lane >> 5;
+    // operand lane l: row l % 16 of its block, depth 8 (l / 16) .. +7 of the step
+    const int r16 = lane & 15, g = lane >> 4;
+    xr_off = krow_off(wm * 128 + r16, g);
+    if constexpr (kWKN) {
+      // transposed read: in each 16-lane group, lane 4e+q points at depth row e of the
+      // group's 4 rows, features 4q..4q+3; lane i receives feature i of all 4 rows.
+      // Block i's chunk is that of block 0 OR 2 i (bits 1, 2 of block 0's chunk are
+      // clear), so its offset is block 0's XOR 32 i: no bits of the row, the half-chunk
+      // or the tile base carry into bits 5, 6.
+      const int e = r16 >> 2, q = r16 & 3;
+      const int nb = wn * kWaveN + 4 * q;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      xr_off[ks] = krow_off(wm * 128 + r32, 2 * ks + hs);
-      if constexpr (kWKN) {
-        // transposed read: in each 16-lane group, lane 4e+q points at depth row e of the
-        // group's 4 rows, features 4q..4q+3; lane i receives feature i of all 4 rows
-        const int g = lane >> 4, s = lane & 15, e = s >> 2, q = s & 3;
-#pragma unroll
-        for (int i = 0; i < kNI; ++i) {
-          const int nb = wn * kWaveN + i * 32 + (g & 1) * 16 + 4 * q;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int row = ks * 16 + (g >> 1) * 8 + 4 * h + e;
-            wr_off[ks][i][h] = kTileBytes + nrow_off(row, nb >> 3) + (uint32_t)((nb >> 2) & 1) * 8u;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < kNI; ++i) {
-          wr_off[ks][i][0] = kTileBytes + krow_off(wn * kWaveN + i * 32 + r32, 2 * ks + hs);
-          wr_off[ks][i][1] = 0;
-        }
+      for (int h = 0; h < 2; ++h) {
+        const int row = 8 * g + 4 * h + e;
+        wr_off[h] = kTileBytes + nrow_off(row, nb >> 3) + (uint32_t)((nb >> 2) & 1) * 8u;
       }
+    } else {
+      // NK-W rows are features: block i is 16 rows (1 KiB) on, and the swizzle uses only
+      // row bit 3
+      wr_off[0] = kTileBytes + krow_off(wn * kWaveN + r16, g);
+      wr_off[1] = 0;
     }
   }
 
@@ -312,23 +327,26 @@ struct Mainloop {
     for (int j = 0; j < kLoadsPerStep; ++j) issue_one(s, slot, kt, j);
   }
 
-  __device__ __forceinline__ void read(const char* slot, int ks, bf16x8_t (&a)[kNI], bf16x8_t (&b)[kMJ]) const {
-    // Opaque, wave-uniform slot base: keeps the compiler from hoisting one address
-    // register per (slot, read) out of the loop.
+  // Opaque, wave-uniform slot base: keeps the compiler from hoisting one address
+  // register per (slot, read) out of the loop.
+  __device__ __forceinline__ static uint32_t opaque_base(const char* slot) {
     uint32_t base = lds_addr(slot);
     asm volatile("" : "+s"(base));
-    const uint32_t xb = base + xr_off[ks];
-#pragma unroll
-    for (int j = 0; j < kMJ; ++j) b[j] = *(lds_b128_ptr)(uintptr_t)(xb + j * 32 * 64);
-#pragma unroll
-    for (int i = 0; i < kNI; ++i) {
-      if constexpr (kWKN) {
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr_ptr)(uintptr_t)(base + wr_off[ks][i][0]));
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr_ptr)(uintptr_t)(base + wr_off[ks][i][1]));
-        a[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      } else {
-        a[i] = *(lds_b128_ptr)(uintptr_t)(base + wr_off[ks][i][0]);
-      }
+    return base;
+  }
+  // X operand block j (16 tokens) of a slot
+  __device__ __forceinline__ bf16x8_t read_x(const char* slot, int j) const {
+    return *(lds_b128_ptr)(uintptr_t)(opaque_base(slot) + xr_off + (uint32_t)j * 16u * 64u);
+  }
+  // W operand block i (16 features) of a slot
+  __device__ __forceinline__ bf16x8_t read_w(const char* slot, int i) const {
+    const uint32_t base = opaque_base(slot);
+    if constexpr (kWKN) {
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr_ptr)(uintptr_t)(base + (wr_off[0] ^ (32u * i))));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr_ptr)(uintptr_t)(base + (wr_off[1] ^ (32u * i))));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      return *(lds_b128_ptr)(uintptr_t)(base + wr_off[0] + (uint32_t)i * 16u * 64u);
     }
   }
 };
@@ -352,14 +370,29 @@ __device__ __forceinline__ TileSrc pick(bool second, const TileSrc& a, const Til
   return s;
 }
 
-// Prologue: steps 0, 1, 2 and the X half of step 3 in flight; wait for step 0.
+// X loads of depth steps kk (into slot a) and kk + 1 (slot b), row halves back to back.
+template <bool kWKN>
+__device__ __forceinline__ void issue_x_pair(const Mainloop<kWKN>& ml, const TileSrc& src, char* a, char* b, int kk) {
+  ml.issue_one(src, a, kk, 0);
+  ml.issue_one(src, b, kk + 1, 0);
+  ml.issue_one(src, a, kk, 1);
+  ml.issue_one(src, b, kk + 1, 1);
+}
+
+// Prologue: the loads the schedule would issue in its steps -3, -2, -1 (W of 0; X of 0
+// and 1; W of 1; W of 2; X of 2 and 3), so that the loop's wait counts hold from step 0
+// on; wait for step 0.
 template <bool kWKN>
 __device__ __forceinline__ void mainloop_prologue(const Mainloop<kWKN>& ml, const TileSrc& src, const LdsRing& lds) {
-#pragma unroll
-  for (int s = 0; s < 3; ++s) ml.issue(src, lds.slot[s], s);
-  ml.issue_one(src, lds.slot[3], 3, 0);
-  ml.issue_one(src, lds.slot[3], 3, 1);
-  wait_vmcnt<10>();
+  ml.issue_one(src, lds.slot[0], 0, 2);
+  ml.issue_one(src, lds.slot[0], 0, 3);
+  issue_x_pair(ml, src, lds.slot[0], lds.slot[1], 0);
+  ml.issue_one(src, lds.slot[1], 1, 2);
+  ml.issue_one(src, lds.slot[1], 1, 3);
+  ml.issue_one(src, lds.slot[2], 2, 2);
+  ml.issue_one(src, lds.slot[2], 2, 3);
+  issue_x_pair(ml, src, lds.slot[2], lds.slot[3], 2);
+  wait_vmcnt<9>();  // 9 loads were issued after step 0's last one
   __builtin_amdgcn_s_barrier();
 }
 
@@ -369,12 +402,12 @@ __device__ __forceinline__ void mainloop_prologue(const Mainloop<kWKN>& ml, cons
 constexpr int kNextSteps = 2;
 
 // Start of a persistent workgroup's next tile, after its epilogue and a barrier: steps
-// 0 and 1 are already in LDS; put step 2 and the X half of step 3 in flight.
+// 0 and 1 are already in LDS; put the loads of step -1 (W of 2; X of 2 and 3) in flight.
 template <bool kWKN>
 __device__ __forceinline__ void mainloop_resume(const Mainloop<kWKN>& ml, const TileSrc& src, const LdsRing& lds) {
-  ml.issue(src, lds.slot[2], 2);
-  ml.issue_one(src, lds.slot[3], 3, 0);
-  ml.issue_one(src, lds.slot[3], 3, 1);
+  ml.issue_one(src, lds.slot[2], 2, 2);
+  ml.issue_one(src, lds.slot[2], 2, 3);
+  issue_x_pair(ml, src, lds.slot[2], lds.slot[3], 2);
 }
 
 // The depth loop of one tile, after its prologue (or resume). With kPersist and a next
@@ -388,13 +421,11 @@ __device__ __forceinline__ void mainloop_body(const Mainloop<kWKN>& ml, const Ti
 #pragma unroll
   for (int i = 0; i < kNI; ++i)
 #pragma unroll
-    for (int j = 0; j < kMJ; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    for (int j = 0; j < kMJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int KT = ml.KT;
-  constexpr int kReads = kMJ + (kWKN ? 2 * kNI : kNI);  // LDS read instructions per k16 sub-step
-  constexpr int kMfma = kNI * kMJ;                      // MFMAs per k16 sub-step
+  constexpr int kH = kMJ / 2;                           // token blocks per half step
+  constexpr int kMfmaH = kNI * kH;                      // MFMAs per half step
 
   // load j of schedule step kk: in a tail step (kTail) of a persistent workgroup it may
   // be a step of the next tile; elsewhere it is this tile's (or a zero fill)
@@ -406,70 +437,102 @@ __device__ __forceinline__ void mainloop_body(const Mainloop<kWKN>& ml, const Ti
       ml.issue_one(cur, slot, kk, j);
     }
   };
-  const std::false_type steady;
-  const std::true_type tail;
+  const std::false_type steady, even;
+  const std::true_type tail, odd;
 
-  bf16x8_t a0[kNI], b0[kMJ], a1[kNI], b1[kMJ];
-  ml.read(lds.slot[0], 0, a0, b0);
+  bf16x8_t a[kNI], b[kMJ];
+#pragma unroll
+  for (int i = 0; i < kNI; ++i) a[i] = ml.read_w(lds.slot[0], i);
+#pragma unroll
+  for (int j = 0; j < kH; ++j) b[j] = ml.read_x(lds.slot[0], j);
 
-  auto step = [&](const int S, const int kt, auto kind) {
-    ml.read(lds.slot[S], 1, a1, b1);
+  // Step kt (ring slot S = kt mod 5). Loads: W of kt+3 each step; X of kt+3 and kt+4 on
+  // odd steps. Issue order over the steps makes 8 loads follow the last one of step
+  // kt+1 at an even step's wait, 5 at an odd step's. Every operand read lands in the
+  // registers of a block no MFMA needs any more (X blocks 4..7 of this step in those of
+  // the last step's, X blocks 0..3 of the next step in those of this step's, W block i
+  // of the next step right after this step's last MFMA on W block i), so the operands
+  // take 12 registers of 8 bf16, as many as the blocks in use.
+  auto step = [&](const int S, const int kt, auto parity, auto kind) {
+    constexpr bool kOdd = decltype(parity)::value;
+#pragma unroll
+    for (int j = kH; j < kMJ; ++j) b[j] = ml.read_x(lds.slot[S], j);
 #pragma unroll
     for (int i = 0; i < kNI; ++i)
 #pragma unroll
-      for (int j = 0; j < kMJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);  // sub-step-1 reads first
-    __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);   // then the sub-step-0 MFMAs
+      for (int j = 0; j < kH; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kH, 0);      // second-half X reads first
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfmaH, 0);  // then the first-half MFMAs
     // W half of step kt+3 into the slot of kt-2 (free since the previous barrier)
     issue_at(lds.slot[(S + 3) % kStages], kt + 3, 2, kind);
     issue_at(lds.slot[(S + 3) % kStages], kt + 3, 3, kind);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<8>();  // this thread's loads of step kt+1 have landed
+    if constexpr (kOdd)
+      wait_vmcnt<5>();  // this thread's loads of step kt+1 have landed
+    else
+      wait_vmcnt<8>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    bf16x8_t na[kNI], nb[kMJ];
-    ml.read(lds.slot[(S + 1) % kStages], 0, na, nb);
+    const char* next = lds.slot[(S + 1) % kStages];
 #pragma unroll
-    for (int r = 0; r < kMfma; ++r) {
-      const int i = r / kMJ, j = r % kMJ;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
-      // X half of step kt+4 into the slot of kt-1 (free since this step's barrier)
-      if (r < 2) issue_at(lds.slot[(S + 4) % kStages], kt + 4, r, kind);
+    for (int r = 0; r < kMfmaH; ++r) {
+      const int i = r / kH, j = kH + r % kH;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      // odd steps: X of kt+3 and kt+4 into the slots of kt-2 and kt-1 (free since the
+      // previous barrier and this one), the two halves of each row back to back
+      if (kOdd && r < 4) issue_at(lds.slot[(S + 3 + (r & 1)) % kStages], kt + 3 + (r & 1), r >> 1, kind);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      if (r < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      if (r < kH) {
+        b[r] = ml.read_x(next, r);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
+      if (r % kH == kH - 1) {  // the last MFMA on W block i
+        a[i] = ml.read_w(next, i);
+        __builtin_amdgcn_sched_group_barrier(0x100, kWKN ? 2 : 1, 1);
+      }
     }
-#pragma unroll
-    for (int i = 0; i < kNI; ++i) a0[i] = na[i];
-#pragma unroll
-    for (int j = 0; j < kMJ; ++j) b0[j] = nb[j];
+    // nothing moves across steps: an operand read pulled ahead of the MFMAs still using
+    // the registers it lands in would need registers of its own
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   int kt = 0;
-  // steady state; a persistent workgroup leaves the last 4 to 8 steps, whose loads
-  // reach past this tile, to the tail below
+  // ten steps per round: ring slot and parity both repeat. A persistent workgroup
+  // leaves the last 4 to 13 steps, whose loads reach past this tile, to the tail.
   constexpr int kLook = kPersist ? 4 : 0;
-  for (; kt + kStages + kLook <= KT; kt += kStages) {
-    step(0, kt, steady);
-    step(1, kt + 1, steady);
-    step(2, kt + 2, steady);
-    step(3, kt + 3, steady);
-    step(4, kt + 4, steady);
+  for (; kt + 2 * kStages + kLook <= KT; kt += 2 * kStages) {
+    step(0, kt, even, steady);
+    step(1, kt + 1, odd, steady);
+    step(2, kt + 2, even, steady);
+    step(3, kt + 3, odd, steady);
+    step(4, kt + 4, even, steady);
+    step(0, kt + 5, odd, steady);
+    step(1, kt + 6, even, steady);
+    step(2, kt + 7, odd, steady);
+    step(3, kt + 8, even, steady);
+    step(4, kt + 9, odd, steady);
   }
-  if constexpr (kPersist) {
-    step(0, kt, tail);
-    step(1, kt + 1, tail);
-    step(2, kt + 2, tail);
-    step(3, kt + 3, tail);
-    if (kt + 4 < KT) step(4, kt + 4, tail);
-    if (kt + 5 < KT) step(0, kt + 5, tail);
-    if (kt + 6 < KT) step(1, kt + 6, tail);
-    if (kt + 7 < KT) step(2, kt + 7, tail);
-  } else {
-    if (kt < KT) step(0, kt, steady);
-    if (kt + 1 < KT) step(1, kt + 1, steady);
-    if (kt + 2 < KT) step(2, kt + 2, steady);
-    if (kt + 3 < KT) step(3, kt + 3, steady);
-  }
+  // (each step its own block: as one straight block the tail does not fit the
+  // register budget)
+  auto rest = [&](auto kind) {
+    if (kt < KT) step(0, kt, even, kind);
+    if (kt + 1 < KT) step(1, kt + 1, odd, kind);
+    if (kt + 2 < KT) step(2, kt + 2, even, kind);
+    if (kt + 3 < KT) step(3, kt + 3, odd, kind);
+    if (kt + 4 < KT) step(4, kt + 4, even, kind);
+    if (kt + 5 < KT) step(0, kt + 5, odd, kind);
+    if (kt + 6 < KT) step(1, kt + 6, even, kind);
+    if (kt + 7 < KT) step(2, kt + 7, odd, kind);
+    if (kt + 8 < KT) step(3, kt + 8, even, kind);
+    if (kPersist && kt + 9 < KT) step(4, kt + 9, odd, kind);
+    if (kPersist && kt + 10 < KT) step(0, kt + 10, even, kind);
+    if (kPersist && kt + 11 < KT) step(1, kt + 11, odd, kind);
+    if (kPersist && kt + 12 < KT) step(2, kt + 12, even, kind);
+  };
+  if constexpr (kPersist)
+    rest(tail);
+  else
+    rest(steady);
   wait_vmcnt<0>();  // zero-fill loads (and the next tile's first steps) have landed
   __syncthreads();  // all operand reads are done before the free slots hold epilogue data
 }
@@ -493,12 +556,12 @@ __device__ __forceinline__ LdsRing make_ring(char* smem, int rot, int e, int tid
 
 // ------------------------------------------------------------------------------------
 // Epilogue. Accumulator block acc[i][j] of a lane covers features
-//   n = n0 + wn*64 + 32 i + 8 g + 4 (lane >> 5) + e,  (register v = 4 g + e)
-// for the token m = m0 + wm*128 + 32 j + (lane & 31): one lane spans 32 tokens, which
-// makes direct loads of per-element side inputs 8-byte gathers from 32 rows. So each
-// wave first re-lays its 128 x 64 fp32 block out row-major through a private 8 KiB LDS
-// area (32 tokens at a time) and then walks it with 16 lanes per token, 4 features per
-// lane: side inputs (residual, gamma, rotary tables, saved activations) are read and
+//   n = n0 + wn*64 + 16 i + 4 (lane >> 4) + v  (register v = 0..3)
+// for the token m = m0 + wm*128 + 16 j + (lane & 15): one lane spans 16 tokens of each
+// feature run, which makes direct loads of per-element side inputs 8-byte gathers from
+// 16 rows. So each wave first re-lays its 128 x 64 fp32 block out row-major through a
+// private 8 KiB LDS area (32 tokens at a time) and then walks it with 16 lanes per
+// token, 4 features per lane: side inputs (residual, gamma, rotary tables, saved activations) are read and
 // outputs written as whole 128-byte row segments, and a row statistic is a 16-lane
 // reduction. No barrier is needed between a wave's own staging writes and reads (one
 // wave's LDS operations complete in order); the only workgroup barrier after the main
@@ -556,20 +619,13 @@ __device__ __forceinline__ f32x4_t epilogue_rows(AccTile& acc, const LdsRing& ld
   const int cq = L.lane & 15, rq = L.lane >> 4;
   typedef typename Op::Pre Pre;
   typedef typename StatOf<Op>::type Stat;
-  // stage accumulator block j (32 tokens) at staging rows row0 .. row0 + 31
-  auto stage = [&](int j, int row0) {
+  // stage token blocks 2J, 2J + 1 (32 tokens) at staging rows 0 .. 31
+  auto stage = [&](int J) {
 #pragma unroll
-    for (int i = 0; i < kNI; ++i)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x16_t& a = acc[i][j];
-        f32x4_t v;
-        v.x = a[4 * g];
-        v.y = a[4 * g + 1];
-        v.z = a[4 * g + 2];
-        v.w = a[4 * g + 3];
-        *(lds_f32x4_ptr)(uintptr_t)(sb + stg_off(row0 + (L.lane & 31), 8 * i + 2 * g + (L.lane >> 5))) = v;
-      }
+      for (int i = 0; i < kNI; ++i)
+        *(lds_f32x4_ptr)(uintptr_t)(sb + stg_off(16 * h + (L.lane & 15), 4 * i + (L.lane >> 4))) = acc[i][2 * J + h];
   };
   // rows row0 + 8 rq + it (it = 0..7) of the staging area are wave rows r0 + 8 rq + it
   auto walk8 = [&](int row0, int r0, const Pre (&pre)[8], Stat (&stat)[8]) {
@@ -604,10 +660,11 @@ __device__ __forceinline__ f32x4_t epilogue_rows(AccTile& acc, const LdsRing& ld
   Pre pre[2][8];
 #pragma unroll
   for (int it = 0; it < 8; ++it) pre[0][it] = op.fetch(8 * rq + it);
+  constexpr int kBlocks = 128 / kStgRows;
 #pragma unroll
-  for (int j = 0; j < kMJ; ++j) {
-    stage(j, 0);
-    if (j + 1 < kMJ) {
+  for (int j = 0; j < kBlocks; ++j) {
+    stage(j);
+    if (j + 1 < kBlocks) {
 #pragma unroll
       for (int it = 0; it < 8; ++it) pre[(j + 1) & 1][it] = op.fetch(32 * (j + 1) + 8 * rq + it);
     }
