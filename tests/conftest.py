@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests cannot run without a visible GPU: skip them (loudly) rather than fail
-    # in a CPU-only container. On a GPU machine they run and call the HIP library.
+    # in a CPU-only container. On a machine with a GPU they run and call the HIP library.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
