@@ -18,6 +18,9 @@ constexpr uint32_t kBufferWord3 = 0x00020000u;
 // A byte offset that lies beyond every buffer range built in this library (ranges are
 // capped below 2^31), so a load from it returns zero and a store to it is dropped.
 constexpr uint32_t kOutOfRange = 0x80000000u;
+// Cache-policy operand of the buffer load/store builtins on gfx950: bit 1 is nt
+// (non-temporal: stream the line, keep it from displacing reused data).
+constexpr int kCachePolicyNT = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kBufferWord3);

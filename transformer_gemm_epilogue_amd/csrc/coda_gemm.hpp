@@ -755,6 +755,10 @@ struct WaveRowsF32 {  // [M] fp32, one value per row
 // width starts from an out-of-range column offset (2^31; adding a row offset below 2^30
 // keeps it out of every range), so those stores are dropped by the hardware and the
 // stores need no branch. Outputs of the same shape share one row offset (row_off).
+// The stores are non-temporal (cache policy nt): a tile's outputs are not read again by
+// this kernel, and streaming them keeps the operand panels that other tiles still read
+// in L2 and the Infinity Cache (measured on MI355X: GEMM1 -1.8% / -2.3% time, GEMM2
+// -1.2% / -0.4%, interleaved against normal stores on two boxes).
 struct WaveRowsOutBf16 {
   __amdgpu_buffer_rsrc_t rs;
   uint32_t pitch, coff;
@@ -771,7 +775,7 @@ struct WaveRowsOutBf16 {
     u32x2_t v;
     v.x = pack_bf16x2(a, b);
     v.y = pack_bf16x2(c, d);
-    __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, kCachePolicyNT);
   }
   __device__ __forceinline__ void store4(int r, float a, float b, float c, float d) const {
     store4_at(row_off(r), a, b, c, d);
@@ -783,7 +787,7 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* __restrict__ base, size_t
   u32x2_t v;
   v.x = pack_bf16x2(a, b);
   v.y = pack_bf16x2(c, d);
-  *(u32x2_t*)(base + idx) = v;
+  __builtin_nontemporal_store(v, (u32x2_t*)(base + idx));
 }
 
 // ---------------------------------------------------------------- plain store (baseline)
