@@ -504,6 +504,8 @@ def main():
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain 1 GiB copy kernel (reference for HBM traffic counters)")
+    ap.add_argument("--aux-sweep-only", action="store_true",
+                    help="only run the auxiliary row reduction's bandwidth sweep (for profiling it)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused GEMM-epilogue path is row-independent and "
@@ -523,6 +525,9 @@ def main():
             coda.coda_baseline_copy(src, dst)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": src.numel() * 2, "launches": args.steps}), flush=True)
+        return
+    if args.aux_sweep_only:
+        print(json.dumps({"aux_reduce_sweep": aux_reduce_sweep(coda, torch, args.reps)}), flush=True)
         return
     aux_cool = None if args.headline_only else aux_reduce_sweep(coda, torch, args.reps)
     torch.cuda.empty_cache()
