@@ -118,29 +118,23 @@ struct EpiSwiGLUBwd {
   };
   __device__ __forceinline__ static uint32_t pair_grad(float d, uint32_t gu) {
     const float g = bf16_lo(gu), u = bf16_hi(gu);
-    const float sg = 1.0f / (1.0f + __expf(-g));
+    const float sg = sigmoid_f32(g);
     return pack_bf16x2(d * u * (sg * (1.0f + g * (1.0f - sg))), d * (g * sg));
   }
   struct Op {
-    const EpiLane& L;
-    const Args& a;
-    int M, N, n;
-    bool nok;
-    WaveRowsBf16 hv;
+    WaveRowsBf16 hv;       // [M, 2F] saved (G, U) pairs of this lane's 4 columns
+    WaveRowsOutBf16 dho;   // [M, 2F] their gradients, same positions
     static constexpr bool kRowStat = false;
     static constexpr bool kColStat = false;
     typedef u32x4_t Pre;
     __device__ __forceinline__ Pre fetch(int r) const { return hv.load8(r); }
     __device__ __forceinline__ float row(int r, const f32x4_t& v, const Pre& t) const {
-      const int m = L.token(r);
-      if (nok && m < M) {
-        u32x4_t o;
-        o.x = pair_grad(v.x, t.x);
-        o.y = pair_grad(v.y, t.y);
-        o.z = pair_grad(v.z, t.z);
-        o.w = pair_grad(v.w, t.w);
-        *(u32x4_t*)(a.dh + (size_t)m * (2 * (size_t)N) + 2 * n) = o;
-      }
+      u32x4_t o;
+      o.x = pair_grad(v.x, t.x);
+      o.y = pair_grad(v.y, t.y);
+      o.z = pair_grad(v.z, t.z);
+      o.w = pair_grad(v.w, t.w);
+      dho.store8_at(dho.row_off(r), o);
       return 0.f;
     }
   };
@@ -149,7 +143,7 @@ struct EpiSwiGLUBwd {
     const EpiLane L(m0, n0, lds.tid);
     const int n = L.col4();
     const bool nok = n < p.N;
-    Op op{L, a, p.M, p.N, n, nok, WaveRowsBf16(a.h, L, p.M, 2 * p.N, 2 * n, nok)};
+    Op op{WaveRowsBf16(a.h, L, p.M, 2 * p.N, 2 * n, nok), WaveRowsOutBf16(a.dh, L, p.M, 2 * p.N, 2 * n, nok)};
     epilogue_rows(acc, lds, L, op);
   }
 };

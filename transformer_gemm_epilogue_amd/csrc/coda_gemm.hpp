@@ -780,6 +780,14 @@ struct WaveRowsOutBf16 {
   __device__ __forceinline__ void store4(int r, float a, float b, float c, float d) const {
     store4_at(row_off(r), a, b, c, d);
   }
+  // bf16 of (a, b) at byte offset `off`
+  __device__ __forceinline__ void store2_at(uint32_t off, float a, float b) const {
+    __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(a, b), rs, off, 0, kCachePolicyNT);
+  }
+  // 16 bytes (8 bf16, already packed) at byte offset `off`
+  __device__ __forceinline__ void store8_at(uint32_t off, const u32x4_t& v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, kCachePolicyNT);
+  }
 };
 
 __device__ __forceinline__ void store_bf16x4(uint16_t* __restrict__ base, size_t idx, float a, float b, float c,
@@ -961,7 +969,10 @@ struct EpiRope {
 };
 
 // ---------------------------------------------- SwiGLU: out[m, j] = silu(G_j) * U_j
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+// sigmoid(g) = 1 / (1 + e^-g) through the hardware reciprocal (about 1 ulp, far below the
+// bf16 rounding of the output); g -> -inf gives rcp(inf) = 0 exactly.
+__device__ __forceinline__ float sigmoid_f32(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu_f32(float g) { return g * sigmoid_f32(g); }
 
 struct EpiSwiGLU {
   struct Args {
@@ -969,27 +980,21 @@ struct EpiSwiGLU {
     int F;  // output width (= N / 2)
   };
   struct Op {
-    const EpiLane& L;
-    const Args& a;
-    int M, N, n;
+    WaveRowsOutBf16 out;  // [M, F]: this lane's two outputs at column n / 2
     static constexpr bool kRowStat = false;
     static constexpr bool kColStat = false;
     typedef NoPre Pre;
     __device__ __forceinline__ Pre fetch(int) const { return Pre{}; }
     __device__ __forceinline__ float row(int r, const f32x4_t& v, const Pre&) {
-      const int m = L.token(r);
-      if (m < M && n < N) {
-        const float y0 = silu_f32(v.x) * v.y;
-        const float y1 = silu_f32(v.z) * v.w;
-        *(uint32_t*)(a.out + (size_t)m * a.F + (n >> 1)) = pack_bf16x2(y0, y1);
-      }
+      out.store2_at(out.row_off(r), silu_f32(v.x) * v.y, silu_f32(v.z) * v.w);
       return 0.f;
     }
   };
   __device__ __forceinline__ static void apply(AccTile& acc, const Args& a, const GemmProblem& p, int m0, int n0,
                                                const LdsRing& lds) {
     const EpiLane L(m0, n0, lds.tid);
-    Op op{L, a, p.M, p.N, L.col4()};
+    const int n = L.col4();
+    Op op{WaveRowsOutBf16(a.out, L, p.M, a.F, n >> 1, n < p.N)};
     epilogue_rows(acc, lds, L, op);
   }
 };
@@ -1003,22 +1008,15 @@ struct EpiDotRowPartials {
     int nb;
   };
   struct Op {
-    const EpiLane& L;
-    const LdsRing& lds;
-    const Args& a;
-    int M, N, n;
-    bool nok;
-    WaveRowsBf16 hv;
+    WaveRowsBf16 hv;      // h2, this lane's 4 features (rows past M and features past N read zero)
+    WaveRowsOutBf16 dho;  // dh2, same positions (those stores are dropped)
     static constexpr bool kRowStat = true;
     static constexpr bool kColStat = false;
     typedef u32x2_t Pre;
     __device__ __forceinline__ Pre fetch(int r) const { return hv.load4(r); }
     __device__ __forceinline__ float row(int r, const f32x4_t& v, const Pre& hh) {
-      const int m = L.token(r);
-      const bool ok = nok && m < M;
-      const size_t idx = (size_t)m * N + n;
       const float d = (v.x * bf16_lo(hh.x) + v.y * bf16_hi(hh.x)) + (v.z * bf16_lo(hh.y) + v.w * bf16_hi(hh.y));
-      if (ok) store_bf16x4(a.dh2, idx, v.x, v.y, v.z, v.w);
+      dho.store4(r, v.x, v.y, v.z, v.w);
       return sum16(d);
     }
   };
@@ -1026,7 +1024,7 @@ struct EpiDotRowPartials {
                                                const LdsRing& lds) {
     const EpiLane L(m0, n0, lds.tid);
     const int n = L.col4();
-    Op op{L, lds, a, p.M, p.N, n, n < p.N, WaveRowsBf16(a.h2, L, p.M, p.N, n, n < p.N)};
+    Op op{WaveRowsBf16(a.h2, L, p.M, p.N, n, n < p.N), WaveRowsOutBf16(a.dh2, L, p.M, p.N, n, n < p.N)};
     epilogue_rows(acc, lds, L, op);
     store_row_partials(lds, L, a.partials, a.nb, p.M);
   }
