@@ -322,11 +322,6 @@ struct Mainloop {
     }
   }
 
-  __device__ __forceinline__ void issue(const TileSrc& s, char* slot, int kt) const {
-#pragma unroll
-    for (int j = 0; j < kLoadsPerStep; ++j) issue_one(s, slot, kt, j);
-  }
-
   // Opaque, wave-uniform slot base: keeps the compiler from hoisting one address
   // register per (slot, read) out of the loop.
   __device__ __forceinline__ static uint32_t opaque_base(const char* slot) {
