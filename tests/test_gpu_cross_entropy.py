@@ -83,3 +83,26 @@ def test_cross_entropy_large_logits(coda):
     assert np.all(np.isfinite(lse)) and np.max(np.abs(ref["lse"])) > 40
     assert_close("lse", lse, ref["lse"], rel_fro=TIGHT)
     assert_close("loss", loss, ref["loss"], rel_fro=TIGHT)
+
+
+# the merge alone, over widths that take every lane-chain instance (1 .. 32 partials per
+# lane) and the thread-per-row form beyond 512 tiles, with row counts that leave partial
+# 16-row groups; ignored labels on both sides of [0, V)
+@pytest.mark.parametrize("nb", [1, 5, 16, 17, 32, 100, 128, 129, 256, 512, 513, 700])
+def test_lse_merge_widths(coda, nb):
+    import torch
+    rng = np.random.default_rng(nb)
+    V = 256 * nb - 8
+    for M in (1, 37, 1000):
+        log(f"lse merge nb={nb} M={M}")
+        P = (rng.standard_normal((M, nb)) * 3.0).astype(np.float32)
+        labels = rng.integers(-V // 2, V + V // 2, size=M).astype(np.int32)
+        target = rng.standard_normal(M).astype(np.float32)
+        t_target = torch.from_numpy(target.copy()).cuda()
+        loss, lse = coda.coda_lse_reduce(torch.from_numpy(P).cuda(), torch.from_numpy(labels).cuda(), V, t_target)
+        torch.cuda.synchronize()
+        ref_lse = O.logsumexp_rows(P.astype(np.float64))
+        valid = (labels >= 0) & (labels < V)
+        assert_close("lse", lse.cpu().numpy(), ref_lse, rel_fro=2e-6)
+        assert_close("loss", loss.cpu().numpy(), np.where(valid, ref_lse - target, 0.0), rel_fro=2e-6)
+        assert np.array_equal(t_target.cpu().numpy(), np.where(valid, target, np.float32(0)))

@@ -35,6 +35,57 @@ __global__ __launch_bounds__(kLseThreads) void lse_reduce_kernel(const float* __
   }
 }
 
+// The same merge with 16 lanes per row (one DPP row; 4 rows per wave): lane c holds the R
+// partials t = c R .. c R + R - 1. The row maximum is a 16-lane reduction (exact in any
+// order); the sum of exp(t - max) passes from lane to lane in chunk order (a DPP shift by
+// one within the row), so every row is still summed in the order t = 0, 1, ..., nb - 1: the
+// same fp32 operations as one thread per row, bit for bit, with M / 4 waves in flight
+// instead of M / 64 (at 8192 rows x 128 tiles: 35 -> a few microseconds).
+constexpr int kLseMaxR = 32;  // nb <= 16 * 32 = 512 (vocabularies up to 131072)
+
+template <int R>
+__global__ __launch_bounds__(kLseThreads) void lse_chain_kernel(const float* __restrict__ P, const int32_t* labels,
+                                                                int M, int nb, int V, float* __restrict__ target,
+                                                                float* __restrict__ lse, float* __restrict__ loss) {
+  const int lane = threadIdx.x & 63, c = lane & 15;
+  const long long m = ((long long)blockIdx.x * (kLseThreads / 64) + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  const bool ok = m < M;  // lanes of rows past M still take part in the lane exchanges
+  const float ninf = -__builtin_huge_valf();
+  float v[R];
+  float mx = ninf;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int t = c * R + k;
+    v[k] = (ok && t < nb) ? P[m * nb + t] : ninf;
+    mx = fmaxf(mx, v[k]);
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  float run = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float in =
+        __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, run), 0x111, 0xF, 0xF, false));
+    if (c == k) {
+      run = k == 0 ? 0.f : in;  // row_shr:1: lane c receives lane c - 1
+#pragma unroll
+      for (int j = 0; j < R; ++j)
+        if (c * R + j < nb) run += expf(v[j] - mx);
+    }
+  }
+  if (c == 15 && ok) {
+    const float l = mx + logf(run);
+    const int lab = labels[m];
+    lse[m] = l;
+    if (lab >= 0 && lab < V) {
+      loss[m] = l - target[m];
+    } else {
+      loss[m] = 0.f;
+      target[m] = 0.f;
+    }
+  }
+}
+
 int check_ce_outputs(const int32_t* labels, float* target, float* lse, float* loss) {
   CODA_NONNULL(labels);
   CODA_NONNULL(target);
@@ -46,8 +97,25 @@ int check_ce_outputs(const int32_t* labels, float* target, float* lse, float* lo
 
 int launch_lse(const float* P, const int32_t* labels, int M, int nb, int V, float* target, float* lse, float* loss,
                hipStream_t st) {
-  hipLaunchKernelGGL(lse_reduce_kernel, dim3((M + kLseThreads - 1) / kLseThreads), dim3(kLseThreads), 0, st, P,
-                     labels, M, nb, V, target, lse, loss);
+  if (nb > 16 * kLseMaxR) {
+    hipLaunchKernelGGL(lse_reduce_kernel, dim3((M + kLseThreads - 1) / kLseThreads), dim3(kLseThreads), 0, st, P,
+                       labels, M, nb, V, target, lse, loss);
+    return launch_status();
+  }
+  const dim3 grid((unsigned)((M + 4 * (kLseThreads / 64) - 1) / (4 * (kLseThreads / 64))));
+  const int R = (nb + 15) / 16;
+  if (R <= 1)
+    hipLaunchKernelGGL(lse_chain_kernel<1>, grid, dim3(kLseThreads), 0, st, P, labels, M, nb, V, target, lse, loss);
+  else if (R <= 2)
+    hipLaunchKernelGGL(lse_chain_kernel<2>, grid, dim3(kLseThreads), 0, st, P, labels, M, nb, V, target, lse, loss);
+  else if (R <= 4)
+    hipLaunchKernelGGL(lse_chain_kernel<4>, grid, dim3(kLseThreads), 0, st, P, labels, M, nb, V, target, lse, loss);
+  else if (R <= 8)
+    hipLaunchKernelGGL(lse_chain_kernel<8>, grid, dim3(kLseThreads), 0, st, P, labels, M, nb, V, target, lse, loss);
+  else if (R <= 16)
+    hipLaunchKernelGGL(lse_chain_kernel<16>, grid, dim3(kLseThreads), 0, st, P, labels, M, nb, V, target, lse, loss);
+  else
+    hipLaunchKernelGGL(lse_chain_kernel<32>, grid, dim3(kLseThreads), 0, st, P, labels, M, nb, V, target, lse, loss);
   return launch_status();
 }
 
