@@ -155,3 +155,19 @@ def test_rmsnorm_bwd_empty_batch(coda):
     sync()
     assert part.shape == (0, D) and dh1.shape == (0, D) and s.shape == (0,)
     assert bool((dg == 0).all())
+
+
+# the column reduction keeps the order t = 0, 1, ..., tiles-1 (loads batched 16 at a time,
+# adds in order): bit for bit a sequential fp32 sum, across batch boundaries and the tail
+@pytest.mark.parametrize("tiles", [0, 1, 15, 16, 17, 33, 100])
+def test_colsum_reduce_sum_order_is_sequential(coda, tiles):
+    import torch
+    rng = np.random.default_rng(100 + tiles)
+    for width in (8, 1000, 4096):
+        P = (rng.standard_normal((tiles, width)) * np.exp(rng.uniform(-8, 8, (tiles, 1)))).astype(np.float32)
+        got = coda.coda_colsum_reduce(torch.from_numpy(P).cuda())
+        sync()
+        ref = np.zeros(width, dtype=np.float32)
+        for t in range(tiles):
+            ref = ref + P[t]  # fp32 adds in order
+        assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.view(np.uint32))

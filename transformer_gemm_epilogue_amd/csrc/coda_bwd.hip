@@ -39,12 +39,22 @@ __global__ __launch_bounds__(64 * kRdWaves) void rowdot_stat_kernel(const uint16
 }
 
 // out[n] = sum_t P[t, n] in the order t = 0, 1, ..., tiles-1 (one thread per column).
+// The loads go out 16 at a time and are then added in order: a few memory round trips per
+// column instead of one per tile (the width, not the tile count, sets the parallelism).
 __global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* __restrict__ P, int tiles, int width,
                                                             float* __restrict__ out) {
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= width) return;
   float acc = 0.f;
-  for (int t = 0; t < tiles; ++t) acc += P[(size_t)t * width + n];
+  int t = 0;
+  for (; t + 16 <= tiles; t += 16) {
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = P[(size_t)(t + k) * width + n];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc += v[k];
+  }
+  for (; t < tiles; ++t) acc += P[(size_t)t * width + n];
   out[n] = acc;
 }
 
