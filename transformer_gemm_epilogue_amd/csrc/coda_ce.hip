@@ -61,6 +61,9 @@ __global__ __launch_bounds__(kLseThreads) void lse_chain_kernel(const float* __r
   }
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  float e[R];  // every lane's exponentials at once; only the in-order adds run lane by lane
+#pragma unroll
+  for (int j = 0; j < R; ++j) e[j] = expf(v[j] - mx);
   float run = 0.f;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(kLseThreads) void lse_chain_kernel(const float* __r
       run = k == 0 ? 0.f : in;  // row_shr:1: lane c receives lane c - 1
 #pragma unroll
       for (int j = 0; j < R; ++j)
-        if (c * R + j < nb) run += expf(v[j] - mx);
+        if (c * R + j < nb) run += e[j];
     }
   }
   if (c == 15 && ok) {
