@@ -452,6 +452,9 @@ __device__ __forceinline__ void mainloop_body(const Mainloop<kWKN>& ml, const Ti
     constexpr bool kOdd = decltype(parity)::value;
 #pragma unroll
     for (int j = kH; j < kMJ; ++j) b[j] = ml.read_x(lds.slot[S], j);
+    // two waves share each SIMD: the one in its first-half MFMA run (and W issue) wins
+    // issue arbitration over the other's reads and waits
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < kNI; ++i)
 #pragma unroll
@@ -461,6 +464,7 @@ __device__ __forceinline__ void mainloop_body(const Mainloop<kWKN>& ml, const Ti
     // W half of step kt+3 into the slot of kt-2 (free since the previous barrier)
     issue_at(lds.slot[(S + 3) % kStages], kt + 3, 2, kind);
     issue_at(lds.slot[(S + 3) % kStages], kt + 3, 3, kind);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kOdd)
       wait_vmcnt<5>();  // this thread's loads of step kt+1 have landed
