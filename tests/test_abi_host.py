@@ -51,6 +51,14 @@ def test_binding_covers_every_declared_symbol():
     assert declared == set(coda.SIGNATURES)
 
 
+def test_binding_exports_every_public_wrapper():
+    # every public wrapper of an entry point is listed for `from ... import *`
+    import inspect
+    public = {n for n, f in inspect.getmembers(coda, inspect.isfunction)
+              if f.__module__ == coda.__name__ and not n.startswith("_")}
+    assert public <= set(coda.__all__), sorted(public - set(coda.__all__))
+
+
 def test_status_strings(L):
     for st in range(7):
         assert L.coda_status_string(st)

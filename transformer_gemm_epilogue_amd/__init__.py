@@ -31,12 +31,22 @@ __all__ = [
     "coda_gemm_rope_persistent",
     "coda_gemm_swiglu",
     "coda_gemm_rmsnorm_bwd_stats",
+    "num_row_tiles",
+    "coda_rowdot_stat",
+    "coda_gemm_rmsnorm_bwd_dx",
+    "coda_colsum_reduce",
+    "coda_rmsnorm_bwd",
+    "coda_gemm_rope_bwd",
+    "coda_gemm_swiglu_bwd",
+    "coda_gemm_cross_entropy",
+    "coda_lse_reduce",
     "coda_baseline_gemm",
     "coda_baseline_residual_rmsnorm",
     "coda_baseline_rope",
     "coda_baseline_swiglu",
     "coda_baseline_rowdot",
     "coda_baseline_copy",
+    "coda_baseline_mfma_loop",
 ]
 
 PARTIAL_TILE_N = 256
