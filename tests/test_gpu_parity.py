@@ -66,6 +66,32 @@ def test_fwd_small_full_compare(coda, shape):
     check_fwd(got, ref)
 
 
+def test_fwd_degenerate_rows(coda):
+    """Rows whose residual-stream value h1 is exactly zero (x and z zero) have a zero mean
+    square, so r = 1/sqrt(eps) and every output of the row is exactly zero; a row with x
+    zero and z constant c has h1 = c, r = 1/sqrt(c^2 + eps) in closed form and h2 = c gamma
+    exactly (c a power of two). Zero rows sit at tile edges and in the ragged last tile."""
+    M, K, D, N1 = 300, 64, 512, 264
+    base = W.gemm_rmsnorm_fwd_inputs(77, M, K, D, N1, 1e-5)
+    wl = {k: base[k].copy() for k in ("x", "w0", "z", "gamma", "w1")}
+    wl["eps"] = base["eps"]
+    zero_rows, const_row = [0, 5, 255, 256, M - 1], 130
+    for m in zero_rows + [const_row]:
+        wl["x"][m] = 0
+        wl["z"][m] = 0
+    wl["z"][const_row] = 0x4000  # bf16 bits of 2.0
+    got = run_fwd(coda, wl)
+    ref = O.gemm_rmsnorm_fwd(wl["x"], wl["w0"], wl["z"], wl["gamma"], wl["w1"], wl["eps"])
+    check_fwd(got, ref)
+    h1, h2, part, r, y = (dec(got[0]), dec(got[1]), got[2].cpu().numpy(), got[3].cpu().numpy(), dec(got[4]))
+    for m in zero_rows:
+        assert not h1[m].any() and not h2[m].any() and not part[m].any() and not y[m].any(), m
+        assert abs(r[m] * np.sqrt(wl["eps"]) - 1.0) <= 1e-6, (m, r[m])
+    assert np.all(h1[const_row] == 2.0)
+    assert np.array_equal(h2[const_row], 2.0 * O.decode_bf16(wl["gamma"]))
+    assert abs(r[const_row] * np.sqrt(4.0 + wl["eps"]) - 1.0) <= 1e-6, r[const_row]
+
+
 def test_fwd_llama_full_size_sampled(coda):
     wl = W.llama_fwd()
     log(f"fwd {wl.name}")
