@@ -122,3 +122,24 @@ def test_rope_bwd_rotation_properties(coda):
         n_ref = plain[:, 0::2] ** 2 + plain[:, 1::2] ** 2
         assert np.allclose(n_out, n_ref, rtol=2e-2, atol=1e-4)
     assert not np.allclose(fwd, bwd, atol=1e-3)
+
+
+def test_rope_position_zero_is_identity(coda):
+    """At position 0 every pair's angle is zero (the table holds cos 1 and sin 0 exactly),
+    so those rows of the fused output, forward and backward, equal the plain-store GEMM of
+    the same main loop bit for bit; the V block passes through unrotated at every row."""
+    c = coda
+    wl = W.rope_qkv(seed=21, M=600, K=128, n_q=256, n_k=128, n_v=128, head_dim=64, seq_len=256, pos_offset=0)
+    cos_t, sin_t = c.coda_rope_tables(wl["seq_len"], wl["head_dim"], wl["theta"])
+    assert np.all(cos_t[0].cpu().numpy() == 1.0) and np.all(sin_t[0].cpu().numpy() == 0.0)
+    x, w = to_dev_bf16(wl["x"]), to_dev_bf16(wl["w"])
+    args = (wl["n_q"], wl["n_k"], wl["n_v"], wl["head_dim"], wl["seq_len"], wl["pos_offset"])
+    fwd = bf16_bits(c.coda_gemm_rope(x, w, cos_t, sin_t, *args))
+    bwd = bf16_bits(c.coda_gemm_rope_bwd(x, w, cos_t, sin_t, *args))
+    plain = bf16_bits(c.coda_baseline_gemm(x, w))
+    rows = [0, 256, 512]  # (m + pos_offset) mod seq_len == 0, one in the ragged last row tile
+    qk = wl["n_q"] + wl["n_k"]
+    for out in (fwd, bwd):
+        assert np.array_equal(out[rows], plain[rows])
+        assert np.array_equal(out[:, qk:], plain[:, qk:])
+        assert not np.array_equal(out[1:256, :qk], plain[1:256, :qk])  # other positions do rotate
