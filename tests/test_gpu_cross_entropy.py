@@ -106,3 +106,26 @@ def test_lse_merge_widths(coda, nb):
         assert_close("lse", lse.cpu().numpy(), ref_lse, rel_fro=2e-6)
         assert_close("loss", loss.cpu().numpy(), np.where(valid, ref_lse - target, 0.0), rel_fro=2e-6)
         assert np.array_equal(t_target.cpu().numpy(), np.where(valid, target, np.float32(0)))
+
+
+def test_cross_entropy_zero_rows_closed_form(coda):
+    """A row of x that is zero makes every logit of the row zero, so lse = log V, the label
+    logit is 0 and the loss is log V (an ignored label: loss 0); the other rows match the
+    oracle. Zero rows sit on a row-tile edge and in the ragged last tile; V spans a ragged
+    last column tile."""
+    M, K, V = 300, 64, 1000
+    wl = W.cross_entropy(seed=91, M=M, K=K, V=V, ignore_every=0)
+    x, labels = wl["x"].copy(), wl["labels"].copy()
+    zero_rows = [0, 255, 256, M - 1]
+    x[zero_rows] = 0
+    labels[M - 1] = -1  # ignored
+    loss, lse, target, _ = run(coda, dict(x=x, w=wl["w"], labels=labels))
+    ref = O.gemm_cross_entropy(x, wl["w"], labels)
+    assert_close("lse", lse, ref["lse"], rel_fro=TIGHT)
+    assert_close("loss", loss, ref["loss"], rel_fro=TIGHT)
+    for m in zero_rows:
+        assert abs(lse[m] - np.log(V)) <= 1e-6 * np.log(V), (m, lse[m])
+        assert target[m] == 0.0
+    for m in zero_rows[:-1]:
+        assert abs(loss[m] - np.log(V)) <= 1e-6 * np.log(V), (m, loss[m])
+    assert loss[M - 1] == 0.0

@@ -252,6 +252,23 @@ def test_swiglu_small_full_compare(coda, shape):
     assert_close("swiglu", dec(out), O.gemm_swiglu(wl["x"], wl["w"]))
 
 
+def test_swiglu_zero_gate_or_up_columns(coda):
+    """A gate column of W that is zero gives G = 0 and silu(0) = 0; an up column that is
+    zero gives U = 0: either way the output feature is exactly zero for every row. The
+    features sit at both edges of an output tile (128 features per 256-column GEMM tile)
+    and in the ragged last one; the rest matches the oracle."""
+    M, K, F = 333, 136, 200
+    wl = W.swiglu(seed=13, M=M, K=K, F=F)
+    w = wl["w"].copy()
+    gate_zero, up_zero = [0, 127, 128, F - 1], [5, 130]
+    w[:, [2 * j for j in gate_zero]] = 0
+    w[:, [2 * j + 1 for j in up_zero]] = 0
+    out = dec(coda.coda_gemm_swiglu(to_dev_bf16(wl["x"]), to_dev_bf16(w)))
+    sync()
+    assert_close("swiglu", out, O.gemm_swiglu(wl["x"], w))
+    assert not out[:, gate_zero + up_zero].any()
+
+
 def test_swiglu_full_size_sampled(coda):
     wl = W.swiglu()
     log(f"swiglu {wl.name}")

@@ -87,6 +87,32 @@ def test_rmsnorm_bwd_small_full_compare(coda, shape, with_gres):
     assert_close("dgamma", dgamma.cpu().numpy(), ref["dgamma"], rel_fro=TIGHT)
 
 
+def test_rmsnorm_bwd_zero_gradient_rows(coda):
+    """Rows of dY that are zero: both forms of the row statistic (output side, and dH2 . h2
+    from the grad GEMM's epilogue) are exactly zero, the dH2 row is zero, and dh1 reduces to
+    the residual-stream gradient g_res exactly (every other term of the epilogue is an exact
+    zero). Zero rows on a row-tile edge and in the ragged last tile; the rest matches the
+    oracle."""
+    import torch
+    base = W.rmsnorm_bwd_full(31, 300, 256, 264)
+    wl = {k: base[k].copy() for k in ("h1", "gamma", "w1", "dy", "g_res")}
+    wl["eps"] = base["eps"]
+    rows = [0, 255, 256, 299]
+    wl["dy"][rows] = 0
+    dev, r, y = gpu_inputs(coda, wl)
+    s, dh1, part, dgamma = run(coda, dev, r, y)
+    ref = oracle(wl)
+    assert_close("dh1", dec(dh1), ref["dh1"])
+    assert_close("dgamma", dgamma.cpu().numpy(), ref["dgamma"], rel_fro=TIGHT)
+    assert np.all(s.cpu().numpy()[rows] == 0.0)
+    assert np.array_equal(dec(dh1)[rows], O.decode_bf16(wl["g_res"])[rows])
+    h2 = (dev["h1"].float() * dev["gamma"].float()).to(torch.bfloat16).contiguous()
+    dh2, p2, s2 = coda.coda_gemm_rmsnorm_bwd_stats(dev["dy"], dev["w1"], h2)
+    sync()
+    assert not dec(dh2)[rows].any() and not p2.cpu().numpy()[rows].any()
+    assert np.all(s2.cpu().numpy()[rows] == 0.0)
+
+
 def test_rmsnorm_bwd_full_size_sampled(coda):
     wl = W.rmsnorm_bwd_full()
     log(f"rmsnorm_bwd {wl.name}")
