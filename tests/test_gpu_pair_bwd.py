@@ -47,6 +47,25 @@ def test_swiglu_bwd_small_full_compare(coda, shape):
     assert_close("dU", got[:, 1::2], ref[:, 1::2])
 
 
+def test_swiglu_bwd_zero_rows_and_gates(coda):
+    """Zero rows of dY give exactly zero gradient rows; a saved gate G = 0 has silu(G) = 0,
+    so the up-gradient dU = dOut silu(G) of that feature is exactly zero in every row (and
+    dG = dOut U / 2 is the oracle's). Zero rows on a row-tile edge and in the ragged last
+    tile; zero gates at both ends of the ragged feature tile and inside it."""
+    M, Dm, F = 333, 200, 136
+    wl0 = W.swiglu_bwd(seed=78, M=M, Dm=Dm, F=F)
+    wl = {k: wl0[k].copy() for k in ("dy", "w_down", "h")}
+    zero_rows, zero_gates = [0, 255, 256, M - 1], [0, 127, 128, F - 1]
+    wl["dy"][zero_rows] = 0
+    wl["h"][:, [2 * j for j in zero_gates]] = 0
+    got = run_swiglu_bwd(coda, wl)
+    ref = O.gemm_swiglu_bwd(wl["dy"], wl["w_down"], wl["h"])["dh"]
+    assert_close("dG", got[:, 0::2], ref[:, 0::2])
+    assert_close("dU", got[:, 1::2], ref[:, 1::2])
+    assert not got[zero_rows].any()
+    assert not got[:, [2 * j + 1 for j in zero_gates]].any()
+
+
 def test_swiglu_bwd_saturated_gates(coda):
     # gates far into both tails of the logistic (|G| up to ~40): finite, and still the oracle's values
     wl = W.swiglu_bwd(seed=77, M=300, Dm=64, F=128)
