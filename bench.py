@@ -9,7 +9,9 @@ inputs with fp32 accumulation, synthetic seeded data already resident in HBM.
 
 Prints ONE JSON line. `value` is the algorithmic TFLOP/s of the step (2MKD + 2MDN1 per
 step) over the synchronize-bracketed wall time of `--steps` steps. Per-kernel durations
-come from HIP events recorded on the stream the kernels run on. The other fused paths
+come from HIP events recorded on the stream the kernels run on: GEMM1's (the roofline
+kernel's) in every timed step, the other two kernels' in as many steps after the timed
+ones, so the timed steps carry no events between the row reduction and GEMM2. The other fused paths
 (GEMM+RoPE at 4096 and 8192 under both schedules, GEMM+SwiGLU, the backward statistic,
 the rest of the RMSNorm backward, the SwiGLU and RoPE backward maps, GEMM+cross-entropy)
 and the unfused baselines are timed after the headline and reported under "paths"
@@ -116,17 +118,19 @@ def headline(args, coda, torch):
     r = torch.empty((M,), dtype=torch.float32, device="cuda")
     y = torch.empty((M, N1), dtype=torch.bfloat16, device="cuda")
 
-    def step(ev=None):
+    def step(ev=None, each=False):
+        # ev[0], ev[1] bracket GEMM1 (the roofline kernel); with `each`, ev[2] and ev[3]
+        # also close the row reduction and GEMM2
         if ev is not None:
             ev[0].record()
         coda.coda_gemm_residual_rmsnorm_partials(x, w0, z, g, h1=h1, h2=h2, partials=part)
         if ev is not None:
             ev[1].record()
         coda.coda_rowstat_reduce(part, D, eps, coda.ROWSTAT_RSQRT_MEAN_EPS, out=r)
-        if ev is not None:
+        if each:
             ev[2].record()
         coda.coda_gemm_rowscale(h2, w1, r, y=y)
-        if ev is not None:
+        if each:
             ev[3].record()
 
     # Clock settle: the MI355X ramps its clocks over the first tens of milliseconds of
@@ -138,7 +142,8 @@ def headline(args, coda, torch):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # the timed steps carry only GEMM1's two events (the roofline's launch duration)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e in evs:
@@ -146,8 +151,14 @@ def headline(args, coda, torch):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     g1 = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    rs = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    g2 = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    # the row reduction and GEMM2, timed in as many further steps with events between
+    # all three kernels
+    evs_each = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evs_each:
+        step(e, each=True)
+    torch.cuda.synchronize()
+    rs = np.array([e[1].elapsed_time(e[2]) for e in evs_each])
+    g2 = np.array([e[2].elapsed_time(e[3]) for e in evs_each])
 
     # the single fused entry point (same three launches), for cross-checking
     fused = time_reps(lambda: coda.coda_gemm_rmsnorm_fwd(x, w0, z, g, w1, eps, h1=h1, h2=h2, partials=part,
