@@ -320,6 +320,29 @@ def test_bwd_full_size_sampled(coda):
 
 
 # ------------------------------------------------------------------- exact integer results
+def test_kn_large_weight_takes_per_step_descriptors(coda):
+    """A KN weight with (K + 32) N >= 2^30 elements (2.1 GB here) is loaded through one W
+    descriptor per depth step (one descriptor over the whole depth would need offsets past
+    2^31). Ragged last depth step (K mod 32 = 8) and ragged last column tile (N mod 256 =
+    8); sampled rows and columns against the oracle. The weight is drawn on the GPU from a
+    seeded generator and only the sampled columns are brought to the host."""
+    import torch
+    M, K, N = 300, 32776, 32776
+    assert (K + 32) * N >= 1 << 30
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    x = (torch.randn((M, K), generator=gen, device="cuda")).to(torch.bfloat16)
+    w = (torch.randn((K, N), generator=gen, device="cuda") * K ** -0.5).to(torch.bfloat16)
+    out = dec(coda.coda_baseline_gemm(x, w))
+    sync()
+    assert np.all(np.isfinite(out))
+    rows = np.array([0, 1, 255, 256, M - 1])
+    cols = np.array([0, 1, 255, 256, 16384, N - 9, N - 8, N - 1])
+    ref = O.matmul(O.decode_bf16(bf16_bits(x[torch.from_numpy(rows).cuda()])),
+                   O.decode_bf16(bf16_bits(w[:, torch.from_numpy(cols).cuda()])))
+    assert_close("sampled", out[np.ix_(rows, cols)], ref)
+    del w
+
+
 def test_integer_inputs_are_bit_exact(coda):
     """Small integers (|v| <= 2, K <= 256) make every product and fp32 partial sum exact,
     so the bf16 outputs must equal the round-to-nearest-even of the exact result."""

@@ -155,8 +155,12 @@ int coda_gemm_cross_entropy(const uint16_t* x, const uint16_t* w, const int32_t*
   const hipStream_t st = as_stream(stream);
   const GemmProblem p{x, w, M, V, K};
   const EpiCrossEntropy::Args ea{labels, tile_lse, target, nb};
-  hipLaunchKernelGGL((gemm_epilogue_kernel<true, EpiCrossEntropy>), dim3(gemm_grid(M, V)), dim3(kThreads), 0, st, p,
-                     ea);
+  if (kn_one_descriptor_fits(K, V))
+    hipLaunchKernelGGL((gemm_epilogue_kernel<true, EpiCrossEntropy, true>), dim3(gemm_grid(M, V)), dim3(kThreads), 0,
+                       st, p, ea);
+  else
+    hipLaunchKernelGGL((gemm_epilogue_kernel<true, EpiCrossEntropy>), dim3(gemm_grid(M, V)), dim3(kThreads), 0, st,
+                       p, ea);
   CODA_TRY(launch_status());
   return launch_lse(tile_lse, labels, M, nb, V, target, lse, loss, st);
 }

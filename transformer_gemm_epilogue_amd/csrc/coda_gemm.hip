@@ -12,6 +12,12 @@ namespace {
 template <bool kWKN, class Epi>
 int launch_gemm(const GemmProblem& p, const typename Epi::Args& ea, hipStream_t stream) {
   const int grid = gemm_grid(p.M, p.N);
+  if constexpr (kWKN) {
+    if (kn_one_descriptor_fits(p.K, p.N)) {
+      hipLaunchKernelGGL((gemm_epilogue_kernel<true, Epi, true>), dim3(grid), dim3(kThreads), 0, stream, p, ea);
+      return launch_status();
+    }
+  }
   hipLaunchKernelGGL((gemm_epilogue_kernel<kWKN, Epi>), dim3(grid), dim3(kThreads), 0, stream, p, ea);
   return launch_status();
 }

@@ -203,18 +203,33 @@ __device__ __forceinline__ void wait_vmcnt() {
 typedef __attribute__((address_space(3))) const bf16x8_t* lds_b128_ptr;
 typedef __attribute__((address_space(3))) i16x4_t* lds_tr_ptr;
 
-// DMA sources of one output tile: descriptors of its X rows and (NK) W rows, which of
-// this lane's KN-W chunks lie inside the width, and the tile's rotated first depth step.
+// DMA sources of one output tile: descriptors of its X rows and of W (NK: the tile's W
+// rows; KN, one-descriptor form: the tile's W columns over the whole depth; unused by the
+// per-step KN form), which of this lane's KN-W chunks lie inside the width, and the
+// tile's rotated first depth step.
 struct TileSrc {
-  i32x4_t xrs, wrs_nk;
+  i32x4_t xrs, wrs;
   int n0, kstart;
   bool w_col_ok[kXJ];
 };
 
 typedef f32x4_t AccTile[kNI][kMJ];
 
-template <bool kWKN>
+// KN-W loads come in two forms. With kWOneDesc, one descriptor per tile covers W's
+// columns n0.. over the whole depth and a load's depth offset goes into its per-lane
+// offset; rows past K lie outside the descriptor's range and read as zeros. That needs
+// every such offset below 2^31, (K + kBK) N < 2^30 elements. Otherwise each depth step
+// builds a descriptor of its own 32 rows (a 64-bit base computed per step: about 15 more
+// scalar instructions per step; the one-descriptor form measured 1.5-2.3% faster on the
+// 8192-class shapes, bit-identical).
+__host__ __device__ constexpr bool kn_one_descriptor_fits(int K, int N) {
+  return ((long long)K + kBK) * (long long)N < (1ll << 30);
+}
+
+template <bool kWKN, bool kWOneDesc = false>
 struct Mainloop {
+  static constexpr bool kKN = kWKN;
+  static_assert(kWKN || !kWOneDesc, "the one-descriptor form is for the KN layout");
   uint32_t wave_u;        // wave index, wave-uniform
   uint32_t x_off[kXJ];    // byte offsets of this lane's X chunks (depth 0 of the tile)
   uint32_t x_kchunk[kXJ]; // logical depth chunk (0..3) of each X load
@@ -289,7 +304,10 @@ struct Mainloop {
     TileSrc s;
     const uint32_t kb = (uint32_t)K * 2u;
     s.xrs = rsrc_words(xbase + (size_t)m0 * K, (uint32_t)min(kBM, M - m0) * kb);
-    s.wrs_nk = kWKN ? rsrc_words(wbase, 0u) : rsrc_words(wbase + (size_t)n0 * K, (uint32_t)min(kBN, N - n0) * kb);
+    if constexpr (kWOneDesc)
+      s.wrs = rsrc_words(wbase + n0, ((uint32_t)K * (uint32_t)N - (uint32_t)n0) * 2u);
+    else
+      s.wrs = kWKN ? rsrc_words(wbase, 0u) : rsrc_words(wbase + (size_t)n0 * K, (uint32_t)min(kBN, N - n0) * kb);
     s.n0 = n0;
     s.kstart = k_rotation(t, KT);
 #pragma unroll
@@ -310,14 +328,16 @@ struct Mainloop {
     } else {
       const int jj = j - kXJ;
       const uint32_t ws = lds_addr(slot) + (uint32_t)kTileBytes + wave_u * (kXJ * 1024u);
-      if constexpr (kWKN) {
+      if constexpr (kWOneDesc) {
+        dma16(s.wrs, ws + jj * 1024u, s.w_col_ok[jj] ? (uint32_t)k0 * (uint32_t)N * 2u + w_off[jj] : kOutOfRange);
+      } else if constexpr (kWKN) {
         const int krows = max(0, min(kBK, K - k0));
         const i32x4_t wrs = rsrc_words(wbase + (size_t)min(k0, K - 1) * N + s.n0,
                                        krows ? ((uint32_t)krows * (uint32_t)N - (uint32_t)s.n0) * 2u : 0u);
         dma16(wrs, ws + jj * 1024u, s.w_col_ok[jj] ? w_off[jj] : kOutOfRange);
       } else {
         const bool ok = k0 + 8 * (int)w_kchunk[jj] < K;
-        dma16(s.wrs_nk, ws + jj * 1024u, ok ? w_off[jj] + (uint32_t)k0 * 2u : kOutOfRange);
+        dma16(s.wrs, ws + jj * 1024u, ok ? w_off[jj] + (uint32_t)k0 * 2u : kOutOfRange);
       }
     }
   }
@@ -354,10 +374,10 @@ __device__ __forceinline__ TileSrc pick(bool second, const TileSrc& a, const Til
   s.xrs.y = second ? b.xrs.y : a.xrs.y;
   s.xrs.z = second ? b.xrs.z : a.xrs.z;
   s.xrs.w = second ? b.xrs.w : a.xrs.w;
-  s.wrs_nk.x = second ? b.wrs_nk.x : a.wrs_nk.x;
-  s.wrs_nk.y = second ? b.wrs_nk.y : a.wrs_nk.y;
-  s.wrs_nk.z = second ? b.wrs_nk.z : a.wrs_nk.z;
-  s.wrs_nk.w = second ? b.wrs_nk.w : a.wrs_nk.w;
+  s.wrs.x = second ? b.wrs.x : a.wrs.x;
+  s.wrs.y = second ? b.wrs.y : a.wrs.y;
+  s.wrs.z = second ? b.wrs.z : a.wrs.z;
+  s.wrs.w = second ? b.wrs.w : a.wrs.w;
   s.n0 = second ? b.n0 : a.n0;
   s.kstart = second ? b.kstart : a.kstart;
 #pragma unroll
@@ -366,8 +386,8 @@ __device__ __forceinline__ TileSrc pick(bool second, const TileSrc& a, const Til
 }
 
 // X loads of depth steps kk (into slot a) and kk + 1 (slot b), row halves back to back.
-template <bool kWKN>
-__device__ __forceinline__ void issue_x_pair(const Mainloop<kWKN>& ml, const TileSrc& src, char* a, char* b, int kk) {
+template <class ML>
+__device__ __forceinline__ void issue_x_pair(const ML& ml, const TileSrc& src, char* a, char* b, int kk) {
   ml.issue_one(src, a, kk, 0);
   ml.issue_one(src, b, kk + 1, 0);
   ml.issue_one(src, a, kk, 1);
@@ -377,8 +397,8 @@ __device__ __forceinline__ void issue_x_pair(const Mainloop<kWKN>& ml, const Til
 // Prologue: the loads the schedule would issue in its steps -3, -2, -1 (W of 0; X of 0
 // and 1; W of 1; W of 2; X of 2 and 3), so that the loop's wait counts hold from step 0
 // on; wait for step 0.
-template <bool kWKN>
-__device__ __forceinline__ void mainloop_prologue(const Mainloop<kWKN>& ml, const TileSrc& src, const LdsRing& lds) {
+template <class ML>
+__device__ __forceinline__ void mainloop_prologue(const ML& ml, const TileSrc& src, const LdsRing& lds) {
   ml.issue_one(src, lds.slot[0], 0, 2);
   ml.issue_one(src, lds.slot[0], 0, 3);
   issue_x_pair(ml, src, lds.slot[0], lds.slot[1], 0);
@@ -398,8 +418,8 @@ constexpr int kNextSteps = 2;
 
 // Start of a persistent workgroup's next tile, after its epilogue and a barrier: steps
 // 0 and 1 are already in LDS; put the loads of step -1 (W of 2; X of 2 and 3) in flight.
-template <bool kWKN>
-__device__ __forceinline__ void mainloop_resume(const Mainloop<kWKN>& ml, const TileSrc& src, const LdsRing& lds) {
+template <class ML>
+__device__ __forceinline__ void mainloop_resume(const ML& ml, const TileSrc& src, const LdsRing& lds) {
   ml.issue_one(src, lds.slot[2], 2, 2);
   ml.issue_one(src, lds.slot[2], 2, 3);
   issue_x_pair(ml, src, lds.slot[2], lds.slot[3], 2);
@@ -410,9 +430,10 @@ __device__ __forceinline__ void mainloop_resume(const Mainloop<kWKN>& ml, const 
 // (this needs KT >= 4, so that all of them fall inside this loop); otherwise loads past
 // the end zero-fill free slots. Returns once every load has landed and every wave is
 // done reading operands.
-template <bool kWKN, bool kPersist>
-__device__ __forceinline__ void mainloop_body(const Mainloop<kWKN>& ml, const TileSrc& cur, const TileSrc& nxt,
+template <bool kPersist, class ML>
+__device__ __forceinline__ void mainloop_body(const ML& ml, const TileSrc& cur, const TileSrc& nxt,
                                               bool has_next, const LdsRing& lds, AccTile& acc) {
+  constexpr bool kWKN = ML::kKN;
 #pragma unroll
   for (int i = 0; i < kNI; ++i)
 #pragma unroll
@@ -1031,8 +1052,9 @@ struct EpiDotRowPartials {
 
 __host__ __device__ inline int gemm_grid(int M, int N) { return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN); }
 
-// One workgroup per output tile.
-template <bool kWKN, class Epi>
+// One workgroup per output tile. kWOneDesc (KN only): the one-descriptor form of the
+// W loads, for shapes where kn_one_descriptor_fits.
+template <bool kWKN, class Epi, bool kWOneDesc = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void gemm_epilogue_kernel(GemmProblem p, typename Epi::Args ea) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kSlotBytes];
@@ -1040,12 +1062,12 @@ void gemm_epilogue_kernel(GemmProblem p, typename Epi::Args ea) {
   const int t = blockIdx.x;
   int m0, n0;
   tile_coords(p.M, p.N, p.K, p.group_m, t, m0, n0);
-  Mainloop<kWKN> ml;
+  Mainloop<kWKN, kWOneDesc> ml;
   ml.init(p, threadIdx.x);
   const TileSrc src = ml.src(t, m0, n0);
   AccTile acc;
   mainloop_prologue(ml, src, lds);
-  mainloop_body<kWKN, false>(ml, src, src, false, lds, acc);
+  mainloop_body<false>(ml, src, src, false, lds, acc);
   Epi::apply(acc, ea, p, m0, n0, lds);
 }
 
@@ -1054,7 +1076,9 @@ void gemm_epilogue_kernel(GemmProblem p, typename Epi::Args ea) {
 // above). The DMA ring runs on across tiles: the last steps of a tile load the first
 // two depth steps of the next, whose latency the epilogue then covers, and no
 // workgroup launch separates the tiles. Needs K / 32 >= 4. Results are bit-identical
-// to the one-workgroup-per-tile form (same tile sums in the same order).
+// to the one-workgroup-per-tile form (same tile sums in the same order). It keeps the
+// per-step KN-W descriptors: with the one-descriptor form its loop needs more than the
+// 256 registers of two waves per SIMD and spills.
 template <bool kWKN, class Epi>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void gemm_persistent_kernel(GemmProblem p, typename Epi::Args ea) {
@@ -1100,7 +1124,7 @@ void gemm_persistent_kernel(GemmProblem p, typename Epi::Args ea) {
     e = e >= kStages ? e - kStages : e;
     const LdsRing lds = make_ring(smem, rot, e, tid);
     AccTile acc;
-    mainloop_body<kWKN, true>(ml, cur, nxt, has_next, lds, acc);
+    mainloop_body<true>(ml, cur, nxt, has_next, lds, acc);
     Epi::apply(acc, ea, p, m0, n0, lds);
     if (!has_next) break;
     t = tn;
