@@ -21,6 +21,9 @@
  *   - Ownership: the caller owns and allocates every buffer, workspaces included. The
  *     library allocates no device memory, keeps no state between calls and may be
  *     called from several host threads at once (on different buffers).
+ *   - Aliasing: an output buffer may overlap neither an input nor another output
+ *     (byte ranges of the sizes the call implies); such a call returns CODA_ERR_ARG.
+ *     Inputs are only read and may alias each other.
  *   - Errors: argument errors are detected before anything is enqueued and return a
  *     nonzero status (nothing is written). A failed kernel launch returns
  *     CODA_ERR_HIP. Faults during execution surface at the caller's next
@@ -47,9 +50,9 @@ extern "C" {
 #define CODA_ERR_NULL 1      /* a required pointer is NULL */
 #define CODA_ERR_SHAPE 2     /* a size violates the shape rules above */
 #define CODA_ERR_ALIGN 3     /* a bf16 pointer is not 16-byte aligned (fp32: 8-byte) */
-#define CODA_ERR_WORKSPACE 4 /* a workspace size argument is too small */
+#define CODA_ERR_WORKSPACE 4 /* the workspace a call needs exceeds what it has */
 #define CODA_ERR_HIP 5       /* a HIP launch failed */
-#define CODA_ERR_ARG 6       /* another argument is invalid (mode, eps, theta, ...) */
+#define CODA_ERR_ARG 6       /* another argument is invalid (mode, eps, theta, overlap) */
 
 /* Width of one column tile of the row-partial workspace: partial t of a row covers
  * output columns [t*256, (t+1)*256) (the last tile may be ragged). */
@@ -88,7 +91,7 @@ int coda_rowstat_num_partials(int width, int* nb);
  *   h1 [M,D], h2 [M,D]: bf16 outputs (h2 is also GEMM2's input).
  *   partials [M, nb] fp32 workspace/output, nb = coda_rowstat_num_partials(D).
  *   r [M] fp32 output.  y [M,N1] bf16 output.
- * Output buffers must not overlap inputs or each other.
+ * Output buffers must not overlap inputs or each other (CODA_ERR_ARG).
  * ------------------------------------------------------------------------------- */
 int coda_gemm_rmsnorm_fwd(const uint16_t* x, const uint16_t* w0, const uint16_t* z,
                           const uint16_t* gamma, const uint16_t* w1, int M, int K, int D,

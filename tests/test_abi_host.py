@@ -27,11 +27,36 @@ def header_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(coda_\w+)\s*\(", text, flags=re.M)))
 
 
+SPREAD = 1 << 36  # every fake buffer gets a region of its own this large
+
+
+class Spread:
+    """The library, called with each fake pointer argument (P + a small offset) moved to
+    a region of its own: argument i at P + i * 2^36, offset kept. No two fake buffers
+    then overlap, so the overlap rule stays out of the way of the check under test."""
+
+    def __init__(self, lib):
+        self._lib = lib
+
+    def __getattr__(self, name):
+        fn = getattr(self._lib, name)
+
+        def call(*args):
+            return fn(*[P + i * SPREAD + (a - P) if isinstance(a, int) and P <= a < P + 64 else a
+                        for i, a in enumerate(args)])
+        return call
+
+
 @pytest.fixture(scope="module")
-def L():
+def raw():
     if not os.path.exists(LIB_PATH):
         pytest.fail("libcoda.so is not built: run __graft_entry__.build() first")
     return coda.lib()
+
+
+@pytest.fixture(scope="module")
+def L(raw):
+    return Spread(raw)
 
 
 def test_header_declares_the_entry_points():
@@ -41,8 +66,8 @@ def test_header_declares_the_entry_points():
         assert need in names
 
 
-def test_library_exports_every_declared_symbol(L):
-    missing = [n for n in header_functions() if not hasattr(L, n)]
+def test_library_exports_every_declared_symbol(raw):
+    missing = [n for n in header_functions() if not hasattr(raw, n)]
     assert not missing, missing
 
 
@@ -235,3 +260,46 @@ def test_cross_entropy_validation(L):
     assert L.coda_lse_reduce(P, P, 64, 3, 512, P, P, P, None) == SHAPE
     assert L.coda_lse_reduce(None, P, 64, 2, 512, P, P, P, None) == NULL
     assert L.coda_lse_reduce(P, P, 0, 2, 512, None, None, None, None) == OK
+
+
+def test_overlapping_buffers_are_rejected(raw):
+    """Outputs may overlap neither an input nor another output (CODA_ERR_ARG, before
+    anything is enqueued). The ranges are the buffers' true byte sizes: sharing a buffer's
+    last 16 bytes is refused. (Adjacent buffers and inputs that alias each other pass;
+    that needs a launch, so the GPU tests cover it.)"""
+    M, K, D, N1 = 256, 512, 256, 264
+    b = 1 << 40
+    def at(i):
+        return b + i * SPREAD
+    x, w0, z, g, w1, h1, h2, part, r, y = (at(i) for i in range(10))
+    def fwd(**kw):
+        a = dict(x=x, w0=w0, z=z, g=g, w1=w1, h1=h1, h2=h2, part=part, r=r, y=y)
+        a.update(kw)
+        return raw.coda_gemm_rmsnorm_fwd(a["x"], a["w0"], a["z"], a["g"], a["w1"], M, K, D, N1, 1e-5, a["h1"],
+                                         a["h2"], a["part"], a["r"], a["y"], None)
+    h1_bytes = M * D * 2
+    assert fwd(h2=h1) == ARG                      # two outputs on one buffer
+    assert fwd(h2=h1 + h1_bytes - 16) == ARG      # last 16 bytes of h1 shared
+    assert fwd(y=x + 16) == ARG                   # output inside an input
+    assert fwd(r=w1) == ARG
+    assert fwd(part=z) == ARG
+    assert fwd(h1=g + D * 2 - 16) == ARG          # h1 starts in the last 16 bytes of gamma
+    assert raw.coda_gemm_residual_rmsnorm_partials(x, w0, z, g, M, K, D, h1, x, part, None) == ARG
+    assert raw.coda_gemm_rowscale(h2, w1, r, M, D, N1, h2, None) == ARG
+    # the stages' GEMM2 input h2 and r are outputs of the earlier stages: overlapping them is refused
+    assert fwd(h2=y) == ARG
+    assert raw.coda_gemm_swiglu(x, w0, M, K, 64, x + 2 * M * K - 16, None) == ARG   # last 16 bytes of x
+    assert raw.coda_gemm_swiglu(x, x, M, K, 64, x, None) == ARG
+    assert raw.coda_rowstat_reduce(part, M, 16, 4096, 1e-5, 0, part + 4 * (16 * M - 1), None) == ARG
+    assert raw.coda_gemm_rmsnorm_bwd_stats(x, w0, z, M, D, K, z, part, r, None) == ARG    # dh2 on h2
+    assert raw.coda_gemm_rmsnorm_bwd_stats(x, w0, z, M, D, K, h1, part, part, None) == ARG  # s on partials
+    assert raw.coda_gemm_rope(x, w0, z, g, M, K, 128, 128, 0, 128, 64, 0, g, None) == ARG  # out on a table
+    assert raw.coda_gemm_cross_entropy(x, w0, z, M, K, 512, part, r, r, y, None) == ARG     # target == lse
+    assert raw.coda_gemm_cross_entropy(x, w0, z, M, K, 512, part, z, r, y, None) == ARG     # target on labels
+    assert raw.coda_lse_reduce(part, z, M, 2, 512, r, y, part, None) == ARG                 # loss on tile_lse
+    assert raw.coda_rowdot_stat(x, w0, M, K, K, x, None) == ARG
+    assert raw.coda_colsum_reduce(part, 4, 256, part + 4 * 256 * 3, None) == ARG
+    assert raw.coda_baseline_copy(x, x + 16, 64, None) == ARG
+    assert raw.coda_baseline_gemm(x, w0, M, K, N1, 1, w0, None) == ARG
+    assert raw.coda_gemm_swiglu_bwd(x, w0, z, M, K, 64, z, None) == ARG
+    assert raw.coda_rope_tables(g, g + 4 * 8, 16, 128, 1e4, None) == ARG

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "coda.h"
 
 namespace coda {
@@ -20,6 +22,35 @@ inline int check_depth_or_width(int v) {
 }
 
 inline int check_rows(int M) { return (M < 0 || M > kMaxRows) ? CODA_ERR_SHAPE : CODA_OK; }
+
+// Byte range of one argument buffer, for the rule that output buffers overlap neither
+// the inputs nor each other (a NULL or empty range overlaps nothing).
+struct Span {
+  const void* p;
+  uint64_t bytes;
+};
+inline Span bf16_span(const void* p, long long rows, long long cols = 1) {
+  return Span{p, (uint64_t)rows * (uint64_t)cols * 2u};
+}
+inline Span f32_span(const void* p, long long rows, long long cols = 1) {
+  return Span{p, (uint64_t)rows * (uint64_t)cols * 4u};
+}
+inline bool overlap(const Span& a, const Span& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uint64_t a0 = (uint64_t)(uintptr_t)a.p, b0 = (uint64_t)(uintptr_t)b.p;
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+// CODA_ERR_ARG if an output overlaps another output or an input (inputs are only read,
+// so they may alias each other).
+inline int check_disjoint(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+  for (const Span* o = outs.begin(); o != outs.end(); ++o) {
+    for (const Span* o2 = o + 1; o2 != outs.end(); ++o2)
+      if (overlap(*o, *o2)) return CODA_ERR_ARG;
+    for (const Span& i : ins)
+      if (overlap(*o, i)) return CODA_ERR_ARG;
+  }
+  return CODA_OK;
+}
 
 inline int launch_status() {
   const hipError_t e = hipGetLastError();

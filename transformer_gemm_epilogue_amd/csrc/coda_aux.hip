@@ -298,6 +298,7 @@ int coda_rowstat_reduce(const float* partials, int M, int nb, int d, float eps, 
   CODA_NONNULL(partials);
   CODA_NONNULL(out);
   if (!aligned(partials, 4) || !aligned(out, 4)) return CODA_ERR_ALIGN;
+  CODA_TRY(check_disjoint({f32_span(out, M)}, {f32_span(partials, M, nb)}));
   return coda_rowstat_reduce_impl(partials, M, nb, d, eps, mode, out, as_stream(stream));
 }
 
@@ -308,6 +309,7 @@ int coda_rope_tables(float* cos_t, float* sin_t, int seq_len, int head_dim, doub
   if (!(theta > 0.0) || !(theta < __builtin_huge_val())) return CODA_ERR_ARG;
   if (!aligned(cos_t, 8) || !aligned(sin_t, 8)) return CODA_ERR_ALIGN;
   const long long n = (long long)seq_len * (head_dim / 2);
+  CODA_TRY(check_disjoint({f32_span(cos_t, n), f32_span(sin_t, n)}, {}));
   hipLaunchKernelGGL(rope_tables_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, as_stream(stream), cos_t, sin_t,
                      seq_len, head_dim / 2, head_dim, theta);
   return launch_status();
@@ -329,6 +331,8 @@ int coda_baseline_residual_rmsnorm(const uint16_t* h0, const uint16_t* z, const 
   CODA_ALIGN16(gamma);
   CODA_ALIGN16(h1);
   CODA_ALIGN16(o);
+  CODA_TRY(check_disjoint({bf16_span(h1, M, D), f32_span(r, M), bf16_span(o, M, D)},
+                          {bf16_span(h0, M, D), bf16_span(z, M, D), bf16_span(gamma, D)}));
   hipLaunchKernelGGL(residual_rmsnorm_kernel, dim3(M), dim3(256), 0, as_stream(stream), h0, z, gamma, D, eps, h1, r,
                      o);
   return launch_status();
@@ -343,6 +347,7 @@ int coda_baseline_rowdot(const uint16_t* a, const uint16_t* b, int M, int D, flo
   CODA_NONNULL(s);
   CODA_ALIGN16(a);
   CODA_ALIGN16(b);
+  CODA_TRY(check_disjoint({f32_span(s, M)}, {bf16_span(a, M, D), bf16_span(b, M, D)}));
   hipLaunchKernelGGL(rowdot_kernel, dim3(M), dim3(256), 0, as_stream(stream), a, b, D, s);
   return launch_status();
 }
@@ -363,6 +368,8 @@ int coda_baseline_rope(const uint16_t* h, const float* cos_t, const float* sin_t
   CODA_ALIGN16(h);
   CODA_ALIGN16(out);
   if (!aligned(cos_t, 16) || !aligned(sin_t, 16)) return CODA_ERR_ALIGN;
+  const long long tab = (long long)seq_len * (head_dim / 2);
+  CODA_TRY(check_disjoint({bf16_span(out, M, N)}, {bf16_span(h, M, N), f32_span(cos_t, tab), f32_span(sin_t, tab)}));
   const long long n = (long long)M * (N / 8);
   hipLaunchKernelGGL(rope_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, as_stream(stream), h, cos_t, sin_t, M,
                      (int)N, n_q + n_k, head_dim, seq_len, pos_offset, out);
@@ -377,6 +384,7 @@ int coda_baseline_swiglu(const uint16_t* h, int M, int F, uint16_t* out, void* s
   CODA_NONNULL(out);
   CODA_ALIGN16(h);
   CODA_ALIGN16(out);
+  CODA_TRY(check_disjoint({bf16_span(out, M, F)}, {bf16_span(h, M, 2LL * F)}));
   const long long n = (long long)M * (F / 4);
   hipLaunchKernelGGL(swiglu_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, as_stream(stream), h, M, F, out);
   return launch_status();
@@ -388,6 +396,7 @@ int coda_baseline_copy(const void* src, void* dst, int64_t bytes, void* stream) 
   if (bytes <= 0 || bytes % 16 != 0) return CODA_ERR_SHAPE;
   CODA_ALIGN16(src);
   CODA_ALIGN16(dst);
+  CODA_TRY(check_disjoint({Span{dst, (uint64_t)bytes}}, {Span{src, (uint64_t)bytes}}));
   const long long n16 = bytes / 16;
   const unsigned grid = (unsigned)std::min<long long>(blocks_for(n16, 256), 256LL * 16);
   hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, as_stream(stream), (const u32x4_t*)src, (u32x4_t*)dst,
@@ -401,6 +410,7 @@ int coda_baseline_mfma_loop(const uint16_t* operands, int n_frag, int iters, int
   CODA_NONNULL(out);
   CODA_ALIGN16(operands);
   if (!aligned(out, 4)) return CODA_ERR_ALIGN;
+  CODA_TRY(check_disjoint({f32_span(out, (long long)grid * 512)}, {bf16_span(operands, n_frag, 8)}));
   hipLaunchKernelGGL(mfma_loop_kernel, dim3(grid), dim3(512), 0, as_stream(stream), (const bf16x8_t*)operands, n_frag,
                      iters, out);
   return launch_status();

@@ -143,6 +143,7 @@ int coda_colstat_num_partials(int rows, int* tiles) {
 int coda_rowdot_stat(const uint16_t* dy, const uint16_t* y, int M, int N, int d, float* s, void* stream) {
   CODA_TRY(check_rowdot(dy, y, M, N, d, s));
   if (M == 0) return CODA_OK;
+  CODA_TRY(check_disjoint({f32_span(s, M)}, {bf16_span(dy, M, N), bf16_span(y, M, N)}));
   return launch_rowdot(dy, y, M, N, d, s, as_stream(stream));
 }
 
@@ -151,6 +152,7 @@ int coda_colsum_reduce(const float* partials, int tiles, int width, float* out, 
   CODA_NONNULL(out);
   if (tiles > 0) CODA_NONNULL(partials);
   if ((partials && !aligned(partials, 4)) || !aligned(out, 4)) return CODA_ERR_ALIGN;
+  CODA_TRY(check_disjoint({f32_span(out, width)}, {f32_span(partials, tiles, width)}));
   return launch_colsum(partials, tiles, width, out, as_stream(stream));
 }
 
@@ -159,6 +161,9 @@ int coda_gemm_rmsnorm_bwd_dx(const uint16_t* dy, const uint16_t* w1, const uint1
                              uint16_t* dh1, float* dgamma_partials, void* stream) {
   CODA_TRY(check_dx(dy, w1, h1, gamma, r, s, g_res, M, D, N, dh1, dgamma_partials));
   if (M == 0) return CODA_OK;
+  CODA_TRY(check_disjoint({bf16_span(dh1, M, D), f32_span(dgamma_partials, row_tiles(M), D)},
+                          {bf16_span(dy, M, N), bf16_span(w1, D, N), bf16_span(h1, M, D), bf16_span(gamma, D),
+                           f32_span(r, M), f32_span(s, M), bf16_span(g_res, M, D)}));
   return launch_dx(dy, w1, h1, gamma, r, s, g_res, M, D, N, dh1, dgamma_partials, as_stream(stream));
 }
 
@@ -169,6 +174,12 @@ int coda_rmsnorm_bwd(const uint16_t* dy, const uint16_t* w1, const uint16_t* h1,
   CODA_TRY(check_rowdot(dy, y, M, N, D, s));
   CODA_NONNULL(dgamma);
   if (!aligned(dgamma, 4)) return CODA_ERR_ALIGN;
+  // s is written by the first launch and read by the second: an output here
+  if (M > 0)
+    CODA_TRY(check_disjoint({f32_span(s, M), bf16_span(dh1, M, D), f32_span(dgamma_partials, row_tiles(M), D),
+                             f32_span(dgamma, D)},
+                            {bf16_span(dy, M, N), bf16_span(w1, D, N), bf16_span(h1, M, D), bf16_span(gamma, D),
+                             f32_span(r, M), bf16_span(y, M, N), bf16_span(g_res, M, D)}));
   const hipStream_t st = as_stream(stream);
   if (M > 0) {
     CODA_TRY(launch_rowdot(dy, y, M, N, D, s, st));
@@ -191,6 +202,8 @@ int coda_gemm_swiglu_bwd(const uint16_t* dy, const uint16_t* w_down, const uint1
   CODA_ALIGN16(w_down);
   CODA_ALIGN16(h);
   CODA_ALIGN16(dh);
+  CODA_TRY(check_disjoint({bf16_span(dh, M, 2LL * F)},
+                          {bf16_span(dy, M, Dm), bf16_span(w_down, F, Dm), bf16_span(h, M, 2LL * F)}));
   // dy [M, Dm] times W_down^T: depth = Dm, output width = F; W_down [F, Dm] is the NK layout.
   const GemmProblem p{dy, w_down, M, F, Dm};
   const EpiSwiGLUBwd::Args ea{h, dh};

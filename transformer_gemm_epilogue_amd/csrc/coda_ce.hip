@@ -135,6 +135,9 @@ int coda_lse_reduce(const float* tile_lse, const int32_t* labels, int M, int nb,
   CODA_NONNULL(tile_lse);
   if (!aligned(tile_lse, 4)) return CODA_ERR_ALIGN;
   CODA_TRY(check_ce_outputs(labels, target, lse, loss));
+  // target is read and rewritten (zero on ignored rows): an output
+  CODA_TRY(check_disjoint({f32_span(target, M), f32_span(lse, M), f32_span(loss, M)},
+                          {f32_span(tile_lse, M, nb), Span{labels, (uint64_t)M * 4u}}));
   return launch_lse(tile_lse, labels, M, nb, V, target, lse, loss, as_stream(stream));
 }
 
@@ -152,6 +155,8 @@ int coda_gemm_cross_entropy(const uint16_t* x, const uint16_t* w, const int32_t*
   if (!aligned(tile_lse, 4)) return CODA_ERR_ALIGN;
   const int nb = (V + kBN - 1) / kBN;
   CODA_TRY(check_ce_outputs(labels, target, lse, loss));
+  CODA_TRY(check_disjoint({f32_span(tile_lse, M, nb), f32_span(target, M), f32_span(lse, M), f32_span(loss, M)},
+                          {bf16_span(x, M, K), bf16_span(w, K, V), Span{labels, (uint64_t)M * 4u}}));
   const hipStream_t st = as_stream(stream);
   const GemmProblem p{x, w, M, V, K};
   const EpiCrossEntropy::Args ea{labels, tile_lse, target, nb};

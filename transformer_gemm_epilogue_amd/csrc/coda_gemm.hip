@@ -63,6 +63,13 @@ int check_gemm1(const uint16_t* x, const uint16_t* w0, const uint16_t* z, const 
   return CODA_OK;
 }
 
+int disjoint_gemm1(const uint16_t* x, const uint16_t* w0, const uint16_t* z, const uint16_t* gamma, int M, int K,
+                   int D, uint16_t* h1, uint16_t* h2, float* partials) {
+  const int nb = (D + kBN - 1) / kBN;
+  return check_disjoint({bf16_span(h1, M, D), bf16_span(h2, M, D), f32_span(partials, M, nb)},
+                        {bf16_span(x, M, K), bf16_span(w0, K, D), bf16_span(z, M, D), bf16_span(gamma, D)});
+}
+
 int check_gemm2(const uint16_t* h2, const uint16_t* w1, const float* r, int M, int D, int N1, uint16_t* y) {
   CODA_TRY(check_rows(M));
   CODA_TRY(check_depth_or_width(D));
@@ -77,6 +84,17 @@ int check_gemm2(const uint16_t* h2, const uint16_t* w1, const float* r, int M, i
   CODA_ALIGN16(y);
   if (!aligned(r, 4)) return CODA_ERR_ALIGN;
   return CODA_OK;
+}
+
+// The three stages' buffers together: h2 and r are outputs that later stages read back;
+// x, w0, z, gamma and w1 are inputs.
+int disjoint_fwd(const uint16_t* x, const uint16_t* w0, const uint16_t* z, const uint16_t* gamma,
+                 const uint16_t* w1, int M, int K, int D, int N1, uint16_t* h1, uint16_t* h2, float* partials,
+                 float* r, uint16_t* y) {
+  return check_disjoint({bf16_span(h1, M, D), bf16_span(h2, M, D), f32_span(partials, M, (D + kBN - 1) / kBN),
+                         f32_span(r, M), bf16_span(y, M, N1)},
+                        {bf16_span(x, M, K), bf16_span(w0, K, D), bf16_span(z, M, D), bf16_span(gamma, D),
+                         bf16_span(w1, D, N1)});
 }
 
 int run_gemm1(const uint16_t* x, const uint16_t* w0, const uint16_t* z, const uint16_t* gamma, int M, int K,
@@ -124,6 +142,7 @@ int coda_gemm_residual_rmsnorm_partials(const uint16_t* x, const uint16_t* w0, c
                                         uint16_t* h2, float* partials, void* stream) {
   CODA_TRY(check_gemm1(x, w0, z, gamma, M, K, D, h1, h2, partials));
   if (M == 0) return CODA_OK;
+  CODA_TRY(disjoint_gemm1(x, w0, z, gamma, M, K, D, h1, h2, partials));
   return run_gemm1(x, w0, z, gamma, M, K, D, h1, h2, partials, as_stream(stream));
 }
 
@@ -131,6 +150,7 @@ int coda_gemm_rowscale(const uint16_t* h2, const uint16_t* w1, const float* r, i
                        uint16_t* y, void* stream) {
   CODA_TRY(check_gemm2(h2, w1, r, M, D, N1, y));
   if (M == 0) return CODA_OK;
+  CODA_TRY(check_disjoint({bf16_span(y, M, N1)}, {bf16_span(h2, M, D), bf16_span(w1, D, N1), f32_span(r, M)}));
   return run_gemm2(h2, w1, r, M, D, N1, y, as_stream(stream));
 }
 
@@ -141,6 +161,7 @@ int coda_gemm_rmsnorm_fwd(const uint16_t* x, const uint16_t* w0, const uint16_t*
   CODA_TRY(check_gemm1(x, w0, z, gamma, M, K, D, h1, h2, partials));
   CODA_TRY(check_gemm2(h2, w1, r, M, D, N1, y));
   if (M == 0) return CODA_OK;
+  CODA_TRY(disjoint_fwd(x, w0, z, gamma, w1, M, K, D, N1, h1, h2, partials, r, y));
   const hipStream_t s = as_stream(stream);
   CODA_TRY(run_gemm1(x, w0, z, gamma, M, K, D, h1, h2, partials, s));
   CODA_TRY(coda_rowstat_reduce_impl(partials, M, (D + kBN - 1) / kBN, D, eps, CODA_ROWSTAT_RSQRT_MEAN_EPS, r, s));
@@ -169,6 +190,9 @@ int gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, const fl
   CODA_ALIGN16(w);
   CODA_ALIGN16(out);
   if (!aligned(cos_t, 8) || !aligned(sin_t, 8)) return CODA_ERR_ALIGN;
+  const long long tab = (long long)seq_len * (head_dim / 2);
+  CODA_TRY(check_disjoint({bf16_span(out, M, N)},
+                          {bf16_span(x, M, K), bf16_span(w, K, N), f32_span(cos_t, tab), f32_span(sin_t, tab)}));
   const GemmProblem p{x, w, M, (int)N, K};
   const EpiRope::Args ea{cos_t, sin_t, out, n_q + n_k, head_dim, seq_len, pos_offset, inverse};
   if (persistent) return launch_gemm_persistent<true, EpiRope>(p, ea, stream);
@@ -208,6 +232,7 @@ int coda_gemm_swiglu(const uint16_t* x, const uint16_t* w, int M, int K, int F, 
   CODA_ALIGN16(x);
   CODA_ALIGN16(w);
   CODA_ALIGN16(out);
+  CODA_TRY(check_disjoint({bf16_span(out, M, F)}, {bf16_span(x, M, K), bf16_span(w, K, 2LL * F)}));
   const GemmProblem p{x, w, M, 2 * F, K};
   const EpiSwiGLU::Args ea{out, F};
   return launch_gemm<true, EpiSwiGLU>(p, ea, as_stream(stream));
@@ -230,10 +255,12 @@ int coda_gemm_rmsnorm_bwd_stats(const uint16_t* dy, const uint16_t* w1, const ui
   CODA_ALIGN16(h2);
   CODA_ALIGN16(dh2);
   if (!aligned(partials, 4) || !aligned(s, 4)) return CODA_ERR_ALIGN;
+  const int nb = (D + kBN - 1) / kBN;
+  CODA_TRY(check_disjoint({bf16_span(dh2, M, D), f32_span(partials, M, nb), f32_span(s, M)},
+                          {bf16_span(dy, M, N), bf16_span(w1, D, N), bf16_span(h2, M, D)}));
   const hipStream_t st = as_stream(stream);
   // dy [M, N] times W1^T: depth = N, output width = D, W1 [D, N] is the NK layout.
   const GemmProblem p{dy, w1, M, D, N};
-  const int nb = (D + kBN - 1) / kBN;
   const EpiDotRowPartials::Args ea{h2, dh2, partials, nb};
   CODA_TRY((launch_gemm<false, EpiDotRowPartials>(p, ea, st)));
   return coda_rowstat_reduce_impl(partials, M, nb, D, 0.0f, CODA_ROWSTAT_MEAN, s, st);
@@ -251,6 +278,7 @@ int coda_baseline_gemm(const uint16_t* a, const uint16_t* b, int M, int K, int N
   CODA_ALIGN16(a);
   CODA_ALIGN16(b);
   CODA_ALIGN16(c);
+  CODA_TRY(check_disjoint({bf16_span(c, M, N)}, {bf16_span(a, M, K), bf16_span(b, K, N)}));
   const GemmProblem p{a, b, M, N, K};
   const EpiStore::Args ea{c};
   if (b_kn) return launch_gemm<true, EpiStore>(p, ea, as_stream(stream));
