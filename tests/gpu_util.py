@@ -55,11 +55,37 @@ def assert_close(name: str, got, ref, rel_fro=REL_FRO, max_abs_frac=MAX_ABS):
     assert ma <= max_abs_frac * mr, f"{name}: max abs error {ma:.3e} > {max_abs_frac:.1e} * {mr:.3e}"
 
 
-def sample_rows(M: int, n: int, seed: int = 0) -> np.ndarray:
-    """Rows to check at full size: the first and last rows of the batch, rows at tile
-    edges, and random rows."""
-    rng = np.random.default_rng(seed)
-    fixed = {0, 1, 255, 256, M // 2, M - 257, M - 256, M - 1}
-    fixed = {r for r in fixed if 0 <= r < M}
-    rnd = rng.choice(M, size=max(0, n - len(fixed)), replace=False)
-    return np.array(sorted(fixed | set(int(r) for r in rnd)))
+def _block_reduce(ufunc, a: np.ndarray, tile_m: int, tile_n: int) -> np.ndarray:
+    """ufunc.reduceat of a 1-D or 2-D array over blocks of tile_m rows (x tile_n columns)."""
+    s = ufunc.reduceat(a, np.arange(0, a.shape[0], tile_m), axis=0)
+    return s if a.ndim == 1 else ufunc.reduceat(s, np.arange(0, a.shape[1], tile_n), axis=1)
+
+
+def assert_close_tiles(name: str, got, ref, rel_fro=REL_FRO, max_abs_frac=MAX_ABS, tile_m=256, tile_n=256):
+    """The gate on the whole tensor, then on every output tile of the GEMM on its own.
+
+    A kernel computes each 256 x 256 output tile independently (its own depth loop, its
+    own epilogue), so a fault confined to one tile (a dropped or repeated depth step, a
+    misplaced side input) can stay below the whole-tensor relative error of thousands of
+    tiles. The same relative bound therefore applies per tile (per 256-row block for 1-D
+    outputs); a tile whose reference is exactly zero must come out within the max-abs
+    bound of the whole tensor."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert_close(name, got, ref, rel_fro, max_abs_frac)
+    if ref.size == 0:
+        return
+    diff = got - ref
+    num = _block_reduce(np.add, diff * diff, tile_m, tile_n)
+    den = _block_reduce(np.add, ref * ref, tile_m, tile_n)
+    nz = den > 0
+    rel = np.zeros_like(num)
+    rel[nz] = np.sqrt(num[nz] / den[nz])
+    worst = float(rel.max())
+    log(f"  {name}: {num.size} tiles, worst tile rel_fro={worst:.3e}")
+    bad = np.argwhere(rel > rel_fro)
+    assert bad.size == 0, f"{name}: {len(bad)} tiles above {rel_fro:.1e}, first at block {bad[0].tolist()}"
+    if not nz.all():
+        dmax = _block_reduce(np.maximum, np.abs(diff), tile_m, tile_n)
+        limit = max_abs_frac * float(np.max(np.abs(ref)))
+        assert float(dmax[~nz].max()) <= limit, f"{name}: a tile with an all-zero reference is off by more than {limit}"

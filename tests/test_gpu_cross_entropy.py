@@ -5,7 +5,7 @@ import pytest
 
 import oracle as O
 import workloads as W
-from gpu_util import assert_close, log, sample_rows, to_dev_bf16
+from gpu_util import assert_close, assert_close_tiles, log, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -43,17 +43,29 @@ def test_cross_entropy_small_full_compare(coda, shape):
     assert np.all(loss[~ref["valid"]] == 0) and np.all(target[~ref["valid"]] == 0)
 
 
-def test_cross_entropy_full_size_sampled(coda):
+def check_full(wl, got):
+    loss, lse, target, tile = got
+    ref = O.gemm_cross_entropy(wl["x"], wl["w"], wl["labels"])
+    assert_close_tiles("tile_lse", tile, ref["tile_lse"], rel_fro=TIGHT, tile_n=1)
+    assert_close_tiles("lse", lse, ref["lse"], rel_fro=TIGHT)
+    assert_close_tiles("target", target, ref["target"], rel_fro=TIGHT)
+    assert_close_tiles("loss", loss, ref["loss"], rel_fro=TIGHT)
+    assert np.all(loss[~ref["valid"]] == 0) and np.all(target[~ref["valid"]] == 0)
+    assert np.all(np.isfinite(loss)) and np.all(loss >= 0)
+
+
+# the kernel table's two cross-entropy shapes (M x vocab x K), every row compared; every
+# 97th row's label is ignored
+def test_cross_entropy_full_size(coda):
     wl = W.cross_entropy(ignore_every=97)
     log(f"cross_entropy {wl.name}")
-    loss, lse, target, tile = run(coda, wl)
-    rows = sample_rows(wl["M"], 40, seed=8)
-    rows = np.union1d(rows, [0, 97])           # include ignored rows
-    ref = O.gemm_cross_entropy(wl["x"], wl["w"], wl["labels"], rows=rows)
-    assert_close("tile_lse", tile[rows], ref["tile_lse"], rel_fro=TIGHT)
-    assert_close("lse", lse[rows], ref["lse"], rel_fro=TIGHT)
-    assert_close("loss", loss[rows], ref["loss"], rel_fro=TIGHT)
-    assert np.all(np.isfinite(loss)) and np.all(loss >= 0)
+    check_full(wl, run(coda, wl))
+
+
+def test_cross_entropy_8192_full_size(coda):
+    wl = W.cross_entropy_8k(ignore_every=97)
+    log(f"cross_entropy {wl.name}")
+    check_full(wl, run(coda, wl))
 
 
 def test_cross_entropy_deterministic_and_stages(coda):

@@ -205,6 +205,12 @@ def cross_entropy(seed: int = 8, M: int = 4096, K: int = 4096, V: int = 32768, i
                     dict(M=M, K=K, V=V))
 
 
+def cross_entropy_8k(seed: int = 8, ignore_every: int = 0) -> Workload:
+    """GEMM + cross-entropy at the larger of the kernel table's two shapes: 8192 tokens,
+    vocabulary 32768, hidden 8192; same distributions as cross_entropy."""
+    return cross_entropy(seed=seed, M=8192, K=8192, V=32768, ignore_every=ignore_every)
+
+
 # The five workloads at their stated sizes (seed i for workload i).
 WORKLOADS = {
     "tiny_fwd": tiny_fwd,
