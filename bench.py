@@ -479,11 +479,21 @@ def cpu_baseline(target_s: float):
     row-independent), timed on this host's cores; scaled to the metric's unit."""
     import oracle as O
     import workloads as W
+    blas = "unknown BLAS"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        cores = max([int(i.get("num_threads", 1)) for i in info] or [1])
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '?')}"
     except Exception:
         cores = os.cpu_count() or 1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next(ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name"))
+    except Exception:
+        pass
     wl = W.llama_fwd()
     M, K, D, N1 = wl["M"], wl["K"], wl["D"], wl["N1"]
 
@@ -500,7 +510,9 @@ def cpu_baseline(target_s: float):
     flops = 2.0 * n * K * D + 2.0 * n * D * N1
     return {"value": round(flops / t / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} of {M} rows of the same workload (all five fp64 outputs per row, incl. "
-                      f"weight decode), {t:.1f} s wall"}
+                      f"weight decode), {t:.1f} s wall",
+            "implementation": f"numpy fp64, matrix products through {blas} with {cores} threads",
+            "host": {"nproc": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model}}
 
 
 def main():

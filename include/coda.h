@@ -68,6 +68,11 @@ const char* coda_status_string(int status);
 /* ABI version of this header (major * 100 + minor). */
 int coda_abi_version(void);
 
+/* SHA-256 (64 hex digits, static string) of the sources and compile flags this library
+ * was built from, as computed by the build step; "unknown" for a build that did not
+ * set it. Lets a loader refuse a library that is stale against its sources. */
+const char* coda_build_source_hash(void);
+
 /* Number of row partials nb = ceil(width / CODA_PARTIAL_TILE_N) that the epilogues
  * write per row for an output of `width` columns. Returns CODA_ERR_NULL or
  * CODA_ERR_SHAPE (width < 1). */

@@ -72,7 +72,7 @@ def test_library_exports_every_declared_symbol(raw):
 
 
 def test_binding_covers_every_declared_symbol():
-    declared = set(header_functions()) - {"coda_status_string"}
+    declared = set(header_functions()) - {"coda_status_string", "coda_build_source_hash"}
     assert declared == set(coda.SIGNATURES)
 
 
@@ -303,3 +303,18 @@ def test_overlapping_buffers_are_rejected(raw):
     assert raw.coda_baseline_gemm(x, w0, M, K, N1, 1, w0, None) == ARG
     assert raw.coda_gemm_swiglu_bwd(x, w0, z, M, K, 64, z, None) == ARG
     assert raw.coda_rope_tables(g, g + 4 * 8, 16, 128, 1e4, None) == ARG
+
+
+def test_library_matches_its_sources(raw, tmp_path):
+    """The loaded library was built from the sources next to it; a copy of those sources
+    with one edited file no longer matches, and the check refuses it."""
+    import shutil
+    coda.check_source_hash(raw)            # the in-tree build is current
+    shutil.copytree(os.path.join(ROOT, "transformer_gemm_epilogue_amd", "csrc"),
+                    tmp_path / "transformer_gemm_epilogue_amd" / "csrc")
+    shutil.copytree(os.path.join(ROOT, "include"), tmp_path / "include")
+    coda.check_source_hash(raw, str(tmp_path))   # an unedited copy matches
+    src = tmp_path / "transformer_gemm_epilogue_amd" / "csrc" / "coda_aux.hip"
+    src.write_text(src.read_text() + "\n// edited\n")
+    with pytest.raises(coda.StaleLibraryError):
+        coda.check_source_hash(raw, str(tmp_path))

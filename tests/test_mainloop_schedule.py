@@ -16,7 +16,19 @@ as the kernel issues it, at the granularity of one DMA instruction per thread:
 
 and replays it for many depths and tile sequences, asserting the invariants. Planted
 schedule mistakes (a wait one load too short, loads issued a step late or shifted by a
-step, an epilogue area on a prefetched slot) must make it fail."""
+step, an epilogue area on a prefetched slot) must make it fail.
+
+Every vector-memory instruction of the loop is counted by the waits, whatever its
+destination: the DMA loads into LDS, and any load whose data returns into a VGPR. Such a
+load writes its register when the data arrives, not when it issues; the hardware does
+not hold back other writers of that register, so it must stay reserved until a wait has
+retired the load. A load issued from inline asm with the register as an asm output is
+done, as far as the compiler knows, when the asm statement ends: the register may be
+reassigned right away (to an address, say) and then be overwritten by the late data. An
+L2 prefetch of future depth steps written that way (one 4-byte load per lane into a
+dummy "+v" operand, its loads counted in the waits) faulted the GPU; the model shows the
+cause: the waits retire the prefetch loads a step later, long after their register was
+given back. The main loop itself issues no load with a register destination."""
 import itertools
 
 import pytest
@@ -51,6 +63,8 @@ class Ring:
     def wait(self, n):
         while len(self.pending) > n:
             ld = self.pending.pop(0)
+            if ld["slot"] is None:     # a load into a register: nothing lands in LDS
+                continue
             self.landed[ld["slot"]][(ld["half"], ld["j"])] = ld["what"]
             self.retired_epoch[(ld["slot"], ld["what"], ld["half"], ld["j"])] = self.epoch
 
@@ -58,6 +72,28 @@ class Ring:
         check(self.last_read[slot] < self.epoch,
               f"DMA into slot {slot} ({what}) in the barrier interval of its last read")
         self.pending.append(dict(slot=slot, what=what, half=half, j=j))
+
+    def issue_to_vgpr(self, reg):
+        """A load whose data returns into VGPR `reg` (counted by the waits like a DMA)."""
+        self.pending.append(dict(slot=None, reg=reg))
+
+    def release(self, reg):
+        """The compiler may hand `reg` to another value from here on: no load into it may
+        still be in flight."""
+        check(all(ld.get("reg") != reg for ld in self.pending),
+              f"VGPR {reg} given back while a load into it is in flight")
+
+    def retire_reg(self, reg):
+        """The wait a compiler inserts before it reuses `reg`: every load into it retired."""
+        last = max((i for i, ld in enumerate(self.pending) if ld.get("reg") == reg), default=-1)
+        self.wait(len(self.pending) - 1 - last)
+
+    def wait_for_step(self, what):
+        """The shortest wait that retires every pending load of step `what`: the vmcnt a
+        schedule with extra loads would have to use."""
+        last = max((i for i, ld in enumerate(self.pending) if ld["slot"] is not None and ld["what"] == what),
+                   default=-1)
+        self.wait(len(self.pending) - 1 - last)
 
     def read(self, slot, what, halves):
         """A read of step `what` needs every thread's loads of it retired before the last
@@ -75,10 +111,16 @@ class Ring:
         self.last_read[slot] = self.epoch
 
 
-def run(KTs, waits=(8, 5), prologue_wait=9, pair_ahead=3, w_ahead=3, epi_shift=NEXT):
+def run(KTs, waits=(8, 5), prologue_wait=9, pair_ahead=3, w_ahead=3, epi_shift=NEXT, prefetch=None):
     """Replay one workgroup walking tiles of depths KTs (a single entry: the per-tile
     schedule). waits = (even step, odd step) vmcnt limits; step kt loads W of kt + w_ahead
-    and, on odd steps, X of kt + pair_ahead and the step after it."""
+    and, on odd steps, X of kt + pair_ahead and the step after it.
+
+    prefetch (not in the kernel: the rejected variant and its repair) adds one load per
+    step into a VGPR after the barrier, with every wait lengthened to retire exactly the
+    loads it needs: "asm" gives the register back right after the issuing statement;
+    "reserved" keeps it until a wait has retired the load (the wait a compiler inserts
+    before it reuses a register that a tracked load writes)."""
     R = Ring()
     rot = 0
 
@@ -120,7 +162,10 @@ def run(KTs, waits=(8, 5), prologue_wait=9, pair_ahead=3, w_ahead=3, epi_shift=N
             odd = kt % 2 == 1
             R.read(phys(S), (tile, kt), "X")        # X blocks 4..7 of kt
             wload(tile, KT, has_next, kt + w_ahead)  # W of kt+3 into the slot of kt-2
-            R.wait(waits[1] if odd else waits[0])
+            if prefetch:
+                R.wait_for_step((tile, kt + 1) if kt + 1 < KT else None)
+            else:
+                R.wait(waits[1] if odd else waits[0])
             R.barrier()
             nxt = phys((S + 1) % NS)
             if kt + 1 < KT:
@@ -129,7 +174,16 @@ def run(KTs, waits=(8, 5), prologue_wait=9, pair_ahead=3, w_ahead=3, epi_shift=N
                 R.touch(nxt)
             if odd:
                 pair(tile, KT, has_next, kt + pair_ahead)  # X of kt+3, kt+4 into the slots of kt-2, kt-1
+            if prefetch == "reserved":
+                R.retire_reg("pf")                  # the register is reused: its last load is waited for
+                R.release("pf")
+            if prefetch:
+                R.issue_to_vgpr("pf")               # an L2 prefetch of a later step
+                if prefetch == "asm":
+                    R.release("pf")                 # the asm output is dead to the compiler
         R.wait(0)
+        if prefetch:
+            R.release("pf")
         R.barrier()
         e = (rot + KT % NS + epi_shift) % NS
         epi = {e, (e + 1) % NS, (e + 2) % NS}
@@ -183,3 +237,15 @@ def test_planted_schedule_mistakes_fail(plant):
     with pytest.raises(ScheduleError):
         for KTs in ([9], [12, 12], [7, 10, 5], [4] * 4, [13] * 3):
             run(KTs, **plant)
+
+
+def test_register_destination_loads():
+    """An L2 prefetch into a register, every wait lengthened to count it: with the
+    register kept until a wait retires the load the schedule holds; with the register
+    given back at the end of the issuing asm statement (the rejected variant) a later
+    load lands in a register that may already hold something else."""
+    for KTs in ([1], [2], [9], [30], [12, 12], [7, 10, 5]):
+        run(KTs, prefetch="reserved")
+    for KTs in ([9], [12, 12]):
+        with pytest.raises(ScheduleError, match="in flight"):
+            run(KTs, prefetch="asm")

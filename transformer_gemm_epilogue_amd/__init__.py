@@ -13,10 +13,12 @@ from __future__ import annotations
 import ctypes
 import os
 
-from .build import LIB_PATH
+from .build import LIB_PATH, ROOT, source_hash
 
 __all__ = [
     "CodaError",
+    "StaleLibraryError",
+    "check_source_hash",
     "lib",
     "PARTIAL_TILE_N",
     "ROWSTAT_RSQRT_MEAN_EPS",
@@ -100,13 +102,31 @@ class CodaError(RuntimeError):
 _lib = None
 
 
+class StaleLibraryError(RuntimeError):
+    """libcoda.so was built from sources other than those next to it."""
+
+
+def check_source_hash(L: ctypes.CDLL, root: str = ROOT) -> None:
+    """Raise StaleLibraryError unless the library's embedded source hash equals the hash
+    of the sources under `root`."""
+    built = L.coda_build_source_hash().decode()
+    here = source_hash(root)
+    if built != here:
+        raise StaleLibraryError(f"{LIB_PATH} was built from other sources (built {built[:16]}, sources "
+                                f"{here[:16]}): rebuild it with transformer_gemm_epilogue_amd.build.build()")
+
+
 def lib() -> ctypes.CDLL:
-    """Load libcoda.so (built in-tree by build.py) and declare its signatures."""
+    """Load libcoda.so (built in-tree by build.py), check that it was built from the
+    sources next to it, and declare its signatures."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built: run transformer_gemm_epilogue_amd.build.build()")
         L = ctypes.CDLL(LIB_PATH)
+        L.coda_build_source_hash.argtypes = []
+        L.coda_build_source_hash.restype = ctypes.c_char_p
+        check_source_hash(L)
         for name, args in SIGNATURES.items():
             fn = getattr(L, name)
             fn.argtypes = args

@@ -1,10 +1,14 @@
 """Build step for libcoda.so: compiles the HIP sources for gfx950 with hipcc.
 
 The library is built in-tree (next to this file) so that it travels with the source
-tree; nothing is JIT-compiled or cached elsewhere.
+tree; nothing is JIT-compiled or cached elsewhere. The build embeds a SHA-256 of what
+it was built from (every file under csrc/, include/coda.h and the compile flags), which
+the library returns from coda_build_source_hash(); loading compares it with the sources
+next to the library and refuses a stale build.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -42,11 +46,29 @@ def compile_flags() -> list:
     ]
 
 
+def source_hash(root: str = ROOT, extra_flags=()) -> str:
+    """SHA-256 (hex) of every file under <root>/transformer_gemm_epilogue_amd/csrc and of
+    <root>/include/coda.h, in sorted order of their paths, and of the compile flags."""
+    csrc = os.path.join(root, "transformer_gemm_epilogue_amd", "csrc")
+    files = sorted(os.path.join("transformer_gemm_epilogue_amd", "csrc", f) for f in os.listdir(csrc)
+                   if os.path.isfile(os.path.join(csrc, f)))
+    files.append(os.path.join("include", "coda.h"))
+    h = hashlib.sha256()
+    for rel in files:
+        h.update(rel.encode() + b"\0")
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read() + b"\0")
+    flags = [f for f in compile_flags() if not f.startswith("-I")] + list(extra_flags)
+    h.update(" ".join(flags).encode())
+    return h.hexdigest()
+
+
 def build(verbose: bool = False, out: str = LIB_PATH, extra_flags=()) -> str:
     """Compile every HIP source into one shared library; returns its path."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = out + ".tmp"
-    cmd = [hipcc(), *compile_flags(), *extra_flags, "-shared", "-o", tmp, *srcs]
+    digest = source_hash(extra_flags=extra_flags)
+    cmd = [hipcc(), *compile_flags(), *extra_flags, f'-DCODA_SOURCE_HASH="{digest}"', "-shared", "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -130,10 +130,15 @@ const char* coda_status_string(int status) {
 
 int coda_abi_version(void) { return 100; }
 
+#ifndef CODA_SOURCE_HASH
+#define CODA_SOURCE_HASH "unknown"
+#endif
+const char* coda_build_source_hash(void) { return CODA_SOURCE_HASH; }
+
 int coda_rowstat_num_partials(int width, int* nb) {
   CODA_NONNULL(nb);
   if (width < 1) return CODA_ERR_SHAPE;
-  *nb = (width + CODA_PARTIAL_TILE_N - 1) / CODA_PARTIAL_TILE_N;
+  *nb = (int)(((long long)width + CODA_PARTIAL_TILE_N - 1) / CODA_PARTIAL_TILE_N);
   return CODA_OK;
 }
 
