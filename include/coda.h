@@ -103,6 +103,27 @@ int coda_gemm_rmsnorm_fwd(const uint16_t* x, const uint16_t* w0, const uint16_t*
                           int N1, float eps, uint16_t* h1, uint16_t* h2, float* partials,
                           float* r, uint16_t* y, void* stream);
 
+/* Capacity, in fp32 values, of the fixed device array that coda_gemm_rmsnorm_fwd_noalloc
+ * uses as its row-partial workspace (4 MiB per GPU). */
+#define CODA_NOALLOC_SCRATCH_FLOATS (1 << 20)
+
+/* coda_gemm_rmsnorm_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same three
+ * launches and bit-identical h1, h2, r and y, with the row partials kept in a fixed
+ * device array inside the library instead of a caller's buffer. The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); the first call on a
+ * device looks up that device's copy of the array.
+ * Limits and sharing: M * nb <= CODA_NOALLOC_SCRATCH_FLOATS with nb =
+ * coda_rowstat_num_partials(D) (e.g. M <= 65536 at D = 4096), else CODA_ERR_WORKSPACE.
+ * Every call on one GPU shares that GPU's array, and every partial is written before it
+ * is read, so nothing needs clearing between calls; but calls whose work overlaps in time
+ * on one GPU (different streams, or different host threads) race on the array and give
+ * undefined results. Other arguments, rules and errors as coda_gemm_rmsnorm_fwd. */
+int coda_gemm_rmsnorm_fwd_noalloc(const uint16_t* x, const uint16_t* w0, const uint16_t* z,
+                                  const uint16_t* gamma, const uint16_t* w1, int M, int K,
+                                  int D, int N1, float eps, uint16_t* h1, uint16_t* h2,
+                                  float* r, uint16_t* y, void* stream);
+
 /* Stage (1) of coda_gemm_rmsnorm_fwd alone (same arguments and outputs). */
 int coda_gemm_residual_rmsnorm_partials(const uint16_t* x, const uint16_t* w0,
                                         const uint16_t* z, const uint16_t* gamma, int M,

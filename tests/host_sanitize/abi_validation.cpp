@@ -77,6 +77,14 @@ int main() {
                                256, 256, 1e-5f, F<uint16_t>(6), F<uint16_t>(6), F<float>(8), F<float>(9),
                                F<uint16_t>(10), nullptr) == CODA_ERR_ARG,
          "h1 == h2");
+  auto noalloc = [&](const std::vector<int>& a) {
+    return coda_gemm_rmsnorm_fwd_noalloc(F<uint16_t>(1), F<uint16_t>(2), F<uint16_t>(3), F<uint16_t>(4),
+                                         F<uint16_t>(5), a[0], a[1], a[2], a[3], 1e-5f, F<uint16_t>(6),
+                                         F<uint16_t>(7), F<float>(9), F<uint16_t>(10), nullptr);
+  };
+  sweep("coda_gemm_rmsnorm_fwd_noalloc", {256, 256, 256, 256}, noalloc);
+  EXPECT(noalloc({CODA_NOALLOC_SCRATCH_FLOATS + 1, 256, 256, 256}) == CODA_ERR_WORKSPACE, "noalloc capacity");
+  EXPECT(noalloc({256, 256, 256, 256}) == CODA_ERR_HIP, "noalloc without a device");
   sweep("coda_gemm_residual_rmsnorm_partials", {256, 256, 256}, [&](const std::vector<int>& a) {
     return coda_gemm_residual_rmsnorm_partials(b, F<uint16_t>(2), F<uint16_t>(3), F<uint16_t>(4), a[0], a[1], a[2],
                                                F<uint16_t>(6), F<uint16_t>(7), F<float>(8), nullptr);

@@ -305,6 +305,17 @@ def test_overlapping_buffers_are_rejected(raw):
     assert raw.coda_rope_tables(g, g + 4 * 8, 16, 128, 1e4, None) == ARG
 
 
+def test_noalloc_capacity_and_arguments(L):
+    def call(M=256, K=256, D=256, N1=256, eps=1e-5, x=P, h1=P, r=P):
+        return L.coda_gemm_rmsnorm_fwd_noalloc(x, P, P, P, P, M, K, D, N1, eps, h1, P, r, P, None)
+    cap = coda.NOALLOC_SCRATCH_FLOATS
+    assert call(M=cap // 16 + 1, D=4096) == WS     # 16 partials per row past the array
+    assert call(M=cap + 1, D=256) == WS
+    assert call(M=-1) == SHAPE and call(K=12) == SHAPE and call(N1=0) == SHAPE
+    assert call(eps=-1.0) == ARG
+    assert call(M=0, x=None, h1=None, r=None) == OK
+
+
 def test_library_matches_its_sources(raw, tmp_path):
     """The loaded library was built from the sources next to it; a copy of those sources
     with one edited file no longer matches, and the check refuses it."""

@@ -25,6 +25,8 @@ __all__ = [
     "ROWSTAT_MEAN",
     "num_partials",
     "coda_gemm_rmsnorm_fwd",
+    "coda_gemm_rmsnorm_fwd_noalloc",
+    "NOALLOC_SCRATCH_FLOATS",
     "coda_gemm_residual_rmsnorm_partials",
     "coda_gemm_rowscale",
     "coda_rowstat_reduce",
@@ -54,6 +56,7 @@ __all__ = [
 PARTIAL_TILE_N = 256
 ROWSTAT_RSQRT_MEAN_EPS = 0
 ROWSTAT_MEAN = 1
+NOALLOC_SCRATCH_FLOATS = 1 << 20
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -66,6 +69,7 @@ SIGNATURES = {
     "coda_abi_version": [],
     "coda_rowstat_num_partials": [_I, ctypes.POINTER(_I)],
     "coda_gemm_rmsnorm_fwd": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P],
+    "coda_gemm_rmsnorm_fwd_noalloc": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P],
     "coda_gemm_residual_rmsnorm_partials": [_P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
     "coda_gemm_rowscale": [_P, _P, _P, _I, _I, _I, _P, _P],
     "coda_rowstat_reduce": [_P, _I, _I, _I, _F, _I, _P, _P],
@@ -207,6 +211,21 @@ def coda_gemm_rmsnorm_fwd(x, w0, z, gamma, w1, eps, h1=None, h2=None, partials=N
           _bf16(w1, "w1"), M, K, D, N1, float(eps), _bf16(h1, "h1"), _bf16(h2, "h2"),
           _f32(partials, "partials"), _f32(r, "r"), _bf16(y, "y"), _stream(stream))
     return h1, h2, partials, r, y
+
+
+def coda_gemm_rmsnorm_fwd_noalloc(x, w0, z, gamma, w1, eps, h1, h2, r, y, stream=None):
+    """coda_gemm_rmsnorm_fwd with the row partials in the library's fixed device array:
+    nothing is allocated, by the library or here, so every output is the caller's."""
+    M, K = x.shape
+    D = w0.shape[1]
+    N1 = w1.shape[1]
+    if (w0.shape[0] != K or z.shape != (M, D) or gamma.shape != (D,) or w1.shape[0] != D or h1.shape != (M, D)
+            or h2.shape != (M, D) or r.shape != (M,) or y.shape != (M, N1)):
+        raise ValueError("coda_gemm_rmsnorm_fwd_noalloc: inconsistent shapes")
+    _call("coda_gemm_rmsnorm_fwd_noalloc", _bf16(x, "x"), _bf16(w0, "w0"), _bf16(z, "z"), _bf16(gamma, "gamma"),
+          _bf16(w1, "w1"), M, K, D, N1, float(eps), _bf16(h1, "h1"), _bf16(h2, "h2"), _f32(r, "r"), _bf16(y, "y"),
+          _stream(stream))
+    return h1, h2, r, y
 
 
 def coda_gemm_residual_rmsnorm_partials(x, w0, z, gamma, h1=None, h2=None, partials=None, stream=None):

@@ -1,4 +1,6 @@
 // C-ABI entry points of the fused GEMM-epilogue programs (declared in coda.h).
+#include <mutex>
+
 #include "coda_abi.hpp"
 #include "coda_gemm.hpp"
 
@@ -170,6 +172,56 @@ int coda_gemm_rmsnorm_fwd(const uint16_t* x, const uint16_t* w0, const uint16_t*
   const hipStream_t s = as_stream(stream);
   CODA_TRY(run_gemm1(x, w0, z, gamma, M, K, D, h1, h2, partials, s));
   CODA_TRY(coda_rowstat_reduce_impl(partials, M, (D + kBN - 1) / kBN, D, eps, CODA_ROWSTAT_RSQRT_MEAN_EPS, r, s));
+  return run_gemm2(h2, w1, r, M, D, N1, y, s);
+}
+
+// ----------------------------------------------------------- forward without allocation
+// The row-partial workspace of the forward rewrite in a fixed device array, for callers
+// that cannot allocate device memory. Each GPU the library runs on holds its own copy of
+// the array (at its own address) until the process ends. In host code `scratch` names a
+// host-side stand-in, never the device memory: kernels and copies get the address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) float scratch[CODA_NOALLOC_SCRATCH_FLOATS];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices];  // device address of `scratch`, per device
+
+int scratch_on_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CODA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CODA_ERR_HIP;
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return CODA_OK;
+}
+}  // namespace
+
+int coda_gemm_rmsnorm_fwd_noalloc(const uint16_t* x, const uint16_t* w0, const uint16_t* z, const uint16_t* gamma,
+                                  const uint16_t* w1, int M, int K, int D, int N1, float eps, uint16_t* h1,
+                                  uint16_t* h2, float* r, uint16_t* y, void* stream) {
+  if (!(eps >= 0.0f) || !(eps < __builtin_huge_valf())) return CODA_ERR_ARG;
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(K));
+  CODA_TRY(check_depth_or_width(D));
+  CODA_TRY(check_depth_or_width(N1));
+  const int nb = (D + kBN - 1) / kBN;
+  if ((long long)M * nb > CODA_NOALLOC_SCRATCH_FLOATS) return CODA_ERR_WORKSPACE;
+  if (M == 0) return CODA_OK;
+  float* partials = nullptr;
+  CODA_TRY(scratch_on_current_device(&partials));
+  CODA_TRY(check_gemm1(x, w0, z, gamma, M, K, D, h1, h2, partials));
+  CODA_TRY(check_gemm2(h2, w1, r, M, D, N1, y));
+  CODA_TRY(disjoint_fwd(x, w0, z, gamma, w1, M, K, D, N1, h1, h2, partials, r, y));
+  // every partial the reduction reads is written by GEMM1 first: nothing to clear
+  const hipStream_t s = as_stream(stream);
+  CODA_TRY(run_gemm1(x, w0, z, gamma, M, K, D, h1, h2, partials, s));
+  CODA_TRY(coda_rowstat_reduce_impl(partials, M, nb, D, eps, CODA_ROWSTAT_RSQRT_MEAN_EPS, r, s));
   return run_gemm2(h2, w1, r, M, D, N1, y, s);
 }
 
