@@ -473,6 +473,45 @@ def aux_reduce_sweep(coda, torch, reps):
     return res
 
 
+# ------------------------------------------------------- GEMM1 against hipBLASLt (counters)
+def gemm1_compare(coda, torch, reps):
+    """GEMM1 of the Llama-shaped forward three ways, for counter runs: the fused kernel
+    (residual, gamma, row partials), the same main loop with a plain store, and
+    hipBLASLt's plain GEMM (torch.matmul); then the plain kernel on 1/32 .. all of the
+    token rows, i.e. 16 .. 512 concurrent tiles, to see how one tile's time depends on
+    how many CUs run at once (at most one tile per CU up to 256 tiles)."""
+    wl_shape = dict(M=8192, K=14336, D=4096)
+    M, K, D = wl_shape["M"], wl_shape["K"], wl_shape["D"]
+    g = torch.Generator(device="cuda").manual_seed(3)
+    x = (torch.randn((M, K), generator=g, device="cuda")).to(torch.bfloat16)
+    w0 = (torch.randn((K, D), generator=g, device="cuda") * K ** -0.5).to(torch.bfloat16)
+    z = torch.randn((M, D), generator=g, device="cuda").to(torch.bfloat16)
+    gam = (1 + 0.1 * torch.randn((D,), generator=g, device="cuda")).to(torch.bfloat16)
+    h1, h2 = torch.empty_like(z), torch.empty_like(z)
+    part = torch.empty((M, coda.num_partials(D)), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(z)
+    fns = {"fused_gemm1": lambda: coda.coda_gemm_residual_rmsnorm_partials(x, w0, z, gam, h1=h1, h2=h2,
+                                                                          partials=part),
+           "plain_gemm1": lambda: coda.coda_baseline_gemm(x, w0, c=out),
+           "hipblaslt_gemm1": lambda: torch.matmul(x, w0, out=out)}
+    fl = 2.0 * M * K * D
+    settle = time.time() + 1.0  # clock settle before any timing
+    while time.time() < settle:
+        fns["plain_gemm1"]()
+        torch.cuda.synchronize()
+    t = time_interleaved(fns, max(reps, 8))
+    res = {name: dict(us=round(ms * 1e3, 1), tflops=round(fl / (ms * 1e-3) / 1e12, 1)) for name, ms in t.items()}
+    sweep = {}
+    for m in (256, 512, 1024, 2048, 4096, 8192):
+        xs, os_ = x[:m], out[:m]
+        t = time_reps(lambda: coda.coda_baseline_gemm(xs, w0, c=os_), reps)
+        tiles = (m // 256) * (D // 256)
+        sweep[f"{tiles}_tiles"] = dict(M=m, us=round(t["median_ms"] * 1e3, 1),
+                                       tflops=round(2.0 * m * K * D / (t["median_ms"] * 1e-3) / 1e12, 1))
+    res["plain_gemm1_by_concurrent_tiles"] = sweep
+    return res
+
+
 # --------------------------------------------------------------------- CPU oracle leg
 def cpu_baseline(target_s: float):
     """The fp64 oracle, as it stands, on a row sample of the same workload (every op is
@@ -529,6 +568,8 @@ def main():
                     help="only run the plain 1 GiB copy kernel (reference for HBM traffic counters)")
     ap.add_argument("--aux-sweep-only", action="store_true",
                     help="only run the auxiliary row reduction's bandwidth sweep (for profiling it)")
+    ap.add_argument("--gemm1-compare", action="store_true",
+                    help="only run GEMM1 fused / plain / hipBLASLt and the concurrent-tile sweep (counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused GEMM-epilogue path is row-independent and "
@@ -551,6 +592,9 @@ def main():
         return
     if args.aux_sweep_only:
         print(json.dumps({"aux_reduce_sweep": aux_reduce_sweep(coda, torch, args.reps)}), flush=True)
+        return
+    if args.gemm1_compare:
+        print(json.dumps({"gemm1_compare": gemm1_compare(coda, torch, args.reps)}), flush=True)
         return
     aux_cool = None if args.headline_only else aux_reduce_sweep(coda, torch, args.reps)
     torch.cuda.empty_cache()
