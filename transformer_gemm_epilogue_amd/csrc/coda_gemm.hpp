@@ -40,7 +40,8 @@
 //   the DMA of S+3 into the slot of S-2 | wait for this thread's loads of S+1, barrier
 //   (S+1 complete for every wave, S-1 no longer read by anyone) | the 16 MFMAs on token
 //   blocks 4..7 of S, interleaved one for one with the reads of W and X blocks 0..3 of
-//   S+1, and, on odd steps, the X halves of the DMA of S+3 and S+4 (slots of S-2, S-1).
+//   S+1, and, on odd steps, the X halves of the DMA of S+3 and S+4 (slots of S-2, S-1)
+//   behind every other one of the last eight of those MFMAs.
 // X loads go in pairs because a 32-deep X row is 64 bytes, half of a 128-byte vector-L1
 // line: issued back to back, the loads of steps 2p and 2p+1 share each line, where
 // loads a step apart fetched every line from L2 twice (measured on MI355X: L1 -> L2
@@ -498,10 +499,18 @@ __device__ __forceinline__ void mainloop_body(const ML& ml, const TileSrc& cur, 
     for (int r = 0; r < kMfmaH; ++r) {
       const int i = r / kH, j = kH + r % kH;
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-      // odd steps: X of kt+3 and kt+4 into the slots of kt-2 and kt-1 (free since the
-      // previous barrier and this one), the two halves of each row back to back
-      if (kOdd && r < 4) issue_at(lds.slot[(S + 3 + (r & 1)) % kStages], kt + 3 + (r & 1), r >> 1, kind);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      // odd steps: X of kt+3 and kt+4 into the slots of kt-2 and kt-1 (free since the
+      // previous barrier and this one), the two halves of each row back to back, one
+      // load behind every other MFMA of the run's second half. A DMA issue stalls its wave
+      // while the texture unit's command queue is full; issued late in the run the stall
+      // falls where the wave has MFMAs queued and a wait ahead, not in front of 12 of them
+      // (measured on MI355X against the loads behind the run's first four MFMAs,
+      // interleaved, bit-identical: 2-4% faster on GEMM1, GEMM2, 8192^3 and the NK backward)
+      if (kOdd && r >= kMfmaH - 8 && (r & 1) == 0) {
+        const int q = (r - (kMfmaH - 8)) >> 1;
+        issue_at(lds.slot[(S + 3 + (q & 1)) % kStages], kt + 3 + (q & 1), q >> 1, kind);
+      }
       if (r < kH) {
         b[r] = ml.read_x(next, r);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
