@@ -506,9 +506,14 @@ __device__ __forceinline__ void mainloop_body(const ML& ml, const TileSrc& cur, 
       // while the texture unit's command queue is full; issued late in the run the stall
       // falls where the wave has MFMAs queued and a wait ahead, not in front of 12 of them
       // (measured on MI355X against the loads behind the run's first four MFMAs,
-      // interleaved, bit-identical: 2-4% faster on GEMM1, GEMM2, 8192^3 and the NK backward)
-      if (kOdd && r >= kMfmaH - 8 && (r & 1) == 0) {
-        const int q = (r - (kMfmaH - 8)) >> 1;
+      // interleaved, bit-identical: 2-4% faster on GEMM1, GEMM2, 8192^3 and the NK backward).
+      // The persistent kernel keeps them behind the first four MFMAs: it holds the next
+      // tile's sources across its loop, and with the loads that late the loop needs more
+      // than its 256 registers (203 VGPRs spilled). Either way the loads come after the
+      // step's barrier and before the next wait, so the ring's wait counts hold.
+      constexpr int kX0 = kPersist ? 0 : kMfmaH - 8, kXStride = kPersist ? 1 : 2;
+      if (kOdd && r >= kX0 && (r - kX0) % kXStride == 0 && (r - kX0) / kXStride < 4) {
+        const int q = (r - kX0) / kXStride;
         issue_at(lds.slot[(S + 3 + (q & 1)) % kStages], kt + 3 + (q & 1), q >> 1, kind);
       }
       if (r < kH) {
