@@ -512,6 +512,37 @@ def gemm1_compare(coda, torch, reps):
     return res
 
 
+def schedule_probe(coda, torch, steps=20000):
+    """The main loop's LDS reads and MFMAs alone (coda_baseline_schedule_probe: a fixed LDS
+    image of hashed values, no DMA): cycles per 32-deep step of a workgroup (its slowest
+    wave; median over workgroups), on one workgroup and on 256 (one per CU), for each
+    kind; 1024 cycles per step is the nominal MFMA time (64 MFMAs of 16 cycles per SIMD
+    at the published peak)."""
+    kinds = {0: "reads_kn_mfma_barrier", 1: "reads_kn_mfma_no_barrier", 2: "reads_nk_mfma_barrier",
+             3: "reads_kn_only", 4: "mfma_only"}
+    res = {}
+    for grid in (1, 256):
+        for kind, name in list(kinds.items()) + [(4, "mfma_only_constant_image"), (0, "reads_kn_mfma_barrier_constant_image")]:
+            seed = 0 if name.endswith("constant_image") else 11
+            out = torch.empty((grid * 512,), dtype=torch.float32, device="cuda")
+            cyc = torch.empty((grid * 8,), dtype=torch.int64, device="cuda")
+            coda.coda_baseline_schedule_probe(kind, 50, grid, seed=seed, out=out, cycles=cyc)  # warm-up
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            coda.coda_baseline_schedule_probe(kind, steps, grid, seed=seed, out=out, cycles=cyc)
+            e1.record()
+            torch.cuda.synchronize()
+            # a workgroup's time is its slowest wave's (without the per-step barrier the
+            # two waves of a SIMD drift apart, and one may finish long before the other)
+            c = cyc.cpu().numpy().astype(np.float64).reshape(grid, 8).max(axis=1)
+            per = float(np.median(c)) / steps
+            res[f"{name}_grid{grid}"] = dict(cycles_per_step=round(per, 1),
+                                             mfma_occupancy=round(1024.0 / per, 3) if kind != 3 else None,
+                                             clock_ghz=round(float(c.max()) / (e0.elapsed_time(e1) * 1e6), 2))
+    return res
+
+
 # --------------------------------------------------------------------- CPU oracle leg
 def cpu_baseline(target_s: float):
     """The fp64 oracle, as it stands, on a row sample of the same workload (every op is
@@ -570,6 +601,8 @@ def main():
                     help="only run the auxiliary row reduction's bandwidth sweep (for profiling it)")
     ap.add_argument("--gemm1-compare", action="store_true",
                     help="only run GEMM1 fused / plain / hipBLASLt and the concurrent-tile sweep (counter runs)")
+    ap.add_argument("--schedule-probe", action="store_true",
+                    help="only run the main loop's reads and MFMAs on a fixed LDS image (no DMA)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused GEMM-epilogue path is row-independent and "
@@ -595,6 +628,9 @@ def main():
         return
     if args.gemm1_compare:
         print(json.dumps({"gemm1_compare": gemm1_compare(coda, torch, args.reps)}), flush=True)
+        return
+    if args.schedule_probe:
+        print(json.dumps({"schedule_probe": schedule_probe(coda, torch)}), flush=True)
         return
     aux_cool = None if args.headline_only else aux_reduce_sweep(coda, torch, args.reps)
     torch.cuda.empty_cache()

@@ -327,6 +327,23 @@ int coda_baseline_copy(const void* src, void* dst, int64_t bytes, void* stream);
  * nominal peak). Rules: n_frag, iters >= 1; 1 <= grid <= 65535; operands 16-byte aligned. */
 int coda_baseline_mfma_loop(const uint16_t* operands, int n_frag, int iters, int grid,
                             float* out, void* stream);
+/* Measurement probe (no step of the method): the GEMM main loop's per-step LDS operand
+ * reads and MFMAs, in its order and with its priorities, on an LDS image written once
+ * (seed 0: every bf16 element = bf16(fill); otherwise bits hashed from (seed, position):
+ * values +-[1/4, 1/2) with random signs and mantissas, as the MFMA's rate depends on
+ * the operand bits); no DMA and nothing rewritten. `grid` workgroups of
+ * 512 threads run `steps` 32-deep steps each. kind 0: KN-W reads (two transposed 8-byte
+ * reads per W block), one workgroup barrier per step as in the GEMM; 1: the same without
+ * the barrier; 2: NK-W reads (one 16-byte read per W block) with the barrier; 3: the
+ * reads of kind 0 alone, no MFMAs; 4: the MFMAs of kind 0 alone, on operands read once
+ * before the loop, no barrier. out [grid * 512] fp32: kinds 0-2 and 4 each thread's
+ * accumulator sum (seed 0: = 128 * 32 * fill^2 * steps up to rounding; every workgroup
+ * computes the same values); kind 3 the bit pattern of
+ * the 32-bit wrapping sum of every word the thread read (48 words per step). cycles
+ * [grid * 8] int64: each wave's core-clock cycles over the steps (s_memtime). Rules:
+ * 0 <= kind <= 4, steps >= 1, 1 <= grid <= 65535; out 4-, cycles 8-byte aligned. */
+int coda_baseline_schedule_probe(int kind, int steps, int grid, float fill, uint32_t seed,
+                                 float* out, long long* cycles, void* stream);
 
 #ifdef __cplusplus
 }

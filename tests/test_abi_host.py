@@ -329,3 +329,18 @@ def test_library_matches_its_sources(raw, tmp_path):
     src.write_text(src.read_text() + "\n// edited\n")
     with pytest.raises(coda.StaleLibraryError):
         coda.check_source_hash(raw, str(tmp_path))
+
+
+def test_schedule_probe_validation(L, raw):
+    f = ctypes.c_float(0.125)
+    assert L.coda_baseline_schedule_probe(-1, 5, 1, f, 0, P, P + 16, None) == SHAPE
+    assert L.coda_baseline_schedule_probe(5, 5, 1, f, 0, P, P + 16, None) == SHAPE
+    assert L.coda_baseline_schedule_probe(0, 0, 1, f, 0, P, P + 16, None) == SHAPE
+    assert L.coda_baseline_schedule_probe(0, 5, 0, f, 0, P, P + 16, None) == SHAPE
+    assert L.coda_baseline_schedule_probe(0, 5, 65536, f, 0, P, P + 16, None) == SHAPE
+    assert L.coda_baseline_schedule_probe(0, 5, 1, f, 0, None, P + 16, None) == NULL
+    assert L.coda_baseline_schedule_probe(0, 5, 1, f, 0, P, None, None) == NULL
+    assert L.coda_baseline_schedule_probe(0, 5, 1, f, 0, P + 2, P + 16, None) == ALIGN
+    assert L.coda_baseline_schedule_probe(0, 5, 1, f, 0, P, P + 20, None) == ALIGN
+    # out [512] fp32 and cycles [8] int64 overlapping
+    assert raw.coda_baseline_schedule_probe(0, 5, 1, f, 0, P, P + 64, None) == ARG

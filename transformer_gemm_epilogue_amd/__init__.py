@@ -51,6 +51,7 @@ __all__ = [
     "coda_baseline_rowdot",
     "coda_baseline_copy",
     "coda_baseline_mfma_loop",
+    "coda_baseline_schedule_probe",
 ]
 
 PARTIAL_TILE_N = 256
@@ -94,6 +95,7 @@ SIGNATURES = {
     "coda_baseline_rowdot": [_P, _P, _I, _I, _P, _P],
     "coda_baseline_copy": [_P, _P, _I64, _P],
     "coda_baseline_mfma_loop": [_P, _I, _I, _I, _P, _P],
+    "coda_baseline_schedule_probe": [_I, _I, _I, _F, ctypes.c_uint32, _P, _P, _P],
 }
 
 
@@ -515,3 +517,19 @@ def coda_baseline_mfma_loop(operands, iters, grid, out=None, stream=None):
     _call("coda_baseline_mfma_loop", _bf16(operands, "operands"), operands.numel() // 8, int(iters), int(grid),
           _f32(out, "out"), _stream(stream))
     return out
+
+
+def coda_baseline_schedule_probe(kind, steps, grid, fill=0.125, seed=0, out=None, cycles=None, device="cuda",
+                                 stream=None):
+    """The main loop's LDS reads and MFMAs on a fixed LDS image (every element `fill`, or
+    hashed bits when seed != 0; kind 0: KN-W reads with the per-step barrier, 1: without
+    it, 2: NK-W reads, 3: the reads of kind 0 alone, 4: its MFMAs alone);
+    returns (out [grid * 512] fp32, cycles [grid * 8] int64 per wave over `steps` steps)."""
+    torch = _torch()
+    out = torch.empty((grid * 512,), dtype=torch.float32, device=device) if out is None else out
+    cycles = torch.empty((grid * 8,), dtype=torch.int64, device=device) if cycles is None else cycles
+    if out.numel() < grid * 512 or cycles.numel() < grid * 8:
+        raise ValueError("coda_baseline_schedule_probe: out or cycles too small for the grid")
+    _call("coda_baseline_schedule_probe", int(kind), int(steps), int(grid), float(fill), int(seed), _f32(out, "out"),
+          _dev(cycles, torch.int64, "cycles"), _stream(stream))
+    return out, cycles

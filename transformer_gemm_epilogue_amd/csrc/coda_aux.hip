@@ -1,9 +1,12 @@
-// Auxiliary kernels: the row reduction over tile partials, the RoPE table builder, and
-// the unfused baseline operators (kept for measurement and the numerics comparison).
+// Auxiliary kernels: the row reduction over tile partials, the RoPE table builder, the
+// unfused baseline operators (kept for measurement and the numerics comparison), and two
+// measurement probes (a register-only MFMA loop and the GEMM main loop's reads and MFMAs
+// on a fixed LDS image).
 #include <algorithm>
 
 #include "coda_abi.hpp"
 #include "coda_common.hpp"
+#include "coda_gemm.hpp"
 
 using namespace coda;
 
@@ -413,6 +416,153 @@ int coda_baseline_mfma_loop(const uint16_t* operands, int n_frag, int iters, int
   CODA_TRY(check_disjoint({f32_span(out, (long long)grid * 512)}, {bf16_span(operands, n_frag, 8)}));
   hipLaunchKernelGGL(mfma_loop_kernel, dim3(grid), dim3(512), 0, as_stream(stream), (const bf16x8_t*)operands, n_frag,
                      iters, out);
+  return launch_status();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Main-loop schedule probe, a measurement kernel (no step of the method): the GEMM main
+// loop's per-step LDS operand reads and MFMAs, with its read order, priorities and
+// scheduling pins, on an LDS image written once before the timed loop (seed 0: every bf16
+// element equal to `fill`; otherwise element bits from a hash of (seed, position), values
+// +-[1/4, 1/2) with random signs and mantissas, since the MFMA's rate depends on the
+// operand bits; nothing rewrites the image, so there is no DMA and no hazard). Kinds:
+//   0  KN-W reads (two transposed 8-byte reads per W block), the per-step barrier
+//   1  the same without the barrier
+//   2  NK-W reads (one 16-byte read per W block), the per-step barrier
+//   3  the reads of kind 0 alone, no MFMAs: every 32-bit word read is added (mod 2^32)
+//   4  the MFMAs of kind 0 alone, on operands read once before the loop
+// out[thread]: kinds 0-2 and 4 the sum of the thread's 128 accumulator values; kind 3 the
+// bits of its word sum. Each wave records the core-clock cycles of its `steps` steps
+// (s_memtime) in cycles[].
+template <int kKind>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void schedule_probe_kernel(float fill, uint32_t seed, int steps, float* __restrict__ out,
+                           long long* __restrict__ cycles) {
+  constexpr bool kKN = kKind != 2;
+  constexpr bool kBarrier = kKind != 1 && kKind != 4;
+  constexpr bool kMfma = kKind != 3;
+  constexpr bool kReads = kKind != 4;
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kSlotBytes];
+  const uint32_t fill2 = f32_to_bf16(fill) * 0x10001u;
+  for (int i = threadIdx.x; i < kStages * kSlotBytes / 4; i += kThreads) {
+    uint32_t h = (uint32_t)i * 0x9E3779B1u ^ seed * 0x85EBCA77u;  // multiplicative hash and mix
+    h ^= h >> 15;
+    h *= 0x2C1B3C6Du;
+    h ^= h >> 12;
+    h *= 0x297A2D39u;
+    h ^= h >> 15;
+    ((uint32_t*)smem)[i] = seed ? (h & 0x807F807Fu) | 0x3E803E80u : fill2;
+  }
+  __syncthreads();
+  const LdsRing lds = make_ring(smem, 0, 0, threadIdx.x);
+  const GemmProblem p{nullptr, nullptr, kBM, kBN, kBK, 0};  // only the LDS offsets are used
+  Mainloop<kKN> ml;
+  ml.init(p, threadIdx.x);
+  AccTile acc;
+#pragma unroll
+  for (int i = 0; i < kNI; ++i)
+#pragma unroll
+    for (int j = 0; j < kMJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint32_t rsum = 0u;
+  constexpr int kH = kMJ / 2;
+  constexpr int kMfmaH = kNI * kH;
+  bf16x8_t a[kNI], b[kMJ];
+#pragma unroll
+  for (int i = 0; i < kNI; ++i) a[i] = ml.read_w(lds.slot[0], i);
+#pragma unroll
+  for (int j = 0; j < (kReads ? kH : kMJ); ++j) b[j] = ml.read_x(lds.slot[0], j);
+  auto use = [&](int i, int j) {
+    if constexpr (kMfma)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+  auto fold = [&](const bf16x8_t& v) {
+    if constexpr (!kMfma) {
+      const u32x4_t w = __builtin_bit_cast(u32x4_t, v);
+      rsum += (w.x + w.y) + (w.z + w.w);
+    }
+  };
+  __syncthreads();
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  auto step = [&](const int S) {
+#pragma unroll
+    for (int j = kH; j < kMJ; ++j) {
+      if constexpr (kReads) b[j] = ml.read_x(lds.slot[S], j);
+      fold(b[j]);
+    }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < kNI; ++i)
+#pragma unroll
+      for (int j = 0; j < kH; ++j) use(i, j);
+    __builtin_amdgcn_sched_group_barrier(0x100, kH, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfmaH, 0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kBarrier) __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const char* next = lds.slot[(S + 1) % kStages];
+#pragma unroll
+    for (int r = 0; r < kMfmaH; ++r) {
+      const int i = r / kH, j = kH + r % kH;
+      use(i, j);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if (kReads && r < kH) {
+        b[r] = ml.read_x(next, r);
+        fold(b[r]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
+      if (kReads && r % kH == kH - 1) {
+        a[i] = ml.read_w(next, i);
+        fold(a[i]);
+        __builtin_amdgcn_sched_group_barrier(0x100, kKN ? 2 : 1, 1);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int s = 0;
+  for (; s + kStages <= steps; s += kStages) {
+    step(0);
+    step(1);
+    step(2);
+    step(3);
+    step(4);
+  }
+  if (s < steps) step(0);
+  if (s + 1 < steps) step(1);
+  if (s + 2 < steps) step(2);
+  if (s + 3 < steps) step(3);
+  const long long t1 = __builtin_amdgcn_s_memtime();
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNI; ++i)
+#pragma unroll
+    for (int j = 0; j < kMJ; ++j) sum += (acc[i][j][0] + acc[i][j][1]) + (acc[i][j][2] + acc[i][j][3]);
+  out[(size_t)blockIdx.x * kThreads + threadIdx.x] = kMfma ? sum : __uint_as_float(rsum);
+  if ((threadIdx.x & 63) == 0) cycles[(size_t)blockIdx.x * kWaves + (threadIdx.x >> 6)] = t1 - t0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int coda_baseline_schedule_probe(int kind, int steps, int grid, float fill, uint32_t seed, float* out,
+                                 long long* cycles, void* stream) {
+  if (kind < 0 || kind > 4 || steps < 1 || grid < 1 || grid > 65535) return CODA_ERR_SHAPE;
+  CODA_NONNULL(out);
+  CODA_NONNULL(cycles);
+  if (!aligned(out, 4) || !aligned(cycles, 8)) return CODA_ERR_ALIGN;
+  CODA_TRY(check_disjoint({f32_span(out, (long long)grid * kThreads), Span{cycles, 8ull * grid * kWaves}}, {}));
+  const hipStream_t st = as_stream(stream);
+  switch (kind) {
+    case 0: hipLaunchKernelGGL(schedule_probe_kernel<0>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
+    case 1: hipLaunchKernelGGL(schedule_probe_kernel<1>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
+    case 2: hipLaunchKernelGGL(schedule_probe_kernel<2>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
+    case 3: hipLaunchKernelGGL(schedule_probe_kernel<3>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
+    default: hipLaunchKernelGGL(schedule_probe_kernel<4>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
+  }
   return launch_status();
 }
 
