@@ -244,7 +244,18 @@ def unfused_fwd(coda, torch, b, reps):
     t_norm = time_reps(lambda: coda.coda_baseline_residual_rmsnorm(h0, z, g, eps, h1=h1, r=r, o=o), reps)
     t_mm1 = time_reps(lambda: torch.matmul(x, w0), reps)
     t_mm2 = time_reps(lambda: torch.matmul(o, w1), reps)
-    return dict(fused_entry_point_ms=t["fused"],
+    # GEMM1 alone, three ways in one interleaved run: the fused kernel (residual, gamma, row
+    # partials), the same main loop with a plain store, and hipBLASLt's plain GEMM
+    g1 = time_interleaved({
+        "fused": lambda: coda.coda_gemm_residual_rmsnorm_partials(x, w0, z, g, h1=b["h1"], h2=b["h2"],
+                                                                  partials=b["part"]),
+        "plain": lambda: coda.coda_baseline_gemm(x, w0, c=h0),
+        "hipblaslt": lambda: torch.matmul(x, w0, out=h0)}, 2 * reps)
+    fl1 = 2.0 * M * x.shape[1] * D
+    return dict(gemm1_interleaved={k: dict(us=round(v * 1e3, 1), tflops=round(fl1 / (v * 1e-3) / 1e12, 1))
+                                   for k, v in g1.items()},
+                gemm1_fused_vs_hipblaslt_plain=round(g1["hipblaslt"] / g1["fused"], 3),
+                fused_entry_point_ms=t["fused"],
                 same_mainloop_plus_separate_kernels_ms=t["ours"],
                 torch_hipblaslt_eager_ms=t["torch"],
                 separate_residual_rmsnorm_kernel_us=round(t_norm["median_ms"] * 1e3, 2),
