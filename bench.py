@@ -264,6 +264,36 @@ def unfused_fwd(coda, torch, b, reps):
                 hipblaslt_gemm2_tflops=round(2 * M * D * w1.shape[1] / (t_mm2["median_ms"] * 1e-3) / 1e12, 1))
 
 
+def shard_share(coda, torch, b, reps):
+    """The forward on one GPU's share of the headline workload under token sharding over
+    G GPUs (M/G rows; every step is row-independent, so a shard runs the same kernels with
+    no exchange), through coda_gemm_rmsnorm_fwd (one kernel per GEMM) and through
+    coda_gemm_rmsnorm_fwd_ws (split depth for GEMMs with fewer tiles than CUs), timed
+    interleaved. One GPU only: no multi-GPU figure is implied."""
+    x, w0, z, g, w1, eps = b["x"], b["w0"], b["z"], b["g"], b["w1"], b["eps"]
+    M, D = b["h1"].shape
+    K, N1 = x.shape[1], w1.shape[1]
+    fns, ws = {}, {}
+    for G in (1, 2, 4, 8):
+        m = M // G
+        outs = dict(h1=b["h1"][:m], h2=b["h2"][:m], partials=b["part"][:m], r=b["r"][:m], y=b["y"][:m])
+        fns[(G, "one_kernel")] = (lambda m=m, outs=outs: coda.coda_gemm_rmsnorm_fwd(x[:m], w0, z[:m], g, w1, eps,
+                                                                                 **outs))
+        need = coda.coda_gemm_rmsnorm_fwd_workspace_bytes(m, K, D, N1)
+        ws[G] = torch.empty((max(need, 16),), dtype=torch.uint8, device="cuda")
+        fns[(G, "split_depth")] = (lambda m=m, outs=outs, G=G: coda.coda_gemm_rmsnorm_fwd_ws(
+            x[:m], w0, z[:m], g, w1, eps, workspace=ws[G], **outs))
+    t = time_interleaved(fns, reps)
+    out = {}
+    for (G, how), ms in t.items():
+        m = M // G
+        fl = 2.0 * m * K * D + 2.0 * m * D * N1
+        out.setdefault(f"G{G}", dict(rows=m, workspace_bytes=coda.coda_gemm_rmsnorm_fwd_workspace_bytes(m, K, D, N1)))
+        out[f"G{G}"][how] = dict(ms=round(ms, 4), tflops=round(fl / (ms * 1e-3) / 1e12, 1))
+    del ws
+    return out
+
+
 # ------------------------------------------------------------------ other fused paths
 def path_record(t, fl):
     rec = dict(fused_us=round(t["fused"] * 1e3, 1), tflops=round(fl / (t["fused"] * 1e-3) / 1e12, 1),
@@ -614,6 +644,8 @@ def main():
                     help="only run GEMM1 fused / plain / hipBLASLt and the concurrent-tile sweep (counter runs)")
     ap.add_argument("--schedule-probe", action="store_true",
                     help="only run the main loop's reads and MFMAs on a fixed LDS image (no DMA)")
+    ap.add_argument("--shard-share", action="store_true",
+                    help="only run the headline and one GPU's share of it under token sharding (M/G rows)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused GEMM-epilogue path is row-independent and "
@@ -647,8 +679,12 @@ def main():
     torch.cuda.empty_cache()
     res, bufs = headline(args, coda, torch)
     log(f"headline: {res['value']} TFLOP/s, {res['ms_per_step']} ms/step")
+    if args.shard_share:
+        print(json.dumps({"one_gpu_share_of_token_shards": shard_share(coda, torch, bufs, args.reps)}), flush=True)
+        return
     if not args.headline_only:
         res["unfused_fwd"] = unfused_fwd(coda, torch, bufs, args.reps)
+        res["one_gpu_share_of_token_shards"] = shard_share(coda, torch, bufs, args.reps)
         u = res["unfused_fwd"]
         res["speedup_vs_unfused_same_mainloop"] = round(u["same_mainloop_plus_separate_kernels_ms"] / u["fused_entry_point_ms"], 3)
         res["speedup_vs_torch_hipblaslt"] = round(u["torch_hipblaslt_eager_ms"] / u["fused_entry_point_ms"], 3)

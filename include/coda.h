@@ -103,6 +103,31 @@ int coda_gemm_rmsnorm_fwd(const uint16_t* x, const uint16_t* w0, const uint16_t*
                           int N1, float eps, uint16_t* h1, uint16_t* h2, float* partials,
                           float* r, uint16_t* y, void* stream);
 
+/* coda_gemm_rmsnorm_fwd with a split-depth schedule for outputs with fewer 256 x 256
+ * tiles than the current device has compute units (small batches, one GPU's share of a
+ * token-sharded batch). The same steps (1)-(3), where a GEMM with too few tiles cuts
+ * each tile's depth into S equal slices, runs one workgroup per slice (fp32 partial
+ * tiles into `workspace`) and then one per tile that sums the S partials in slice order
+ * and runs the tile's epilogue, (1) or (3) above, on the sum. A GEMM with enough tiles
+ * runs as in coda_gemm_rmsnorm_fwd. Results are deterministic for a given shape and
+ * device; their fp32 rounding differs from coda_gemm_rmsnorm_fwd's by the order of the
+ * depth sum, within the same tolerance against exact arithmetic.
+ * workspace: caller-owned device memory of workspace_bytes bytes, 16-byte aligned, at
+ * least coda_gemm_rmsnorm_fwd_workspace_bytes(M, K, D, N1) (else CODA_ERR_WORKSPACE;
+ * may be NULL when that is 0); read and written by the call, overlapping no other
+ * argument (CODA_ERR_ARG). Calls that overlap in time must not share a workspace.
+ * Three to five launches on `stream`. Other arguments, rules and errors as
+ * coda_gemm_rmsnorm_fwd; a negative workspace_bytes is CODA_ERR_ARG. */
+int coda_gemm_rmsnorm_fwd_ws(const uint16_t* x, const uint16_t* w0, const uint16_t* z,
+                             const uint16_t* gamma, const uint16_t* w1, int M, int K, int D,
+                             int N1, float eps, uint16_t* h1, uint16_t* h2, float* partials,
+                             float* r, uint16_t* y, void* workspace, long long workspace_bytes,
+                             void* stream);
+/* Bytes of workspace coda_gemm_rmsnorm_fwd_ws needs on the current device (0 when no
+ * GEMM of the shape is split): 256 KiB per slice of every tile of the larger split GEMM.
+ * Shape rules as coda_gemm_rmsnorm_fwd; CODA_ERR_HIP if the device cannot be queried. */
+int coda_gemm_rmsnorm_fwd_workspace_bytes(int M, int K, int D, int N1, long long* bytes);
+
 /* Capacity, in fp32 values, of the fixed device array that coda_gemm_rmsnorm_fwd_noalloc
  * uses as its row-partial workspace (4 MiB per GPU). */
 #define CODA_NOALLOC_SCRATCH_FLOATS (1 << 20)

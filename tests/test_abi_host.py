@@ -344,3 +344,19 @@ def test_schedule_probe_validation(L, raw):
     assert L.coda_baseline_schedule_probe(0, 5, 1, f, 0, P, P + 20, None) == ALIGN
     # out [512] fp32 and cycles [8] int64 overlapping
     assert raw.coda_baseline_schedule_probe(0, 5, 1, f, 0, P, P + 64, None) == ARG
+
+
+def test_split_forward_validation(L):
+    out = ctypes.c_int64(-1)
+    assert L.coda_gemm_rmsnorm_fwd_workspace_bytes(8, 8, 8, 8, None) == NULL
+    assert L.coda_gemm_rmsnorm_fwd_workspace_bytes(-1, 8, 8, 8, ctypes.byref(out)) == SHAPE
+    assert L.coda_gemm_rmsnorm_fwd_workspace_bytes(8, 12, 8, 8, ctypes.byref(out)) == SHAPE
+    assert L.coda_gemm_rmsnorm_fwd_workspace_bytes(0, 8, 8, 8, ctypes.byref(out)) == OK and out.value == 0
+    f = ctypes.c_float(1e-5)
+    args = [P, P, P, P, P, 8, 8, 8, 8]
+    outs = [P, P, P, P, P]
+    assert L.coda_gemm_rmsnorm_fwd_ws(*args, ctypes.c_float(-1.0), *outs, P, 0, None) == ARG
+    assert L.coda_gemm_rmsnorm_fwd_ws(*args, f, *outs, P, -1, None) == ARG
+    assert L.coda_gemm_rmsnorm_fwd_ws(None, P, P, P, P, 8, 8, 8, 8, f, *outs, P, 0, None) == NULL
+    assert L.coda_gemm_rmsnorm_fwd_ws(P, P, P, P, P, 8, 12, 8, 8, f, *outs, P, 0, None) == SHAPE
+    assert L.coda_gemm_rmsnorm_fwd_ws(P, P, P, P, P, 0, 8, 8, 8, f, *outs, None, 0, None) == OK

@@ -26,6 +26,8 @@ __all__ = [
     "num_partials",
     "coda_gemm_rmsnorm_fwd",
     "coda_gemm_rmsnorm_fwd_noalloc",
+    "coda_gemm_rmsnorm_fwd_ws",
+    "coda_gemm_rmsnorm_fwd_workspace_bytes",
     "NOALLOC_SCRATCH_FLOATS",
     "coda_gemm_residual_rmsnorm_partials",
     "coda_gemm_rowscale",
@@ -71,6 +73,8 @@ SIGNATURES = {
     "coda_rowstat_num_partials": [_I, ctypes.POINTER(_I)],
     "coda_gemm_rmsnorm_fwd": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P],
     "coda_gemm_rmsnorm_fwd_noalloc": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P],
+    "coda_gemm_rmsnorm_fwd_ws": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _I64, _P],
+    "coda_gemm_rmsnorm_fwd_workspace_bytes": [_I, _I, _I, _I, ctypes.POINTER(_I64)],
     "coda_gemm_residual_rmsnorm_partials": [_P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
     "coda_gemm_rowscale": [_P, _P, _P, _I, _I, _I, _P, _P],
     "coda_rowstat_reduce": [_P, _I, _I, _I, _F, _I, _P, _P],
@@ -212,6 +216,39 @@ def coda_gemm_rmsnorm_fwd(x, w0, z, gamma, w1, eps, h1=None, h2=None, partials=N
     _call("coda_gemm_rmsnorm_fwd", _bf16(x, "x"), _bf16(w0, "w0"), _bf16(z, "z"), _bf16(gamma, "gamma"),
           _bf16(w1, "w1"), M, K, D, N1, float(eps), _bf16(h1, "h1"), _bf16(h2, "h2"),
           _f32(partials, "partials"), _f32(r, "r"), _bf16(y, "y"), _stream(stream))
+    return h1, h2, partials, r, y
+
+
+def coda_gemm_rmsnorm_fwd_workspace_bytes(M, K, D, N1):
+    """Bytes of workspace coda_gemm_rmsnorm_fwd_ws needs on the current device."""
+    out = ctypes.c_int64(0)
+    _call("coda_gemm_rmsnorm_fwd_workspace_bytes", int(M), int(K), int(D), int(N1), ctypes.byref(out))
+    return out.value
+
+
+def coda_gemm_rmsnorm_fwd_ws(x, w0, z, gamma, w1, eps, h1=None, h2=None, partials=None, r=None, y=None,
+                             workspace=None, stream=None):
+    """coda_gemm_rmsnorm_fwd with the split-depth schedule for GEMMs with fewer tiles than
+    CUs; `workspace` is a uint8 GPU tensor of at least coda_gemm_rmsnorm_fwd_workspace_bytes
+    bytes (allocated here when None). Returns (h1, h2, partials, r, y)."""
+    torch = _torch()
+    M, K = x.shape
+    D = w0.shape[1]
+    N1 = w1.shape[1]
+    if w0.shape[0] != K or z.shape != (M, D) or gamma.shape != (D,) or w1.shape[0] != D:
+        raise ValueError("coda_gemm_rmsnorm_fwd_ws: inconsistent shapes")
+    h1 = _empty((M, D), torch.bfloat16, x) if h1 is None else h1
+    h2 = _empty((M, D), torch.bfloat16, x) if h2 is None else h2
+    partials = _empty((M, num_partials(D)), torch.float32, x) if partials is None else partials
+    r = _empty((M,), torch.float32, x) if r is None else r
+    y = _empty((M, N1), torch.bfloat16, x) if y is None else y
+    if workspace is None:
+        need = coda_gemm_rmsnorm_fwd_workspace_bytes(M, K, D, N1)
+        workspace = _empty((max(need, 16),), torch.uint8, x)
+    ws = _dev(workspace, torch.uint8, "workspace")
+    _call("coda_gemm_rmsnorm_fwd_ws", _bf16(x, "x"), _bf16(w0, "w0"), _bf16(z, "z"), _bf16(gamma, "gamma"),
+          _bf16(w1, "w1"), M, K, D, N1, float(eps), _bf16(h1, "h1"), _bf16(h2, "h2"),
+          _f32(partials, "partials"), _f32(r, "r"), _bf16(y, "y"), ws, int(workspace.numel()), _stream(stream))
     return h1, h2, partials, r, y
 
 

@@ -3,6 +3,7 @@
 
 #include "coda_abi.hpp"
 #include "coda_gemm.hpp"
+#include "coda_splitk.hpp"
 
 using namespace coda;
 
@@ -24,16 +25,43 @@ int launch_gemm(const GemmProblem& p, const typename Epi::Args& ea, hipStream_t 
   return launch_status();
 }
 
+// Compute units of the current device.
+int device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || *cus < 1)
+    return CODA_ERR_HIP;
+  return CODA_OK;
+}
+
+// Split-depth schedule (coda_splitk.hpp) when the plan has more than one slice: the
+// slices' main loops, then the tiles' epilogues on the summed partials (two launches);
+// otherwise the one-kernel schedule. ws holds split_workspace_floats(M, N, sp) floats.
+template <bool kWKN, class Epi>
+int launch_gemm_split(const GemmProblem& p, const typename Epi::Args& ea, const SplitPlan& sp, float* ws,
+                      hipStream_t stream) {
+  if (sp.S <= 1) return launch_gemm<kWKN, Epi>(p, ea, stream);
+  const int T = gemm_grid(p.M, p.N);
+  const dim3 units((unsigned)(((T + 7) / 8) * 8 * sp.S));
+  f32x4_t* w4 = reinterpret_cast<f32x4_t*>(ws);
+  if (kWKN && kn_one_descriptor_fits(p.K, p.N))
+    hipLaunchKernelGGL((gemm_split_kernel<kWKN, kWKN>), units, dim3(kThreads), 0, stream, p, sp.S, sp.steps, w4);
+  else
+    hipLaunchKernelGGL((gemm_split_kernel<kWKN, false>), units, dim3(kThreads), 0, stream, p, sp.S, sp.steps, w4);
+  CODA_TRY(launch_status());
+  hipLaunchKernelGGL((split_epilogue_kernel<Epi>), dim3(T), dim3(kThreads), 0, stream, p, ea, sp.S,
+                     (const f32x4_t*)w4);
+  return launch_status();
+}
+
 // Persistent schedule: min(tiles, CUs of the current device) workgroups walk the tiles
 // (one workgroup fills a CU's LDS); below the minimum depth the per-tile kernel runs
 // instead. Both give bit-identical results.
 template <bool kWKN, class Epi>
 int launch_gemm_persistent(const GemmProblem& p, const typename Epi::Args& ea, hipStream_t stream) {
   if ((p.K + kBK - 1) / kBK < kPersistMinSteps) return launch_gemm<kWKN, Epi>(p, ea, stream);
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                               hipSuccess || cus < 1)
-    return CODA_ERR_HIP;
+  int cus = 0;
+  CODA_TRY(device_cus(&cus));
   const int tiles = gemm_grid(p.M, p.N);
   const int grid = tiles < cus ? tiles : cus;
   hipLaunchKernelGGL((gemm_persistent_kernel<kWKN, Epi>), dim3(grid), dim3(kThreads), 0, stream, p, ea);
@@ -173,6 +201,56 @@ int coda_gemm_rmsnorm_fwd(const uint16_t* x, const uint16_t* w0, const uint16_t*
   CODA_TRY(run_gemm1(x, w0, z, gamma, M, K, D, h1, h2, partials, s));
   CODA_TRY(coda_rowstat_reduce_impl(partials, M, (D + kBN - 1) / kBN, D, eps, CODA_ROWSTAT_RSQRT_MEAN_EPS, r, s));
   return run_gemm2(h2, w1, r, M, D, N1, y, s);
+}
+
+// ----------------------------------------------------- forward with the split-depth schedule
+int coda_gemm_rmsnorm_fwd_workspace_bytes(int M, int K, int D, int N1, long long* bytes) {
+  CODA_NONNULL(bytes);
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(K));
+  CODA_TRY(check_depth_or_width(D));
+  CODA_TRY(check_depth_or_width(N1));
+  *bytes = 0;
+  if (M == 0) return CODA_OK;
+  int cus = 0;
+  CODA_TRY(device_cus(&cus));
+  const long long f1 = split_workspace_floats(M, D, split_plan(M, D, K, cus));
+  const long long f2 = split_workspace_floats(M, N1, split_plan(M, N1, D, cus));
+  *bytes = 4 * std::max(f1, f2);
+  return CODA_OK;
+}
+
+int coda_gemm_rmsnorm_fwd_ws(const uint16_t* x, const uint16_t* w0, const uint16_t* z, const uint16_t* gamma,
+                             const uint16_t* w1, int M, int K, int D, int N1, float eps, uint16_t* h1,
+                             uint16_t* h2, float* partials, float* r, uint16_t* y, void* workspace,
+                             long long workspace_bytes, void* stream) {
+  if (!(eps >= 0.0f) || !(eps < __builtin_huge_valf())) return CODA_ERR_ARG;
+  if (workspace_bytes < 0) return CODA_ERR_ARG;
+  CODA_TRY(check_gemm1(x, w0, z, gamma, M, K, D, h1, h2, partials));
+  CODA_TRY(check_gemm2(h2, w1, r, M, D, N1, y));
+  if (M == 0) return CODA_OK;
+  CODA_TRY(disjoint_fwd(x, w0, z, gamma, w1, M, K, D, N1, h1, h2, partials, r, y));
+  int cus = 0;
+  CODA_TRY(device_cus(&cus));
+  const SplitPlan sp1 = split_plan(M, D, K, cus), sp2 = split_plan(M, N1, D, cus);
+  const long long need = 4 * std::max(split_workspace_floats(M, D, sp1), split_workspace_floats(M, N1, sp2));
+  if (need > 0) {
+    CODA_NONNULL(workspace);
+    CODA_ALIGN16(workspace);
+    if (workspace_bytes < need) return CODA_ERR_WORKSPACE;
+    CODA_TRY(check_disjoint({Span{workspace, (uint64_t)need}},
+                            {bf16_span(x, M, K), bf16_span(w0, K, D), bf16_span(z, M, D), bf16_span(gamma, D),
+                             bf16_span(w1, D, N1), bf16_span(h1, M, D), bf16_span(h2, M, D),
+                             f32_span(partials, M, (D + kBN - 1) / kBN), f32_span(r, M), bf16_span(y, M, N1)}));
+  }
+  float* ws = static_cast<float*>(workspace);
+  const hipStream_t s = as_stream(stream);
+  const int nb = (D + kBN - 1) / kBN;
+  CODA_TRY((launch_gemm_split<true, EpiResidualRmsPartials>(GemmProblem{x, w0, M, D, K},
+                                                            EpiResidualRmsPartials::Args{z, gamma, h1, h2, partials, nb},
+                                                            sp1, ws, s)));
+  CODA_TRY(coda_rowstat_reduce_impl(partials, M, nb, D, eps, CODA_ROWSTAT_RSQRT_MEAN_EPS, r, s));
+  return launch_gemm_split<true, EpiRowScale>(GemmProblem{h2, w1, M, N1, D}, EpiRowScale::Args{r, y}, sp2, ws, s);
 }
 
 // ----------------------------------------------------------- forward without allocation

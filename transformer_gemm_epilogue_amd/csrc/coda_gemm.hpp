@@ -426,21 +426,23 @@ __device__ __forceinline__ void mainloop_resume(const ML& ml, const TileSrc& src
   issue_x_pair(ml, src, lds.slot[2], lds.slot[3], 2);
 }
 
-// The depth loop of one tile, after its prologue (or resume). With kPersist and a next
-// tile, the loads of steps KT and KT+1 of the schedule are that tile's steps 0 and 1
-// (this needs KT >= 4, so that all of them fall inside this loop); otherwise loads past
-// the end zero-fill free slots. Returns once every load has landed and every wave is
-// done reading operands.
+// The depth loop of one tile, after its prologue (or resume), over `steps` depth steps
+// from the tile's first one (all of its ml.KT steps, or a slice of them in the split-depth
+// schedule). With kPersist and a next tile, the loads of steps KT and KT+1 of the
+// schedule are that tile's steps 0 and 1 (this needs KT >= 4, so that all of them fall
+// inside this loop); otherwise loads past the end zero-fill free slots (or, past the end
+// of a slice, load depth steps nobody reads). Returns once every load has landed and
+// every wave is done reading operands.
 template <bool kPersist, class ML>
 __device__ __forceinline__ void mainloop_body(const ML& ml, const TileSrc& cur, const TileSrc& nxt,
-                                              bool has_next, const LdsRing& lds, AccTile& acc) {
+                                              bool has_next, const LdsRing& lds, AccTile& acc, int steps) {
   constexpr bool kWKN = ML::kKN;
 #pragma unroll
   for (int i = 0; i < kNI; ++i)
 #pragma unroll
     for (int j = 0; j < kMJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int KT = ml.KT;
+  const int KT = steps;
   constexpr int kH = kMJ / 2;                           // token blocks per half step
   constexpr int kMfmaH = kNI * kH;                      // MFMAs per half step
 
@@ -1081,7 +1083,7 @@ void gemm_epilogue_kernel(GemmProblem p, typename Epi::Args ea) {
   const TileSrc src = ml.src(t, m0, n0);
   AccTile acc;
   mainloop_prologue(ml, src, lds);
-  mainloop_body<false>(ml, src, src, false, lds, acc);
+  mainloop_body<false>(ml, src, src, false, lds, acc, ml.KT);
   Epi::apply(acc, ea, p, m0, n0, lds);
 }
 
@@ -1138,7 +1140,7 @@ void gemm_persistent_kernel(GemmProblem p, typename Epi::Args ea) {
     e = e >= kStages ? e - kStages : e;
     const LdsRing lds = make_ring(smem, rot, e, tid);
     AccTile acc;
-    mainloop_body<true>(ml, cur, nxt, has_next, lds, acc);
+    mainloop_body<true>(ml, cur, nxt, has_next, lds, acc, ml.KT);
     Epi::apply(acc, ea, p, m0, n0, lds);
     if (!has_next) break;
     t = tn;

@@ -1,0 +1,117 @@
+// Split-depth schedule for outputs with fewer 256 x 256 tiles than the GPU has CUs (a
+// small batch, or one GPU's share of token-sharded rows): with one workgroup per tile
+// most CUs would idle. Each tile's depth steps are cut into S slices of equal, even
+// length; a workgroup runs the same main loop over one slice and stores its fp32
+// accumulator tile to a workspace; a second kernel then sums a tile's S partial tiles in
+// the fixed order s = 0, 1, ..., S-1 and runs the tile's epilogue program on the sum, as
+// the one-kernel schedule runs it on its accumulator. The result is deterministic (it
+// depends only on the shape and S), though its fp32 rounding differs from the one-kernel
+// schedule's, whose depth order is rotated per tile.
+#pragma once
+
+#include <algorithm>
+
+#include "coda_gemm.hpp"
+
+namespace coda {
+
+constexpr int kSplitMinSteps = 16;  // depth steps per slice at least (the ring's fill costs ~3)
+constexpr int kSplitMax = 8;        // slices per tile at most
+constexpr long long kSplitTileFloats = (long long)kNI * kMJ * kThreads * 4;  // one fp32 tile: 256 KiB
+
+struct SplitPlan {
+  int S;      // slices per tile (1: the one-kernel schedule)
+  int steps;  // depth steps per slice (the last one may be shorter)
+};
+
+// S = as many slices as fit one workgroup per CU (T S <= CUs: a second, partial wave of
+// workgroups would cost a whole slice's time for a few of them), at most kSplitMax and
+// with at least kSplitMinSteps steps each; slices are an even number of steps (paired X
+// loads share 128-byte lines), and S is recomputed so that none is empty.
+__host__ inline SplitPlan split_plan(int M, int N, int K, int cus) {
+  const int T = gemm_grid(M, N), KT = (K + kBK - 1) / kBK;
+  if (2 * T > cus) return SplitPlan{1, KT};
+  int S = std::min(cus / T, std::min(kSplitMax, KT / kSplitMinSteps));
+  if (S <= 1) return SplitPlan{1, KT};
+  int steps = (KT + S - 1) / S;
+  steps += steps & 1;
+  S = (KT + steps - 1) / steps;
+  if (S <= 1) return SplitPlan{1, KT};
+  return SplitPlan{S, steps};
+}
+
+// fp32 workspace of a plan, in floats: S partial tiles per output tile.
+__host__ inline long long split_workspace_floats(int M, int N, const SplitPlan& sp) {
+  return sp.S > 1 ? (long long)gemm_grid(M, N) * sp.S * kSplitTileFloats : 0;
+}
+
+// Workgroup u -> (tile t, slice s). Workgroups go round-robin to the 8 XCDs, so the S
+// slices of a tile are placed on the same XCD (u mod 8 = t mod 8), where their partial
+// tiles meet in one L2; ceil(T / 8) * 8 * S workgroups, those past the last tile idle.
+__device__ __forceinline__ void split_unit(int u, int S, int& t, int& s) {
+  const int g = u / (8 * S), r = u - g * 8 * S;
+  s = r / 8;
+  t = g * 8 + (r - s * 8);
+}
+
+// Partial tile layout: [tile][slice][accumulator block i * kMJ + j][thread] of f32x4,
+// so that every store and load instruction of a wave covers 1 KiB of consecutive bytes.
+template <bool kWKN, bool kWOneDesc>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void gemm_split_kernel(GemmProblem p, int S, int slice_steps, f32x4_t* __restrict__ ws) {
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kSlotBytes];
+  int t, s;
+  split_unit(blockIdx.x, S, t, s);
+  if (t >= gemm_grid(p.M, p.N)) return;  // workgroup-uniform
+  const LdsRing lds = make_ring(smem, 0, 0, threadIdx.x);
+  int m0, n0;
+  tile_coords(p.M, p.N, p.K, p.group_m, t, m0, n0);
+  Mainloop<kWKN, kWOneDesc> ml;
+  ml.init(p, threadIdx.x);
+  TileSrc src = ml.src(t, m0, n0);
+  src.kstart = s * slice_steps;  // no per-XCD rotation: the slice starts the walk
+  const int steps = min(slice_steps, ml.KT - src.kstart);
+  AccTile acc;
+  mainloop_prologue(ml, src, lds);
+  mainloop_body<false>(ml, src, src, false, lds, acc, steps);
+  f32x4_t* out = ws + ((size_t)t * S + s) * (size_t)(kNI * kMJ * kThreads) + threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kNI; ++i)
+#pragma unroll
+    for (int j = 0; j < kMJ; ++j) out[(size_t)(i * kMJ + j) * kThreads] = acc[i][j];
+}
+
+// One workgroup per output tile: the sum of its S partial tiles, in slice order, then the
+// tile's epilogue program, exactly as the one-kernel schedule calls it.
+template <class Epi>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void split_epilogue_kernel(GemmProblem p, typename Epi::Args ea, int S, const f32x4_t* __restrict__ ws) {
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kSlotBytes];
+  const int t = blockIdx.x;
+  int m0, n0;
+  tile_coords(p.M, p.N, p.K, p.group_m, t, m0, n0);
+  const LdsRing lds = make_ring(smem, 0, 0, threadIdx.x);
+  const f32x4_t* in = ws + (size_t)t * S * (size_t)(kNI * kMJ * kThreads) + threadIdx.x;
+  AccTile acc;
+#pragma unroll
+  for (int i = 0; i < kNI; ++i)
+#pragma unroll
+    for (int j = 0; j < kMJ; ++j) acc[i][j] = in[(size_t)(i * kMJ + j) * kThreads];
+  for (int s = 1; s < S; ++s) {
+    in += (size_t)(kNI * kMJ * kThreads);
+    // one feature block (8 loads) at a time: the next partial tile's 128 values in flight
+    // at once would not fit beside the accumulators in the register budget
+#pragma unroll
+    for (int i = 0; i < kNI; ++i) {
+      f32x4_t v[kMJ];
+#pragma unroll
+      for (int j = 0; j < kMJ; ++j) v[j] = in[(size_t)(i * kMJ + j) * kThreads];
+#pragma unroll
+      for (int j = 0; j < kMJ; ++j) acc[i][j] += v[j];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  Epi::apply(acc, ea, p, m0, n0, lds);
+}
+
+}  // namespace coda
