@@ -169,6 +169,31 @@ int main() {
   sweep("coda_baseline_mfma_loop", {8, 4, 16}, [&](const std::vector<int>& a) {
     return coda_baseline_mfma_loop(b, a[0], a[1], a[2], F<float>(2), nullptr);
   });
+  sweep("coda_baseline_schedule_probe", {0, 5, 1}, [&](const std::vector<int>& a) {
+    return coda_baseline_schedule_probe(a[0], a[1], a[2], 0.125f, 7u, F<float>(1), F<long long>(2), nullptr);
+  });
+  // ------------------------------------------------------- split-depth forward
+  sweep("coda_gemm_rmsnorm_fwd_ws", {256, 256, 256, 256}, [&](const std::vector<int>& a) {
+    return coda_gemm_rmsnorm_fwd_ws(b, F<uint16_t>(1), F<uint16_t>(2), F<uint16_t>(3), F<uint16_t>(4), a[0], a[1],
+                                    a[2], a[3], 1e-5f, F<uint16_t>(5), F<uint16_t>(6), F<float>(7), F<float>(8),
+                                    F<uint16_t>(9), fake(10), 1ll << 32, nullptr);
+  });
+  for (long long ws : {LLONG_MIN, -1ll, 0ll, 1ll << 40, LLONG_MAX})
+    status_ok(coda_gemm_rmsnorm_fwd_ws(b, F<uint16_t>(1), F<uint16_t>(2), F<uint16_t>(3), F<uint16_t>(4), 256, 256,
+                                       256, 256, 1e-5f, F<uint16_t>(5), F<uint16_t>(6), F<float>(7), F<float>(8),
+                                       F<uint16_t>(9), fake(10), ws, nullptr),
+              "coda_gemm_rmsnorm_fwd_ws workspace_bytes");
+  EXPECT(coda_gemm_rmsnorm_fwd_ws(b, F<uint16_t>(1), F<uint16_t>(2), F<uint16_t>(3), F<uint16_t>(4), 256, 256, 256,
+                                  256, 1e-5f, F<uint16_t>(5), F<uint16_t>(6), F<float>(7), F<float>(8),
+                                  F<uint16_t>(9), fake(10), -1, nullptr) == CODA_ERR_ARG,
+         "negative workspace_bytes");
+  {
+    long long bytes = 0;
+    sweep("coda_gemm_rmsnorm_fwd_workspace_bytes", {256, 256, 256, 256}, [&](const std::vector<int>& a) {
+      return coda_gemm_rmsnorm_fwd_workspace_bytes(a[0], a[1], a[2], a[3], &bytes);
+    });
+    EXPECT(coda_gemm_rmsnorm_fwd_workspace_bytes(8, 8, 8, 8, nullptr) == CODA_ERR_NULL, "bytes NULL");
+  }
   for (int st = -1; st <= 7; ++st) EXPECT(coda_status_string(st) != nullptr, "status string %d", st);
   printf("%ld calls, %d failures\n", calls, failures);
   return failures ? 1 : 0;
