@@ -20,7 +20,9 @@
  *     enqueued on that stream, asynchronously; the call returns before it finishes.
  *   - Ownership: the caller owns and allocates every buffer, workspaces included. The
  *     library allocates no device memory, keeps no state between calls and may be
- *     called from several host threads at once (on different buffers).
+ *     called from several host threads at once (on different buffers). The one
+ *     exception is coda_gemm_rmsnorm_fwd_noalloc, which keeps its row partials in a
+ *     fixed device array of the library (see there).
  *   - Aliasing: an output buffer may overlap neither an input nor another output
  *     (byte ranges of the sizes the call implies); such a call returns CODA_ERR_ARG.
  *     Inputs are only read and may alias each other.
@@ -65,7 +67,8 @@ extern "C" {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* coda_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor). */
+/* ABI version of this header (major * 100 + minor): 101 adds the split-depth forward
+ * and the schedule probe to 100. */
 int coda_abi_version(void);
 
 /* SHA-256 (64 hex digits, static string) of the sources and compile flags this library

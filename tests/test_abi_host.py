@@ -87,7 +87,7 @@ def test_binding_exports_every_public_wrapper():
 def test_status_strings(L):
     for st in range(7):
         assert L.coda_status_string(st)
-    assert L.coda_abi_version() == 100
+    assert L.coda_abi_version() == 101
 
 
 def test_num_partials(L):

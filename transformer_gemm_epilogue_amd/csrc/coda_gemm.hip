@@ -158,7 +158,7 @@ const char* coda_status_string(int status) {
   }
 }
 
-int coda_abi_version(void) { return 100; }
+int coda_abi_version(void) { return 101; }
 
 #ifndef CODA_SOURCE_HASH
 #define CODA_SOURCE_HASH "unknown"
