@@ -196,6 +196,16 @@ int coda_gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t,
                    const float* sin_t, int M, int K, int n_q, int n_k, int n_v, int head_dim,
                    int seq_len, int pos_offset, uint16_t* out, void* stream);
 
+/* coda_gemm_rope with the split-depth schedule of coda_gemm_rmsnorm_fwd_ws for outputs
+ * with fewer 256 x 256 tiles than the current device has CUs: `workspace` holds at least
+ * coda_split_workspace_bytes(M, n_q + n_k + n_v, K) bytes (16-byte aligned; NULL when
+ * that is 0; overlapping no other argument), else CODA_ERR_WORKSPACE. Same outputs up to
+ * the fp32 order of the depth sum; a negative workspace_bytes is CODA_ERR_ARG. */
+int coda_gemm_rope_ws(const uint16_t* x, const uint16_t* w, const float* cos_t,
+                      const float* sin_t, int M, int K, int n_q, int n_k, int n_v,
+                      int head_dim, int seq_len, int pos_offset, uint16_t* out,
+                      void* workspace, long long workspace_bytes, void* stream);
+
 /* coda_gemm_rope under the persistent schedule ([notes] main experiment table, "主实验":
  * GEMM + RoPE measured at M = N = K = 4096 and 8192 with a 3N QKV width; a schedule
  * variant of the same computation): min(tiles, CUs) workgroups walk the output
@@ -214,6 +224,18 @@ int coda_gemm_rope_persistent(const uint16_t* x, const uint16_t* w, const float*
  * The halving and compaction happen in the epilogue. F % 8 == 0 (and F >= 8). */
 int coda_gemm_swiglu(const uint16_t* x, const uint16_t* w, int M, int K, int F,
                      uint16_t* out, void* stream);
+
+/* coda_gemm_swiglu with the split-depth schedule (as coda_gemm_rope_ws); the GEMM's
+ * output width is 2F: workspace of coda_split_workspace_bytes(M, 2 F, K) bytes. */
+int coda_gemm_swiglu_ws(const uint16_t* x, const uint16_t* w, int M, int K, int F,
+                        uint16_t* out, void* workspace, long long workspace_bytes,
+                        void* stream);
+
+/* Bytes of split-depth workspace one GEMM with output [M, N] (N the GEMM's full output
+ * width) and depth K needs on the current device: 256 KiB per slice of every output
+ * tile, 0 when it does not split. Shape rules as the GEMMs; CODA_ERR_HIP if the device
+ * cannot be queried. */
+int coda_split_workspace_bytes(int M, int N, int K, long long* bytes);
 
 /* RoPE backward ([notes] key design 2; [pith] Fig. 7; the rotation is orthogonal, so its
  * gradient is the rotation by the negated angle): same arguments, layouts and rules as

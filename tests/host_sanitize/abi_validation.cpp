@@ -187,6 +187,19 @@ int main() {
                                   256, 1e-5f, F<uint16_t>(5), F<uint16_t>(6), F<float>(7), F<float>(8),
                                   F<uint16_t>(9), fake(10), -1, nullptr) == CODA_ERR_ARG,
          "negative workspace_bytes");
+  sweep("coda_gemm_rope_ws", {256, 256, 128, 128, 128, 128, 256, 0}, [&](const std::vector<int>& a) {
+    return coda_gemm_rope_ws(b, F<uint16_t>(2), F<float>(3), F<float>(4), a[0], a[1], a[2], a[3], a[4], a[5], a[6],
+                             a[7], F<uint16_t>(5), fake(6), 1ll << 32, nullptr);
+  });
+  sweep("coda_gemm_swiglu_ws", {256, 256, 128}, [&](const std::vector<int>& a) {
+    return coda_gemm_swiglu_ws(b, F<uint16_t>(2), a[0], a[1], a[2], F<uint16_t>(3), fake(4), 1ll << 32, nullptr);
+  });
+  {
+    long long bytes = 0;
+    sweep("coda_split_workspace_bytes", {256, 256, 256}, [&](const std::vector<int>& a) {
+      return coda_split_workspace_bytes(a[0], a[1], a[2], &bytes);
+    });
+  }
   {
     long long bytes = 0;
     sweep("coda_gemm_rmsnorm_fwd_workspace_bytes", {256, 256, 256, 256}, [&](const std::vector<int>& a) {

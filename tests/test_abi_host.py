@@ -360,3 +360,18 @@ def test_split_forward_validation(L):
     assert L.coda_gemm_rmsnorm_fwd_ws(None, P, P, P, P, 8, 8, 8, 8, f, *outs, P, 0, None) == NULL
     assert L.coda_gemm_rmsnorm_fwd_ws(P, P, P, P, P, 8, 12, 8, 8, f, *outs, P, 0, None) == SHAPE
     assert L.coda_gemm_rmsnorm_fwd_ws(P, P, P, P, P, 0, 8, 8, 8, f, *outs, None, 0, None) == OK
+
+
+def test_split_rope_swiglu_validation(L):
+    out = ctypes.c_int64(-1)
+    assert L.coda_split_workspace_bytes(8, 8, 8, None) == NULL
+    assert L.coda_split_workspace_bytes(8, 12, 8, ctypes.byref(out)) == SHAPE
+    assert L.coda_split_workspace_bytes(0, 8, 8, ctypes.byref(out)) == OK and out.value == 0
+    assert L.coda_gemm_swiglu_ws(P, P, 8, 8, 8, P, P, -1, None) == ARG
+    assert L.coda_gemm_swiglu_ws(None, P, 8, 8, 8, P, P, 0, None) == NULL
+    assert L.coda_gemm_swiglu_ws(P, P, 8, 8, 12, P, P, 0, None) == SHAPE
+    assert L.coda_gemm_swiglu_ws(P, P, 0, 8, 8, P, None, 0, None) == OK
+    rope = [P, P, P, P, 8, 8, 8, 8, 8, 8, 8, 0, P]
+    assert L.coda_gemm_rope_ws(*rope, P, -1, None) == ARG
+    assert L.coda_gemm_rope_ws(None, *rope[1:], P, 0, None) == NULL
+    assert L.coda_gemm_rope_ws(P, P, P, P, 0, 8, 8, 8, 8, 8, 8, 0, P, None, 0, None) == OK

@@ -131,3 +131,89 @@ def test_split_depth_workspace_errors(coda):
     assert L.coda_gemm_rmsnorm_fwd_ws(*args_alias, p(big), need, None) == 6      # CODA_ERR_ARG
     assert L.coda_gemm_rmsnorm_fwd_ws(*args, p(ws), need, None) == 0
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ RoPE and SwiGLU, split depth
+def test_rope_split_depth_small(coda):
+    import torch
+    wl = W.rope_qkv(seed=31, M=300, K=1024, n_q=256, n_k=128, n_v=128, head_dim=128, seq_len=300, pos_offset=7)
+    N = 512
+    assert coda.coda_split_workspace_bytes(300, N, 1024) > 0
+    log("rope split M=300 K=1024 N=512")
+    c, s = coda.coda_rope_tables(wl["seq_len"], wl["head_dim"], wl["theta"])
+    out = coda.coda_gemm_rope_ws(to_dev_bf16(wl["x"]), to_dev_bf16(wl["w"]), c, s, wl["n_q"], wl["n_k"], wl["n_v"],
+                                 wl["head_dim"], wl["seq_len"], wl["pos_offset"])
+    torch.cuda.synchronize()
+    ref = O.gemm_rope(wl["x"], wl["w"], wl["n_q"], wl["n_k"], wl["n_v"], wl["head_dim"], wl["seq_len"],
+                      wl["pos_offset"], wl["theta"])
+    assert_close_tiles("qkv", dec(out), ref)
+
+
+def test_rope_split_depth_last_of_eight_shards(coda):
+    """The last of 8 token shards of the RoPE workload (512 rows, 96 output tiles: two
+    slices each), pos_offset = the shard's first row."""
+    import torch
+    wl = W.rope_qkv()
+    M = wl["M"]
+    lo, hi = M - M // 8, M
+    N = wl["n_q"] + wl["n_k"] + wl["n_v"]
+    assert coda.coda_split_workspace_bytes(hi - lo, N, wl["K"]) > 0
+    log(f"rope split shard rows {lo}..{hi - 1}")
+    c, s = coda.coda_rope_tables(wl["seq_len"], wl["head_dim"], wl["theta"])
+    out = coda.coda_gemm_rope_ws(to_dev_bf16(np.ascontiguousarray(wl["x"][lo:hi])), to_dev_bf16(wl["w"]), c, s,
+                                 wl["n_q"], wl["n_k"], wl["n_v"], wl["head_dim"], wl["seq_len"],
+                                 wl["pos_offset"] + lo)
+    torch.cuda.synchronize()
+    ref = O.gemm_rope(wl["x"], wl["w"], wl["n_q"], wl["n_k"], wl["n_v"], wl["head_dim"], wl["seq_len"],
+                      wl["pos_offset"], wl["theta"], rows=np.arange(lo, hi))
+    assert_close_tiles("qkv", dec(out), ref)
+
+
+def test_rope_no_split_equals_one_kernel_schedule(coda):
+    import torch
+    wl = W.rope_qkv(seed=32, M=4096, K=256, n_q=2048, n_k=1024, n_v=1024, head_dim=128, seq_len=4096)
+    assert coda.coda_split_workspace_bytes(4096, 4096, 256) == 0
+    c, s = coda.coda_rope_tables(wl["seq_len"], wl["head_dim"], wl["theta"])
+    args = (to_dev_bf16(wl["x"]), to_dev_bf16(wl["w"]), c, s, wl["n_q"], wl["n_k"], wl["n_v"], wl["head_dim"],
+            wl["seq_len"], wl["pos_offset"])
+    a = coda.coda_gemm_rope_ws(*args)
+    b = coda.coda_gemm_rope(*args)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(a), bf16_bits(b))
+
+
+def test_swiglu_split_depth_small(coda):
+    import torch
+    M, K, F = 300, 1024, 264
+    wl = W.swiglu(seed=33, M=M, K=K, F=F)
+    assert coda.coda_split_workspace_bytes(M, 2 * F, K) > 0
+    log(f"swiglu split M={M} K={K} F={F}")
+    out = coda.coda_gemm_swiglu_ws(to_dev_bf16(wl["x"]), to_dev_bf16(wl["w"]))
+    torch.cuda.synchronize()
+    assert_close_tiles("out", dec(out), O.gemm_swiglu(wl["x"], wl["w"]))
+
+
+def test_rope_and_swiglu_workspace_errors(coda):
+    import torch
+    L = coda.lib()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    M, K, F = 300, 1024, 264
+    need = coda.coda_split_workspace_bytes(M, 2 * F, K)
+    x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((K, 2 * F), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    assert L.coda_gemm_swiglu_ws(p(x), p(w), M, K, F, p(out), p(ws), need - 16, None) == 4
+    assert L.coda_gemm_swiglu_ws(p(x), p(w), M, K, F, p(out), None, 0, None) == 1
+    assert L.coda_gemm_swiglu_ws(p(x), p(w), M, K, F, p(out), p(ws), -1, None) == 6
+    assert L.coda_gemm_swiglu_ws(p(x), p(w), M, K, F, p(out), p(ws), need, None) == 0
+    c = torch.zeros((300 * 64,), dtype=torch.float32, device="cuda")
+    wr = torch.zeros((K, 512), dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty((M, 512), dtype=torch.bfloat16, device="cuda")
+    need2 = coda.coda_split_workspace_bytes(M, 512, K)
+    ws2 = torch.empty((need2,), dtype=torch.uint8, device="cuda")
+    args = [p(x), p(wr), p(c), p(c), M, K, 256, 128, 128, 128, 300, 0, p(o2)]
+    assert L.coda_gemm_rope_ws(*args, p(ws2), need2 - 16, None) == 4
+    assert L.coda_gemm_rope_ws(*args, p(o2), need2, None) == 6        # workspace on the output
+    assert L.coda_gemm_rope_ws(*args, p(ws2), need2, None) == 0
+    torch.cuda.synchronize()

@@ -36,6 +36,9 @@ __all__ = [
     "coda_gemm_rope",
     "coda_gemm_rope_persistent",
     "coda_gemm_swiglu",
+    "coda_gemm_swiglu_ws",
+    "coda_gemm_rope_ws",
+    "coda_split_workspace_bytes",
     "coda_gemm_rmsnorm_bwd_stats",
     "num_row_tiles",
     "coda_rowdot_stat",
@@ -81,7 +84,10 @@ SIGNATURES = {
     "coda_rope_tables": [_P, _P, _I, _I, _D, _P],
     "coda_gemm_rope": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P],
     "coda_gemm_rope_persistent": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P],
+    "coda_gemm_rope_ws": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I64, _P],
     "coda_gemm_swiglu": [_P, _P, _I, _I, _I, _P, _P],
+    "coda_gemm_swiglu_ws": [_P, _P, _I, _I, _I, _P, _P, _I64, _P],
+    "coda_split_workspace_bytes": [_I, _I, _I, ctypes.POINTER(_I64)],
     "coda_gemm_rope_bwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P],
     "coda_gemm_swiglu_bwd": [_P, _P, _P, _I, _I, _I, _P, _P],
     "coda_gemm_cross_entropy": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P],
@@ -330,6 +336,35 @@ def coda_gemm_rope(x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_off
                       stream)
 
 
+def coda_split_workspace_bytes(M, N, K):
+    """Bytes of split-depth workspace one GEMM with output [M, N] and depth K needs."""
+    out = ctypes.c_int64(0)
+    _call("coda_split_workspace_bytes", int(M), int(N), int(K), ctypes.byref(out))
+    return out.value
+
+
+def _workspace(need, like, workspace):
+    if workspace is None:
+        workspace = _empty((max(int(need), 16),), _torch().uint8, like)
+    return _dev(workspace, _torch().uint8, "workspace"), int(workspace.numel())
+
+
+def coda_gemm_rope_ws(x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset=0, out=None, workspace=None,
+                      stream=None):
+    """coda_gemm_rope with the split-depth schedule for outputs with fewer tiles than CUs
+    (`workspace`: uint8 GPU tensor, allocated here when None)."""
+    torch = _torch()
+    M, K = x.shape
+    N = n_q + n_k + n_v
+    if w.shape != (K, N):
+        raise ValueError("coda_gemm_rope_ws: w must be [K, n_q + n_k + n_v]")
+    out = _empty((M, N), torch.bfloat16, x) if out is None else out
+    ws, nbytes = _workspace(coda_split_workspace_bytes(M, N, K) if workspace is None else 0, x, workspace)
+    _call("coda_gemm_rope_ws", _bf16(x, "x"), _bf16(w, "w"), _f32(cos_t, "cos_t"), _f32(sin_t, "sin_t"), M, K,
+          n_q, n_k, n_v, head_dim, seq_len, pos_offset, _bf16(out, "out"), ws, nbytes, _stream(stream))
+    return out
+
+
 def coda_gemm_rope_persistent(x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset=0, out=None,
                               stream=None):
     """coda_gemm_rope under the persistent schedule (same output, bit for bit)."""
@@ -351,6 +386,20 @@ def coda_gemm_swiglu(x, w, out=None, stream=None):
     F = w.shape[1] // 2
     out = _empty((M, F), torch.bfloat16, x) if out is None else out
     _call("coda_gemm_swiglu", _bf16(x, "x"), _bf16(w, "w"), M, K, F, _bf16(out, "out"), _stream(stream))
+    return out
+
+
+def coda_gemm_swiglu_ws(x, w, out=None, workspace=None, stream=None):
+    """coda_gemm_swiglu with the split-depth schedule for outputs with fewer tiles than CUs."""
+    torch = _torch()
+    M, K = x.shape
+    if w.shape[0] != K or w.shape[1] % 2:
+        raise ValueError("coda_gemm_swiglu_ws: w must be [K, 2F]")
+    F = w.shape[1] // 2
+    out = _empty((M, F), torch.bfloat16, x) if out is None else out
+    ws, nbytes = _workspace(coda_split_workspace_bytes(M, 2 * F, K) if workspace is None else 0, x, workspace)
+    _call("coda_gemm_swiglu_ws", _bf16(x, "x"), _bf16(w, "w"), M, K, F, _bf16(out, "out"), ws, nbytes,
+          _stream(stream))
     return out
 
 

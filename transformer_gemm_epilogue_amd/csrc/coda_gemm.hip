@@ -54,6 +54,22 @@ int launch_gemm_split(const GemmProblem& p, const typename Epi::Args& ea, const 
   return launch_status();
 }
 
+// The split plan of one GEMM on the current device and its workspace checks: enough bytes,
+// 16-byte aligned, overlapping none of the call's other buffers (`others`).
+int split_for_call(int M, int N, int K, void* workspace, long long workspace_bytes, std::initializer_list<Span> others,
+                   SplitPlan* sp) {
+  if (workspace_bytes < 0) return CODA_ERR_ARG;
+  int cus = 0;
+  CODA_TRY(device_cus(&cus));
+  *sp = split_plan(M, N, K, cus);
+  const long long need = 4 * split_workspace_floats(M, N, *sp);
+  if (need == 0) return CODA_OK;
+  CODA_NONNULL(workspace);
+  CODA_ALIGN16(workspace);
+  if (workspace_bytes < need) return CODA_ERR_WORKSPACE;
+  return check_disjoint({Span{workspace, (uint64_t)need}}, others);
+}
+
 // Persistent schedule: min(tiles, CUs of the current device) workgroups walk the tiles
 // (one workgroup fills a CU's LDS); below the minimum depth the per-tile kernel runs
 // instead. Both give bit-identical results.
@@ -304,9 +320,12 @@ int coda_gemm_rmsnorm_fwd_noalloc(const uint16_t* x, const uint16_t* w0, const u
 }
 
 namespace {
+enum class Schedule { kPerTile, kPersistent, kSplit };
+
 int gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K, int n_q,
               int n_k, int n_v, int head_dim, int seq_len, int pos_offset, uint16_t* out, int inverse,
-              bool persistent, hipStream_t stream) {
+              Schedule schedule, hipStream_t stream, void* workspace = nullptr, long long workspace_bytes = 0) {
+  if (schedule == Schedule::kSplit && workspace_bytes < 0) return CODA_ERR_ARG;
   CODA_TRY(check_rows(M));
   CODA_TRY(check_depth_or_width(K));
   if (head_dim < 8 || head_dim % 8 != 0 || head_dim > kMaxDim) return CODA_ERR_SHAPE;
@@ -330,36 +349,23 @@ int gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, const fl
                           {bf16_span(x, M, K), bf16_span(w, K, N), f32_span(cos_t, tab), f32_span(sin_t, tab)}));
   const GemmProblem p{x, w, M, (int)N, K};
   const EpiRope::Args ea{cos_t, sin_t, out, n_q + n_k, head_dim, seq_len, pos_offset, inverse};
-  if (persistent) return launch_gemm_persistent<true, EpiRope>(p, ea, stream);
+  if (schedule == Schedule::kPersistent) return launch_gemm_persistent<true, EpiRope>(p, ea, stream);
+  if (schedule == Schedule::kSplit) {
+    SplitPlan sp;
+    CODA_TRY(split_for_call(M, (int)N, K, workspace, workspace_bytes,
+                            {bf16_span(out, M, N), bf16_span(x, M, K), bf16_span(w, K, N), f32_span(cos_t, tab),
+                             f32_span(sin_t, tab)},
+                            &sp));
+    return launch_gemm_split<true, EpiRope>(p, ea, sp, static_cast<float*>(workspace), stream);
+  }
   return launch_gemm<true, EpiRope>(p, ea, stream);
 }
-}  // namespace
-
-int coda_gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K,
-                   int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset, uint16_t* out,
-                   void* stream) {
-  return gemm_rope(x, w, cos_t, sin_t, M, K, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, 0, false,
-                   as_stream(stream));
-}
-
-int coda_gemm_rope_persistent(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M,
-                              int K, int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset,
-                              uint16_t* out, void* stream) {
-  return gemm_rope(x, w, cos_t, sin_t, M, K, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, 0, true,
-                   as_stream(stream));
-}
-
-int coda_gemm_rope_bwd(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K,
-                       int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset, uint16_t* out,
-                       void* stream) {
-  return gemm_rope(x, w, cos_t, sin_t, M, K, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, 1, false,
-                   as_stream(stream));
-}
-
-int coda_gemm_swiglu(const uint16_t* x, const uint16_t* w, int M, int K, int F, uint16_t* out, void* stream) {
+int gemm_swiglu(const uint16_t* x, const uint16_t* w, int M, int K, int F, uint16_t* out, bool split, void* workspace,
+                long long workspace_bytes, hipStream_t stream) {
   CODA_TRY(check_rows(M));
   CODA_TRY(check_depth_or_width(K));
   if (F < 8 || F % 8 != 0 || 2LL * F > kMaxDim) return CODA_ERR_SHAPE;
+  if (split && workspace_bytes < 0) return CODA_ERR_ARG;
   if (M == 0) return CODA_OK;
   CODA_NONNULL(x);
   CODA_NONNULL(w);
@@ -370,7 +376,62 @@ int coda_gemm_swiglu(const uint16_t* x, const uint16_t* w, int M, int K, int F, 
   CODA_TRY(check_disjoint({bf16_span(out, M, F)}, {bf16_span(x, M, K), bf16_span(w, K, 2LL * F)}));
   const GemmProblem p{x, w, M, 2 * F, K};
   const EpiSwiGLU::Args ea{out, F};
-  return launch_gemm<true, EpiSwiGLU>(p, ea, as_stream(stream));
+  if (!split) return launch_gemm<true, EpiSwiGLU>(p, ea, stream);
+  SplitPlan sp;
+  CODA_TRY(split_for_call(M, 2 * F, K, workspace, workspace_bytes,
+                          {bf16_span(out, M, F), bf16_span(x, M, K), bf16_span(w, K, 2LL * F)}, &sp));
+  return launch_gemm_split<true, EpiSwiGLU>(p, ea, sp, static_cast<float*>(workspace), stream);
+}
+}  // namespace
+
+int coda_gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K,
+                   int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset, uint16_t* out,
+                   void* stream) {
+  return gemm_rope(x, w, cos_t, sin_t, M, K, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, 0,
+                   Schedule::kPerTile, as_stream(stream));
+}
+
+int coda_gemm_rope_ws(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K,
+                      int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset, uint16_t* out,
+                      void* workspace, long long workspace_bytes, void* stream) {
+  return gemm_rope(x, w, cos_t, sin_t, M, K, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, 0, Schedule::kSplit,
+                   as_stream(stream), workspace, workspace_bytes);
+}
+
+int coda_gemm_rope_persistent(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M,
+                              int K, int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset,
+                              uint16_t* out, void* stream) {
+  return gemm_rope(x, w, cos_t, sin_t, M, K, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, 0,
+                   Schedule::kPersistent, as_stream(stream));
+}
+
+int coda_gemm_rope_bwd(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K,
+                       int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset, uint16_t* out,
+                       void* stream) {
+  return gemm_rope(x, w, cos_t, sin_t, M, K, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, 1,
+                   Schedule::kPerTile, as_stream(stream));
+}
+
+int coda_gemm_swiglu(const uint16_t* x, const uint16_t* w, int M, int K, int F, uint16_t* out, void* stream) {
+  return gemm_swiglu(x, w, M, K, F, out, false, nullptr, 0, as_stream(stream));
+}
+
+int coda_gemm_swiglu_ws(const uint16_t* x, const uint16_t* w, int M, int K, int F, uint16_t* out, void* workspace,
+                        long long workspace_bytes, void* stream) {
+  return gemm_swiglu(x, w, M, K, F, out, true, workspace, workspace_bytes, as_stream(stream));
+}
+
+int coda_split_workspace_bytes(int M, int N, int K, long long* bytes) {
+  CODA_NONNULL(bytes);
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(N));
+  CODA_TRY(check_depth_or_width(K));
+  *bytes = 0;
+  if (M == 0) return CODA_OK;
+  int cus = 0;
+  CODA_TRY(device_cus(&cus));
+  *bytes = 4 * split_workspace_floats(M, N, split_plan(M, N, K, cus));
+  return CODA_OK;
 }
 
 int coda_gemm_rmsnorm_bwd_stats(const uint16_t* dy, const uint16_t* w1, const uint16_t* h2, int M, int D, int N,
