@@ -325,7 +325,23 @@ def other_paths(coda, torch, reps):
         "hipblaslt": lambda: torch.matmul(x, w)}, reps)
     fl = 2.0 * M * K * N
     out["gemm_rope_qkv_4096x12288x4096"] = path_record(t, fl)
-    del x, w, qkv, h
+    # one GPU's share of it under token sharding (M/G rows, pos_offset = the share's first
+    # row), one kernel against the split-depth schedule
+    fns, wss, shares = {}, {}, {}
+    for G in (4, 8):
+        m = M // G
+        wss[G] = torch.empty((max(coda.coda_split_workspace_bytes(m, N, K), 16),), dtype=torch.uint8, device="cuda")
+        sargs = args[:-1] + (M - m,)
+        fns[(G, "one_kernel")] = (lambda m=m, sargs=sargs: coda.coda_gemm_rope(x[M - m:], w, c, s, *sargs,
+                                                                               out=qkv[:m]))
+        fns[(G, "split_depth")] = (lambda m=m, sargs=sargs, G=G: coda.coda_gemm_rope_ws(
+            x[M - m:], w, c, s, *sargs, out=qkv[:m], workspace=wss[G]))
+    for (G, how), ms in time_interleaved(fns, reps).items():
+        m = M // G
+        shares.setdefault(f"G{G}", dict(rows=m))[how] = dict(ms=round(ms, 4),
+                                                             tflops=round(2.0 * m * K * N / (ms * 1e-3) / 1e12, 1))
+    out["gemm_rope_qkv_4096x12288x4096"]["one_gpu_share_of_token_shards"] = shares
+    del x, w, qkv, h, wss
     torch.cuda.empty_cache()
     # GEMM + RoPE at the 8192 class (M = K = 8192, QKV width 3 x 8192), both schedules
     log("paths: rope 8192 (generating inputs) ...")
