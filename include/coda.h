@@ -68,7 +68,8 @@ extern "C" {
 const char* coda_status_string(int status);
 
 /* ABI version of this header (major * 100 + minor): 101 adds the split-depth forward
- * and the schedule probe to 100. */
+ * and the schedule probe to 100; 102 adds the split-depth backward and cross-entropy
+ * entry points. */
 int coda_abi_version(void);
 
 /* SHA-256 (64 hex digits, static string) of the sources and compile flags this library
@@ -245,6 +246,12 @@ int coda_gemm_rope_bwd(const uint16_t* x, const uint16_t* w, const float* cos_t,
                        const float* sin_t, int M, int K, int n_q, int n_k, int n_v,
                        int head_dim, int seq_len, int pos_offset, uint16_t* out,
                        void* stream);
+/* coda_gemm_rope_bwd with the split-depth schedule of coda_gemm_rope_ws (same workspace:
+ * coda_split_workspace_bytes(M, n_q + n_k + n_v, K) bytes, same rules and errors). */
+int coda_gemm_rope_bwd_ws(const uint16_t* x, const uint16_t* w, const float* cos_t,
+                          const float* sin_t, int M, int K, int n_q, int n_k, int n_v,
+                          int head_dim, int seq_len, int pos_offset, uint16_t* out,
+                          void* workspace, long long workspace_bytes, void* stream);
 
 /* SwiGLU backward pairwise map ([notes] key design 2, last item; [pith] Fig. 7: one
  * incoming gradient becomes the gradients of both paired inputs), in the epilogue of the
@@ -258,6 +265,12 @@ int coda_gemm_rope_bwd(const uint16_t* x, const uint16_t* w, const float* cos_t,
  * M == 0 is a no-op. */
 int coda_gemm_swiglu_bwd(const uint16_t* dy, const uint16_t* w_down, const uint16_t* h,
                          int M, int Dm, int F, uint16_t* dh, void* stream);
+/* coda_gemm_swiglu_bwd with the split-depth schedule (as coda_gemm_rope_ws); the grad
+ * GEMM's output width is F and its depth Dm: workspace of coda_split_workspace_bytes(M, F,
+ * Dm) bytes. */
+int coda_gemm_swiglu_bwd_ws(const uint16_t* dy, const uint16_t* w_down, const uint16_t* h,
+                            int M, int Dm, int F, uint16_t* dh, void* workspace,
+                            long long workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * RMSNorm-backward row statistic from the grad GEMM's epilogue ([notes] key design 3):
@@ -272,6 +285,12 @@ int coda_gemm_swiglu_bwd(const uint16_t* dy, const uint16_t* w_down, const uint1
 int coda_gemm_rmsnorm_bwd_stats(const uint16_t* dy, const uint16_t* w1, const uint16_t* h2,
                                 int M, int D, int N, uint16_t* dh2, float* partials,
                                 float* s, void* stream);
+/* coda_gemm_rmsnorm_bwd_stats with the split-depth schedule (as coda_gemm_rope_ws):
+ * output width D, depth N, workspace of coda_split_workspace_bytes(M, D, N) bytes. */
+int coda_gemm_rmsnorm_bwd_stats_ws(const uint16_t* dy, const uint16_t* w1, const uint16_t* h2,
+                                   int M, int D, int N, uint16_t* dh2, float* partials,
+                                   float* s, void* workspace, long long workspace_bytes,
+                                   void* stream);
 
 /* ---------------------------------------------------------------------------------
  * The rest of the RMSNorm backward ([notes] key design 3 and the duality paragraph
@@ -313,6 +332,15 @@ int coda_gemm_rmsnorm_bwd_dx(const uint16_t* dy, const uint16_t* w1, const uint1
                              const uint16_t* gamma, const float* r, const float* s,
                              const uint16_t* g_res, int M, int D, int N, uint16_t* dh1,
                              float* dgamma_partials, void* stream);
+/* coda_gemm_rmsnorm_bwd_dx with the split-depth schedule (as coda_gemm_rope_ws): output
+ * width D, depth N, workspace of coda_split_workspace_bytes(M, D, N) bytes. The dgamma
+ * partials come from the summed accumulators, so their values match the one-kernel call
+ * up to the fp32 order of the depth sum. */
+int coda_gemm_rmsnorm_bwd_dx_ws(const uint16_t* dy, const uint16_t* w1, const uint16_t* h1,
+                                const uint16_t* gamma, const float* r, const float* s,
+                                const uint16_t* g_res, int M, int D, int N, uint16_t* dh1,
+                                float* dgamma_partials, void* workspace,
+                                long long workspace_bytes, void* stream);
 
 /* All of it: s from (dy, y), the grad GEMM with its epilogue, and dgamma. Three
  * launches on `stream`. s [M], dh1, dgamma_partials and dgamma are outputs. With M == 0
@@ -339,6 +367,12 @@ int coda_rmsnorm_bwd(const uint16_t* dy, const uint16_t* w1, const uint16_t* h1,
 int coda_gemm_cross_entropy(const uint16_t* x, const uint16_t* w, const int32_t* labels,
                             int M, int K, int V, float* tile_lse, float* target, float* lse,
                             float* loss, void* stream);
+/* coda_gemm_cross_entropy with the split-depth schedule (as coda_gemm_rope_ws): output
+ * width V, depth K, workspace of coda_split_workspace_bytes(M, V, K) bytes. */
+int coda_gemm_cross_entropy_ws(const uint16_t* x, const uint16_t* w, const int32_t* labels,
+                               int M, int K, int V, float* tile_lse, float* target,
+                               float* lse, float* loss, void* workspace,
+                               long long workspace_bytes, void* stream);
 /* The auxiliary merge alone (tile_lse and target from the epilogue above). nb must equal
  * coda_rowstat_num_partials(V). */
 int coda_lse_reduce(const float* tile_lse, const int32_t* labels, int M, int nb, int V,

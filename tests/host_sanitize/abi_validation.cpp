@@ -194,6 +194,40 @@ int main() {
   sweep("coda_gemm_swiglu_ws", {256, 256, 128}, [&](const std::vector<int>& a) {
     return coda_gemm_swiglu_ws(b, F<uint16_t>(2), a[0], a[1], a[2], F<uint16_t>(3), fake(4), 1ll << 32, nullptr);
   });
+  // ------------------------------------------ split-depth backward, cross-entropy
+  sweep("coda_gemm_rope_bwd_ws", {256, 256, 128, 128, 128, 128, 256, 0}, [&](const std::vector<int>& a) {
+    return coda_gemm_rope_bwd_ws(b, F<uint16_t>(2), F<float>(3), F<float>(4), a[0], a[1], a[2], a[3], a[4], a[5],
+                                 a[6], a[7], F<uint16_t>(5), fake(6), 1ll << 32, nullptr);
+  });
+  sweep("coda_gemm_swiglu_bwd_ws", {256, 256, 128}, [&](const std::vector<int>& a) {
+    return coda_gemm_swiglu_bwd_ws(b, F<uint16_t>(2), F<uint16_t>(3), a[0], a[1], a[2], F<uint16_t>(4), fake(5),
+                                   1ll << 32, nullptr);
+  });
+  sweep("coda_gemm_rmsnorm_bwd_stats_ws", {256, 256, 256}, [&](const std::vector<int>& a) {
+    return coda_gemm_rmsnorm_bwd_stats_ws(b, F<uint16_t>(2), F<uint16_t>(3), a[0], a[1], a[2], F<uint16_t>(4),
+                                          F<float>(5), F<float>(6), fake(7), 1ll << 32, nullptr);
+  });
+  sweep("coda_gemm_rmsnorm_bwd_dx_ws", {256, 256, 256}, [&](const std::vector<int>& a) {
+    return coda_gemm_rmsnorm_bwd_dx_ws(b, F<uint16_t>(2), F<uint16_t>(3), F<uint16_t>(4), F<float>(5), F<float>(6),
+                                       F<uint16_t>(7), a[0], a[1], a[2], F<uint16_t>(8), F<float>(9), fake(10),
+                                       1ll << 32, nullptr);
+  });
+  sweep("coda_gemm_cross_entropy_ws", {256, 256, 512}, [&](const std::vector<int>& a) {
+    return coda_gemm_cross_entropy_ws(b, F<uint16_t>(2), F<int32_t>(3), a[0], a[1], a[2], F<float>(4), F<float>(5),
+                                      F<float>(6), F<float>(7), fake(8), 1ll << 32, nullptr);
+  });
+  for (long long ws : {LLONG_MIN, -1ll, 0ll, 1ll << 40, LLONG_MAX}) {
+    status_ok(coda_gemm_swiglu_bwd_ws(b, F<uint16_t>(2), F<uint16_t>(3), 256, 256, 128, F<uint16_t>(4), fake(5), ws,
+                                      nullptr),
+              "coda_gemm_swiglu_bwd_ws workspace_bytes");
+    status_ok(coda_gemm_cross_entropy_ws(b, F<uint16_t>(2), F<int32_t>(3), 256, 256, 512, F<float>(4), F<float>(5),
+                                         F<float>(6), F<float>(7), fake(8), ws, nullptr),
+              "coda_gemm_cross_entropy_ws workspace_bytes");
+  }
+  EXPECT(coda_gemm_rmsnorm_bwd_dx_ws(b, F<uint16_t>(2), F<uint16_t>(3), F<uint16_t>(4), F<float>(5), F<float>(6),
+                                     F<uint16_t>(7), 256, 256, 256, F<uint16_t>(8), F<float>(9), fake(10), -1,
+                                     nullptr) == CODA_ERR_ARG,
+         "negative workspace_bytes (dx)");
   {
     long long bytes = 0;
     sweep("coda_split_workspace_bytes", {256, 256, 256}, [&](const std::vector<int>& a) {

@@ -87,7 +87,7 @@ def test_binding_exports_every_public_wrapper():
 def test_status_strings(L):
     for st in range(7):
         assert L.coda_status_string(st)
-    assert L.coda_abi_version() == 101
+    assert L.coda_abi_version() == 102
 
 
 def test_num_partials(L):
@@ -375,3 +375,29 @@ def test_split_rope_swiglu_validation(L):
     assert L.coda_gemm_rope_ws(*rope, P, -1, None) == ARG
     assert L.coda_gemm_rope_ws(None, *rope[1:], P, 0, None) == NULL
     assert L.coda_gemm_rope_ws(P, P, P, P, 0, 8, 8, 8, 8, 8, 8, 0, P, None, 0, None) == OK
+
+
+def test_split_backward_and_cross_entropy_validation(L):
+    # a negative workspace size is refused before any pointer is read (all NULL here)
+    N0 = None
+    assert L.coda_gemm_rmsnorm_bwd_stats_ws(N0, N0, N0, 8, 8, 8, N0, N0, N0, N0, -1, None) == ARG
+    assert L.coda_gemm_rmsnorm_bwd_stats_ws(N0, P, P, 8, 8, 8, P, P, P, P, 0, None) == NULL
+    assert L.coda_gemm_rmsnorm_bwd_stats_ws(P, P, P, 8, 12, 8, P, P, P, P, 0, None) == SHAPE
+    assert L.coda_gemm_rmsnorm_bwd_stats_ws(N0, N0, N0, 0, 8, 8, N0, N0, N0, N0, 0, None) == OK
+    dx = [P, P, P, P, P, P, None]
+    assert L.coda_gemm_rmsnorm_bwd_dx_ws(*([N0] * 7), 8, 8, 8, N0, N0, N0, -1, None) == ARG
+    assert L.coda_gemm_rmsnorm_bwd_dx_ws(N0, *dx[1:], 8, 8, 8, P, P, P, 0, None) == NULL
+    assert L.coda_gemm_rmsnorm_bwd_dx_ws(*dx, 8, 12, 8, P, P, P, 0, None) == SHAPE
+    assert L.coda_gemm_rmsnorm_bwd_dx_ws(*([N0] * 7), 0, 8, 8, N0, N0, N0, 0, None) == OK
+    assert L.coda_gemm_swiglu_bwd_ws(N0, N0, N0, 8, 8, 8, N0, N0, -1, None) == ARG
+    assert L.coda_gemm_swiglu_bwd_ws(N0, P, P, 8, 8, 8, P, P, 0, None) == NULL
+    assert L.coda_gemm_swiglu_bwd_ws(P, P, P, 8, 8, 12, P, P, 0, None) == SHAPE
+    assert L.coda_gemm_swiglu_bwd_ws(N0, N0, N0, 0, 8, 8, N0, N0, 0, None) == OK
+    assert L.coda_gemm_cross_entropy_ws(N0, N0, N0, 8, 8, 8, N0, N0, N0, N0, N0, -1, None) == ARG
+    assert L.coda_gemm_cross_entropy_ws(N0, P, P, 8, 8, 8, P, P, P, P, P, 0, None) == NULL
+    assert L.coda_gemm_cross_entropy_ws(P, P, P, 8, 8, 12, P, P, P, P, P, 0, None) == SHAPE
+    assert L.coda_gemm_cross_entropy_ws(N0, N0, N0, 0, 8, 8, N0, N0, N0, N0, N0, 0, None) == OK
+    rope = [P, P, P, P, 8, 8, 8, 8, 8, 8, 8, 0, P]
+    assert L.coda_gemm_rope_bwd_ws(*rope, P, -1, None) == ARG
+    assert L.coda_gemm_rope_bwd_ws(None, *rope[1:], P, 0, None) == NULL
+    assert L.coda_gemm_rope_bwd_ws(P, P, P, P, 0, 8, 8, 8, 8, 8, 8, 0, P, None, 0, None) == OK

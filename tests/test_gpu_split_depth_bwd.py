@@ -1,0 +1,190 @@
+"""The backward and cross-entropy GEMMs under the split-depth schedule (the *_ws entry
+points), through the C ABI: each output has fewer 256 x 256 tiles than the GPU has CUs, so
+each tile's depth is cut into slices whose fp32 partial tiles go to the caller's
+workspace, and the same epilogue runs on their sum in slice order. Parity with the fp64
+oracle on every element (ragged rows, features and depth; two and eight slices),
+determinism from call to call, and bit-identity with the one-kernel entry point when the
+output is large enough that nothing splits."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_util import assert_close, assert_close_tiles, bf16_bits, log, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+TIGHT = 1e-4  # fp32 outputs against fp64: relative Frobenius bound
+
+
+@pytest.fixture(scope="module")
+def coda():
+    import torch
+    import transformer_gemm_epilogue_amd as c
+    assert torch.cuda.is_available()
+    c.lib()
+    return c
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def dec(t):
+    return O.decode_bf16(bf16_bits(t))
+
+
+# ------------------------------------------------------------ RMSNorm backward statistic
+@pytest.mark.parametrize("shape", [(300, 520, 1096), (517, 264, 4096)])
+def test_bwd_stats_split_depth(coda, shape):
+    M, D, N = shape
+    assert coda.coda_split_workspace_bytes(M, D, N) > 0
+    log(f"bwd_stats split M={M} D={D} N={N}")
+    wl = W.bwd_stats(seed=90 + M % 7, M=M, D=D, N=N)
+    dh2, part, s = coda.coda_gemm_rmsnorm_bwd_stats_ws(to_dev_bf16(wl["dy"]), to_dev_bf16(wl["w1"]),
+                                                       to_dev_bf16(wl["h2"]))
+    sync()
+    ref = O.gemm_rmsnorm_bwd_stats(wl["dy"], wl["w1"], wl["h2"])
+    assert_close_tiles("dh2", dec(dh2), ref["dh2"])
+    assert_close_tiles("partials", part.cpu().numpy(), ref["partials"], rel_fro=TIGHT, tile_n=1)
+    assert_close_tiles("s", s.cpu().numpy(), ref["s_prime"], rel_fro=TIGHT)
+
+
+# ------------------------------------------------------------ RMSNorm backward, dh1 / dgamma
+@pytest.mark.parametrize("shape", [(517, 392, 1064), (300, 264, 4096)])
+def test_rmsnorm_bwd_dx_split_depth(coda, shape):
+    """dh1 and the dgamma column partials from the grad GEMM dy W1^T split over its depth
+    N, with s and r as the GPU path has them (the row-dot of dy and the forward's y)."""
+    import torch
+    M, D, N = shape
+    assert coda.coda_split_workspace_bytes(M, D, N) > 0
+    log(f"rmsnorm_bwd_dx split M={M} D={D} N={N}")
+    wl = W.rmsnorm_bwd_full(93 + M % 5, M, D, N)
+    dev = {k: to_dev_bf16(wl[k]) for k in ("h1", "gamma", "w1", "dy", "g_res")}
+    h = dev["h1"].float()
+    r = torch.rsqrt((h * h).mean(dim=1) + wl["eps"]).contiguous()
+    h2 = (h * dev["gamma"].float()).to(torch.bfloat16).contiguous()
+    y = coda.coda_gemm_rowscale(h2, dev["w1"], r)
+    s = coda.coda_rowdot_stat(dev["dy"], y, D)
+    dh1, part = coda.coda_gemm_rmsnorm_bwd_dx_ws(dev["dy"], dev["w1"], dev["h1"], dev["gamma"], r, s,
+                                                 g_res=dev["g_res"])
+    dgamma = coda.coda_colsum_reduce(part)
+    sync()
+    ref = O.rmsnorm_bwd(wl["h1"], wl["gamma"], wl["w1"], wl["dy"], wl["eps"], g_res=wl["g_res"])
+    assert_close_tiles("dh1", dec(dh1), ref["dh1"])
+    assert_close_tiles("dgamma_partials", part.cpu().numpy(), ref["dgamma_partials"], rel_fro=TIGHT, tile_m=1)
+    assert_close("dgamma", dgamma.cpu().numpy(), ref["dgamma"], rel_fro=TIGHT)
+
+
+# ------------------------------------------------------------ SwiGLU backward
+@pytest.mark.parametrize("shape", [(333, 1040, 136), (300, 4096, 264)])
+def test_swiglu_bwd_split_depth(coda, shape):
+    M, Dm, F = shape
+    assert coda.coda_split_workspace_bytes(M, F, Dm) > 0
+    log(f"swiglu_bwd split M={M} Dm={Dm} F={F}")
+    wl = W.swiglu_bwd(seed=95 + M % 3, M=M, Dm=Dm, F=F)
+    dh = coda.coda_gemm_swiglu_bwd_ws(to_dev_bf16(wl["dy"]), to_dev_bf16(wl["w_down"]), to_dev_bf16(wl["h"]))
+    sync()
+    ref = O.gemm_swiglu_bwd(wl["dy"], wl["w_down"], wl["h"])["dh"]
+    got = dec(dh)
+    assert_close_tiles("dG", got[:, 0::2], ref[:, 0::2])
+    assert_close_tiles("dU", got[:, 1::2], ref[:, 1::2])
+
+
+# ------------------------------------------------------------ RoPE backward
+def test_rope_bwd_split_depth(coda):
+    wl = W.rope_bwd(seed=97, M=300, K=1032, n_q=256, n_k=128, n_v=128, head_dim=128, seq_len=300, pos_offset=11)
+    assert coda.coda_split_workspace_bytes(300, 512, 1032) > 0
+    log("rope_bwd split M=300 K=1032 N=512")
+    c, s = coda.coda_rope_tables(wl["seq_len"], wl["head_dim"], wl["theta"])
+    out = coda.coda_gemm_rope_bwd_ws(to_dev_bf16(wl["x"]), to_dev_bf16(wl["w"]), c, s, wl["n_q"], wl["n_k"],
+                                     wl["n_v"], wl["head_dim"], wl["seq_len"], wl["pos_offset"])
+    sync()
+    ref = O.gemm_rope_bwd(wl["x"], wl["w"], wl["n_q"], wl["n_k"], wl["n_v"], wl["head_dim"], wl["seq_len"],
+                          wl["pos_offset"], wl["theta"])
+    assert_close_tiles("dqkv", dec(out), ref)
+
+
+# ------------------------------------------------------------ cross-entropy
+def run_ce(coda, wl, split=True):
+    import torch
+    labels = torch.from_numpy(wl["labels"]).cuda()
+    fn = coda.coda_gemm_cross_entropy_ws if split else coda.coda_gemm_cross_entropy
+    out = fn(to_dev_bf16(wl["x"]), to_dev_bf16(wl["w"]), labels)
+    sync()
+    return [t.cpu().numpy() for t in out]
+
+
+@pytest.mark.parametrize("shape", [(300, 1024, 1000), (40, 4096, 2056)])
+def test_cross_entropy_split_depth(coda, shape):
+    M, K, V = shape
+    assert coda.coda_split_workspace_bytes(M, V, K) > 0
+    log(f"cross_entropy split M={M} K={K} V={V}")
+    wl = W.cross_entropy(seed=99 + M % 5, M=M, K=K, V=V, ignore_every=7)
+    loss, lse, target, tile = run_ce(coda, wl)
+    ref = O.gemm_cross_entropy(wl["x"], wl["w"], wl["labels"])
+    assert_close_tiles("tile_lse", tile, ref["tile_lse"], rel_fro=TIGHT, tile_n=1)
+    assert_close_tiles("lse", lse, ref["lse"], rel_fro=TIGHT)
+    assert_close_tiles("target", target, ref["target"], rel_fro=TIGHT)
+    assert_close_tiles("loss", loss, ref["loss"], rel_fro=TIGHT)
+    assert np.all(loss[~ref["valid"]] == 0) and np.all(target[~ref["valid"]] == 0)
+
+
+def test_split_depth_backward_is_deterministic(coda):
+    wl = W.cross_entropy(seed=101, M=300, K=1024, V=1000, ignore_every=7)
+    a, b = run_ce(coda, wl), run_ce(coda, wl)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    wl = W.swiglu_bwd(seed=102, M=333, Dm=1040, F=136)
+    args = (to_dev_bf16(wl["dy"]), to_dev_bf16(wl["w_down"]), to_dev_bf16(wl["h"]))
+    u = bf16_bits(coda.coda_gemm_swiglu_bwd_ws(*args))
+    v = bf16_bits(coda.coda_gemm_swiglu_bwd_ws(*args))
+    assert np.array_equal(u, v)
+
+
+def test_no_split_equals_one_kernel_schedule_backward(coda):
+    """Outputs of at least half as many tiles as CUs do not split: the *_ws entry points
+    then run the one-kernel schedule, bit for bit."""
+    M, K, V = 4096, 256, 4096
+    assert coda.coda_split_workspace_bytes(M, V, K) == 0
+    wl = W.cross_entropy(seed=103, M=M, K=K, V=V, ignore_every=11)
+    for u, v in zip(run_ce(coda, wl), run_ce(coda, wl, split=False)):
+        assert np.array_equal(u, v)
+    M, Dm, F = 4096, 256, 4096
+    assert coda.coda_split_workspace_bytes(M, F, Dm) == 0
+    wl = W.swiglu_bwd(seed=104, M=M, Dm=Dm, F=F)
+    args = (to_dev_bf16(wl["dy"]), to_dev_bf16(wl["w_down"]), to_dev_bf16(wl["h"]))
+    assert np.array_equal(bf16_bits(coda.coda_gemm_swiglu_bwd_ws(*args)), bf16_bits(coda.coda_gemm_swiglu_bwd(*args)))
+
+
+def test_split_depth_backward_workspace_errors(coda):
+    import torch
+    L = coda.lib()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    M, Dm, F = 333, 1040, 136
+    need = coda.coda_split_workspace_bytes(M, F, Dm)
+    dy = torch.zeros((M, Dm), dtype=torch.bfloat16, device="cuda")
+    wd = torch.zeros((F, Dm), dtype=torch.bfloat16, device="cuda")
+    h = torch.zeros((M, 2 * F), dtype=torch.bfloat16, device="cuda")
+    dh = torch.empty((M, 2 * F), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    args = [p(dy), p(wd), p(h), M, Dm, F, p(dh)]
+    assert L.coda_gemm_swiglu_bwd_ws(*args, p(ws), need - 16, None) == 4      # CODA_ERR_WORKSPACE
+    assert L.coda_gemm_swiglu_bwd_ws(*args, None, 0, None) == 1               # CODA_ERR_NULL
+    assert L.coda_gemm_swiglu_bwd_ws(*args, p(h), need, None) == 6            # workspace on an input
+    assert L.coda_gemm_swiglu_bwd_ws(*args, p(ws), need, None) == 0
+    M, K, V = 300, 1024, 1000
+    need = coda.coda_split_workspace_bytes(M, V, K)
+    x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((K, V), dtype=torch.bfloat16, device="cuda")
+    labels = torch.zeros((M,), dtype=torch.int32, device="cuda")
+    f = [torch.empty((M, coda.num_partials(V)), dtype=torch.float32, device="cuda")] + \
+        [torch.empty((M,), dtype=torch.float32, device="cuda") for _ in range(3)]
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    args = [p(x), p(w), p(labels), M, K, V] + [p(t) for t in f]
+    assert L.coda_gemm_cross_entropy_ws(*args, p(ws), need - 16, None) == 4
+    assert L.coda_gemm_cross_entropy_ws(*args, p(f[0]), need, None) == 6       # workspace on an output
+    assert L.coda_gemm_cross_entropy_ws(*args, p(ws), need, None) == 0
+    sync()

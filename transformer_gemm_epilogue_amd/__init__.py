@@ -40,14 +40,19 @@ __all__ = [
     "coda_gemm_rope_ws",
     "coda_split_workspace_bytes",
     "coda_gemm_rmsnorm_bwd_stats",
+    "coda_gemm_rmsnorm_bwd_stats_ws",
     "num_row_tiles",
     "coda_rowdot_stat",
     "coda_gemm_rmsnorm_bwd_dx",
+    "coda_gemm_rmsnorm_bwd_dx_ws",
     "coda_colsum_reduce",
     "coda_rmsnorm_bwd",
     "coda_gemm_rope_bwd",
+    "coda_gemm_rope_bwd_ws",
     "coda_gemm_swiglu_bwd",
+    "coda_gemm_swiglu_bwd_ws",
     "coda_gemm_cross_entropy",
+    "coda_gemm_cross_entropy_ws",
     "coda_lse_reduce",
     "coda_baseline_gemm",
     "coda_baseline_residual_rmsnorm",
@@ -89,14 +94,19 @@ SIGNATURES = {
     "coda_gemm_swiglu_ws": [_P, _P, _I, _I, _I, _P, _P, _I64, _P],
     "coda_split_workspace_bytes": [_I, _I, _I, ctypes.POINTER(_I64)],
     "coda_gemm_rope_bwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P],
+    "coda_gemm_rope_bwd_ws": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I64, _P],
     "coda_gemm_swiglu_bwd": [_P, _P, _P, _I, _I, _I, _P, _P],
+    "coda_gemm_swiglu_bwd_ws": [_P, _P, _P, _I, _I, _I, _P, _P, _I64, _P],
     "coda_gemm_cross_entropy": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P],
+    "coda_gemm_cross_entropy_ws": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _I64, _P],
     "coda_lse_reduce": [_P, _P, _I, _I, _I, _P, _P, _P, _P],
     "coda_gemm_rmsnorm_bwd_stats": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
+    "coda_gemm_rmsnorm_bwd_stats_ws": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _I64, _P],
     "coda_colstat_num_partials": [_I, _P],
     "coda_rowdot_stat": [_P, _P, _I, _I, _I, _P, _P],
     "coda_colsum_reduce": [_P, _I, _I, _P, _P],
     "coda_gemm_rmsnorm_bwd_dx": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P],
+    "coda_gemm_rmsnorm_bwd_dx_ws": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _I64, _P],
     "coda_rmsnorm_bwd": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P],
     "coda_baseline_gemm": [_P, _P, _I, _I, _I, _I, _P, _P],
     "coda_baseline_residual_rmsnorm": [_P, _P, _P, _I, _I, _F, _P, _P, _P, _P],
@@ -319,15 +329,24 @@ def coda_rope_tables(seq_len, head_dim, theta=10000.0, device="cuda", stream=Non
     return cos_t, sin_t
 
 
-def _gemm_rope(name, x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, stream):
+def _split_args(split, need, like, workspace):
+    """The (workspace, bytes) arguments of a split-depth entry point (none otherwise)."""
+    if not split:
+        return ()
+    return _workspace(need() if workspace is None else 0, like, workspace)
+
+
+def _gemm_rope(name, x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, stream, split=False,
+               workspace=None):
     torch = _torch()
     M, K = x.shape
     N = n_q + n_k + n_v
     if w.shape != (K, N):
         raise ValueError(f"{name}: w must be [K, n_q + n_k + n_v]")
     out = _empty((M, N), torch.bfloat16, x) if out is None else out
+    ws = _split_args(split, lambda: coda_split_workspace_bytes(M, N, K), x, workspace)
     _call(name, _bf16(x, "x"), _bf16(w, "w"), _f32(cos_t, "cos_t"), _f32(sin_t, "sin_t"), M, K,
-          n_q, n_k, n_v, head_dim, seq_len, pos_offset, _bf16(out, "out"), _stream(stream))
+          n_q, n_k, n_v, head_dim, seq_len, pos_offset, _bf16(out, "out"), *ws, _stream(stream))
     return out
 
 
@@ -353,16 +372,8 @@ def coda_gemm_rope_ws(x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_
                       stream=None):
     """coda_gemm_rope with the split-depth schedule for outputs with fewer tiles than CUs
     (`workspace`: uint8 GPU tensor, allocated here when None)."""
-    torch = _torch()
-    M, K = x.shape
-    N = n_q + n_k + n_v
-    if w.shape != (K, N):
-        raise ValueError("coda_gemm_rope_ws: w must be [K, n_q + n_k + n_v]")
-    out = _empty((M, N), torch.bfloat16, x) if out is None else out
-    ws, nbytes = _workspace(coda_split_workspace_bytes(M, N, K) if workspace is None else 0, x, workspace)
-    _call("coda_gemm_rope_ws", _bf16(x, "x"), _bf16(w, "w"), _f32(cos_t, "cos_t"), _f32(sin_t, "sin_t"), M, K,
-          n_q, n_k, n_v, head_dim, seq_len, pos_offset, _bf16(out, "out"), ws, nbytes, _stream(stream))
-    return out
+    return _gemm_rope("coda_gemm_rope_ws", x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out,
+                      stream, True, workspace)
 
 
 def coda_gemm_rope_persistent(x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset=0, out=None,
@@ -376,6 +387,13 @@ def coda_gemm_rope_bwd(x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos
     """x w with every Q and K pair rotated by the negated angle (the RoPE backward)."""
     return _gemm_rope("coda_gemm_rope_bwd", x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out,
                       stream)
+
+
+def coda_gemm_rope_bwd_ws(x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset=0, out=None,
+                          workspace=None, stream=None):
+    """coda_gemm_rope_bwd with the split-depth schedule."""
+    return _gemm_rope("coda_gemm_rope_bwd_ws", x, w, cos_t, sin_t, n_q, n_k, n_v, head_dim, seq_len, pos_offset,
+                      out, stream, True, workspace)
 
 
 def coda_gemm_swiglu(x, w, out=None, stream=None):
@@ -403,39 +421,61 @@ def coda_gemm_swiglu_ws(x, w, out=None, workspace=None, stream=None):
     return out
 
 
-def coda_gemm_swiglu_bwd(dy, w_down, h, dh=None, stream=None):
-    """dOut = dy w_down^T mapped in the epilogue to the interleaved (gate, up) gradients
-    of the saved pre-activations h [M, 2F]. Returns dh [M, 2F]."""
+def _swiglu_bwd(name, dy, w_down, h, dh, stream, split=False, workspace=None):
     torch = _torch()
     M, Dm = dy.shape
     F = w_down.shape[0]
     if w_down.shape[1] != Dm or h.shape != (M, 2 * F):
-        raise ValueError("coda_gemm_swiglu_bwd: inconsistent shapes")
+        raise ValueError(f"{name}: inconsistent shapes")
     dh = _empty((M, 2 * F), torch.bfloat16, dy) if dh is None else dh
-    _call("coda_gemm_swiglu_bwd", _bf16(dy, "dy"), _bf16(w_down, "w_down"), _bf16(h, "h"), M, Dm, F,
-          _bf16(dh, "dh"), _stream(stream))
+    ws = _split_args(split, lambda: coda_split_workspace_bytes(M, F, Dm), dy, workspace)
+    _call(name, _bf16(dy, "dy"), _bf16(w_down, "w_down"), _bf16(h, "h"), M, Dm, F, _bf16(dh, "dh"), *ws,
+          _stream(stream))
     return dh
+
+
+def coda_gemm_swiglu_bwd(dy, w_down, h, dh=None, stream=None):
+    """dOut = dy w_down^T mapped in the epilogue to the interleaved (gate, up) gradients
+    of the saved pre-activations h [M, 2F]. Returns dh [M, 2F]."""
+    return _swiglu_bwd("coda_gemm_swiglu_bwd", dy, w_down, h, dh, stream)
+
+
+def coda_gemm_swiglu_bwd_ws(dy, w_down, h, dh=None, workspace=None, stream=None):
+    """coda_gemm_swiglu_bwd with the split-depth schedule (output width F, depth Dm)."""
+    return _swiglu_bwd("coda_gemm_swiglu_bwd_ws", dy, w_down, h, dh, stream, True, workspace)
 
 
 def _i32(t, name):
     return _dev(t, _torch().int32, name)
 
 
-def coda_gemm_cross_entropy(x, w, labels, tile_lse=None, target=None, lse=None, loss=None, stream=None):
-    """Cross-entropy of the logits x w (never stored) against int32 labels (outside
-    [0, V): ignored, loss 0). Returns (loss, lse, target, tile_lse)."""
+def _cross_entropy(name, x, w, labels, tile_lse, target, lse, loss, stream, split=False, workspace=None):
     torch = _torch()
     M, K = x.shape
     V = w.shape[1]
     if w.shape[0] != K or labels.shape != (M,):
-        raise ValueError("coda_gemm_cross_entropy: inconsistent shapes")
+        raise ValueError(f"{name}: inconsistent shapes")
     tile_lse = _empty((M, num_partials(V)), torch.float32, x) if tile_lse is None else tile_lse
     target = _empty((M,), torch.float32, x) if target is None else target
     lse = _empty((M,), torch.float32, x) if lse is None else lse
     loss = _empty((M,), torch.float32, x) if loss is None else loss
-    _call("coda_gemm_cross_entropy", _bf16(x, "x"), _bf16(w, "w"), _i32(labels, "labels"), M, K, V,
-          _f32(tile_lse, "tile_lse"), _f32(target, "target"), _f32(lse, "lse"), _f32(loss, "loss"), _stream(stream))
+    ws = _split_args(split, lambda: coda_split_workspace_bytes(M, V, K), x, workspace)
+    _call(name, _bf16(x, "x"), _bf16(w, "w"), _i32(labels, "labels"), M, K, V, _f32(tile_lse, "tile_lse"),
+          _f32(target, "target"), _f32(lse, "lse"), _f32(loss, "loss"), *ws, _stream(stream))
     return loss, lse, target, tile_lse
+
+
+def coda_gemm_cross_entropy(x, w, labels, tile_lse=None, target=None, lse=None, loss=None, stream=None):
+    """Cross-entropy of the logits x w (never stored) against int32 labels (outside
+    [0, V): ignored, loss 0). Returns (loss, lse, target, tile_lse)."""
+    return _cross_entropy("coda_gemm_cross_entropy", x, w, labels, tile_lse, target, lse, loss, stream)
+
+
+def coda_gemm_cross_entropy_ws(x, w, labels, tile_lse=None, target=None, lse=None, loss=None, workspace=None,
+                               stream=None):
+    """coda_gemm_cross_entropy with the split-depth schedule."""
+    return _cross_entropy("coda_gemm_cross_entropy_ws", x, w, labels, tile_lse, target, lse, loss, stream, True,
+                          workspace)
 
 
 def coda_lse_reduce(tile_lse, labels, V, target, lse=None, loss=None, stream=None):
@@ -449,20 +489,30 @@ def coda_lse_reduce(tile_lse, labels, V, target, lse=None, loss=None, stream=Non
     return loss, lse
 
 
-def coda_gemm_rmsnorm_bwd_stats(dy, w1, h2, dh2=None, partials=None, s=None, stream=None):
-    """dh2 = dy w1^T with row partials of dh2 * h2 in the epilogue, then s = mean.
-    Returns (dh2, partials, s)."""
+def _bwd_stats(name, dy, w1, h2, dh2, partials, s, stream, split=False, workspace=None):
     torch = _torch()
     M, N = dy.shape
     D = w1.shape[0]
     if w1.shape[1] != N or h2.shape != (M, D):
-        raise ValueError("coda_gemm_rmsnorm_bwd_stats: inconsistent shapes")
+        raise ValueError(f"{name}: inconsistent shapes")
     dh2 = _empty((M, D), torch.bfloat16, dy) if dh2 is None else dh2
     partials = _empty((M, num_partials(D)), torch.float32, dy) if partials is None else partials
     s = _empty((M,), torch.float32, dy) if s is None else s
-    _call("coda_gemm_rmsnorm_bwd_stats", _bf16(dy, "dy"), _bf16(w1, "w1"), _bf16(h2, "h2"), M, D, N,
-          _bf16(dh2, "dh2"), _f32(partials, "partials"), _f32(s, "s"), _stream(stream))
+    ws = _split_args(split, lambda: coda_split_workspace_bytes(M, D, N), dy, workspace)
+    _call(name, _bf16(dy, "dy"), _bf16(w1, "w1"), _bf16(h2, "h2"), M, D, N, _bf16(dh2, "dh2"),
+          _f32(partials, "partials"), _f32(s, "s"), *ws, _stream(stream))
     return dh2, partials, s
+
+
+def coda_gemm_rmsnorm_bwd_stats(dy, w1, h2, dh2=None, partials=None, s=None, stream=None):
+    """dh2 = dy w1^T with row partials of dh2 * h2 in the epilogue, then s = mean.
+    Returns (dh2, partials, s)."""
+    return _bwd_stats("coda_gemm_rmsnorm_bwd_stats", dy, w1, h2, dh2, partials, s, stream)
+
+
+def coda_gemm_rmsnorm_bwd_stats_ws(dy, w1, h2, dh2=None, partials=None, s=None, workspace=None, stream=None):
+    """coda_gemm_rmsnorm_bwd_stats with the split-depth schedule (output width D, depth N)."""
+    return _bwd_stats("coda_gemm_rmsnorm_bwd_stats_ws", dy, w1, h2, dh2, partials, s, stream, True, workspace)
 
 
 def num_row_tiles(rows: int) -> int:
@@ -496,21 +546,33 @@ def coda_colsum_reduce(partials, out=None, stream=None):
     return out
 
 
-def coda_gemm_rmsnorm_bwd_dx(dy, w1, h1, gamma, r, s, g_res=None, dh1=None, dgamma_partials=None, stream=None):
-    """Grad GEMM dO = dy w1^T whose epilogue stores dh1 = r gamma dO - r^2 s h1 (+ g_res)
-    and the dgamma column partials. Returns (dh1, dgamma_partials)."""
+def _bwd_dx(name, dy, w1, h1, gamma, r, s, g_res, dh1, dgamma_partials, stream, split=False, workspace=None):
     torch = _torch()
     M, N = dy.shape
     D = w1.shape[0]
     if w1.shape[1] != N or h1.shape != (M, D) or gamma.shape != (D,) or r.shape != (M,) or s.shape != (M,) \
             or (g_res is not None and g_res.shape != (M, D)):
-        raise ValueError("coda_gemm_rmsnorm_bwd_dx: inconsistent shapes")
+        raise ValueError(f"{name}: inconsistent shapes")
     dh1 = _empty((M, D), torch.bfloat16, dy) if dh1 is None else dh1
     dgamma_partials = _empty((num_row_tiles(M), D), torch.float32, dy) if dgamma_partials is None else dgamma_partials
-    _call("coda_gemm_rmsnorm_bwd_dx", _bf16(dy, "dy"), _bf16(w1, "w1"), _bf16(h1, "h1"), _bf16(gamma, "gamma"),
-          _f32(r, "r"), _f32(s, "s"), _opt_bf16(g_res, "g_res"), M, D, N, _bf16(dh1, "dh1"),
-          _f32(dgamma_partials, "dgamma_partials"), _stream(stream))
+    ws = _split_args(split, lambda: coda_split_workspace_bytes(M, D, N), dy, workspace)
+    _call(name, _bf16(dy, "dy"), _bf16(w1, "w1"), _bf16(h1, "h1"), _bf16(gamma, "gamma"), _f32(r, "r"),
+          _f32(s, "s"), _opt_bf16(g_res, "g_res"), M, D, N, _bf16(dh1, "dh1"),
+          _f32(dgamma_partials, "dgamma_partials"), *ws, _stream(stream))
     return dh1, dgamma_partials
+
+
+def coda_gemm_rmsnorm_bwd_dx(dy, w1, h1, gamma, r, s, g_res=None, dh1=None, dgamma_partials=None, stream=None):
+    """Grad GEMM dO = dy w1^T whose epilogue stores dh1 = r gamma dO - r^2 s h1 (+ g_res)
+    and the dgamma column partials. Returns (dh1, dgamma_partials)."""
+    return _bwd_dx("coda_gemm_rmsnorm_bwd_dx", dy, w1, h1, gamma, r, s, g_res, dh1, dgamma_partials, stream)
+
+
+def coda_gemm_rmsnorm_bwd_dx_ws(dy, w1, h1, gamma, r, s, g_res=None, dh1=None, dgamma_partials=None, workspace=None,
+                                stream=None):
+    """coda_gemm_rmsnorm_bwd_dx with the split-depth schedule (output width D, depth N)."""
+    return _bwd_dx("coda_gemm_rmsnorm_bwd_dx_ws", dy, w1, h1, gamma, r, s, g_res, dh1, dgamma_partials, stream, True,
+                   workspace)
 
 
 def coda_rmsnorm_bwd(dy, w1, h1, gamma, r, y, g_res=None, s=None, dh1=None, dgamma_partials=None, dgamma=None,

@@ -4,6 +4,7 @@
 // the SwiGLU backward pairwise map on the down projection's grad GEMM.
 #include "coda_abi.hpp"
 #include "coda_bwd.hpp"
+#include "coda_launch.hpp"
 
 using namespace coda;
 
@@ -110,15 +111,14 @@ int launch_rowdot(const uint16_t* dy, const uint16_t* y, int M, int N, int d, fl
   return launch_status();
 }
 
+// sp: the split-depth plan (S == 1: the one-kernel schedule) and ws its workspace.
 int launch_dx(const uint16_t* dy, const uint16_t* w1, const uint16_t* h1, const uint16_t* gamma, const float* r,
               const float* s, const uint16_t* g_res, int M, int D, int N, uint16_t* dh1, float* pgamma,
-              hipStream_t st) {
+              hipStream_t st, const SplitPlan& sp = SplitPlan{1, 0}, float* ws = nullptr) {
   // dy [M, N] times W1^T: depth = N, output width = D; W1 [D, N] is the NK layout.
   const GemmProblem p{dy, w1, M, D, N};
   const EpiRmsNormBwd::Args ea{h1, gamma, r, s, g_res, dh1, pgamma};
-  hipLaunchKernelGGL((gemm_epilogue_kernel<false, EpiRmsNormBwd>), dim3(gemm_grid(M, D)), dim3(kThreads), 0, st, p,
-                     ea);
-  return launch_status();
+  return launch_gemm_split<false, EpiRmsNormBwd>(p, ea, sp, ws, st);
 }
 
 int launch_colsum(const float* P, int tiles, int width, float* out, hipStream_t st) {
@@ -127,6 +127,35 @@ int launch_colsum(const float* P, int tiles, int width, float* out, hipStream_t 
   else
     hipLaunchKernelGGL(colsum_reduce_kernel, dim3(blocks(width, 256)), dim3(256), 0, st, P, tiles, width, out);
   return launch_status();
+}
+
+int gemm_swiglu_bwd(const uint16_t* dy, const uint16_t* w_down, const uint16_t* h, int M, int Dm, int F, uint16_t* dh,
+                    bool split, void* workspace, long long workspace_bytes, hipStream_t st) {
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(Dm));
+  if (F < 8 || F % 8 != 0 || 2LL * F > kMaxDim) return CODA_ERR_SHAPE;
+  if (split && workspace_bytes < 0) return CODA_ERR_ARG;
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(dy);
+  CODA_NONNULL(w_down);
+  CODA_NONNULL(h);
+  CODA_NONNULL(dh);
+  CODA_ALIGN16(dy);
+  CODA_ALIGN16(w_down);
+  CODA_ALIGN16(h);
+  CODA_ALIGN16(dh);
+  CODA_TRY(check_disjoint({bf16_span(dh, M, 2LL * F)},
+                          {bf16_span(dy, M, Dm), bf16_span(w_down, F, Dm), bf16_span(h, M, 2LL * F)}));
+  // dy [M, Dm] times W_down^T: depth = Dm, output width = F; W_down [F, Dm] is the NK layout.
+  const GemmProblem p{dy, w_down, M, F, Dm};
+  const EpiSwiGLUBwd::Args ea{h, dh};
+  SplitPlan sp{1, 0};
+  if (split)
+    CODA_TRY(split_for_call(M, F, Dm, workspace, workspace_bytes,
+                            {bf16_span(dh, M, 2LL * F), bf16_span(dy, M, Dm), bf16_span(w_down, F, Dm),
+                             bf16_span(h, M, 2LL * F)},
+                            &sp));
+  return launch_gemm_split<false, EpiSwiGLUBwd>(p, ea, sp, static_cast<float*>(workspace), st);
 }
 
 }  // namespace
@@ -167,6 +196,26 @@ int coda_gemm_rmsnorm_bwd_dx(const uint16_t* dy, const uint16_t* w1, const uint1
   return launch_dx(dy, w1, h1, gamma, r, s, g_res, M, D, N, dh1, dgamma_partials, as_stream(stream));
 }
 
+int coda_gemm_rmsnorm_bwd_dx_ws(const uint16_t* dy, const uint16_t* w1, const uint16_t* h1, const uint16_t* gamma,
+                                const float* r, const float* s, const uint16_t* g_res, int M, int D, int N,
+                                uint16_t* dh1, float* dgamma_partials, void* workspace, long long workspace_bytes,
+                                void* stream) {
+  if (workspace_bytes < 0) return CODA_ERR_ARG;
+  CODA_TRY(check_dx(dy, w1, h1, gamma, r, s, g_res, M, D, N, dh1, dgamma_partials));
+  if (M == 0) return CODA_OK;
+  CODA_TRY(check_disjoint({bf16_span(dh1, M, D), f32_span(dgamma_partials, row_tiles(M), D)},
+                          {bf16_span(dy, M, N), bf16_span(w1, D, N), bf16_span(h1, M, D), bf16_span(gamma, D),
+                           f32_span(r, M), f32_span(s, M), bf16_span(g_res, M, D)}));
+  SplitPlan sp;
+  CODA_TRY(split_for_call(M, D, N, workspace, workspace_bytes,
+                          {bf16_span(dh1, M, D), f32_span(dgamma_partials, row_tiles(M), D), bf16_span(dy, M, N),
+                           bf16_span(w1, D, N), bf16_span(h1, M, D), bf16_span(gamma, D), f32_span(r, M),
+                           f32_span(s, M), bf16_span(g_res, M, D)},
+                          &sp));
+  return launch_dx(dy, w1, h1, gamma, r, s, g_res, M, D, N, dh1, dgamma_partials, as_stream(stream), sp,
+                   static_cast<float*>(workspace));
+}
+
 int coda_rmsnorm_bwd(const uint16_t* dy, const uint16_t* w1, const uint16_t* h1, const uint16_t* gamma,
                      const float* r, const uint16_t* y, const uint16_t* g_res, int M, int D, int N, float* s,
                      uint16_t* dh1, float* dgamma_partials, float* dgamma, void* stream) {
@@ -190,26 +239,12 @@ int coda_rmsnorm_bwd(const uint16_t* dy, const uint16_t* w1, const uint16_t* h1,
 
 int coda_gemm_swiglu_bwd(const uint16_t* dy, const uint16_t* w_down, const uint16_t* h, int M, int Dm, int F,
                          uint16_t* dh, void* stream) {
-  CODA_TRY(check_rows(M));
-  CODA_TRY(check_depth_or_width(Dm));
-  if (F < 8 || F % 8 != 0 || 2LL * F > kMaxDim) return CODA_ERR_SHAPE;
-  if (M == 0) return CODA_OK;
-  CODA_NONNULL(dy);
-  CODA_NONNULL(w_down);
-  CODA_NONNULL(h);
-  CODA_NONNULL(dh);
-  CODA_ALIGN16(dy);
-  CODA_ALIGN16(w_down);
-  CODA_ALIGN16(h);
-  CODA_ALIGN16(dh);
-  CODA_TRY(check_disjoint({bf16_span(dh, M, 2LL * F)},
-                          {bf16_span(dy, M, Dm), bf16_span(w_down, F, Dm), bf16_span(h, M, 2LL * F)}));
-  // dy [M, Dm] times W_down^T: depth = Dm, output width = F; W_down [F, Dm] is the NK layout.
-  const GemmProblem p{dy, w_down, M, F, Dm};
-  const EpiSwiGLUBwd::Args ea{h, dh};
-  hipLaunchKernelGGL((gemm_epilogue_kernel<false, EpiSwiGLUBwd>), dim3(gemm_grid(M, F)), dim3(kThreads), 0,
-                     as_stream(stream), p, ea);
-  return launch_status();
+  return gemm_swiglu_bwd(dy, w_down, h, M, Dm, F, dh, false, nullptr, 0, as_stream(stream));
+}
+
+int coda_gemm_swiglu_bwd_ws(const uint16_t* dy, const uint16_t* w_down, const uint16_t* h, int M, int Dm, int F,
+                            uint16_t* dh, void* workspace, long long workspace_bytes, void* stream) {
+  return gemm_swiglu_bwd(dy, w_down, h, M, Dm, F, dh, true, workspace, workspace_bytes, as_stream(stream));
 }
 
 }  // extern "C"

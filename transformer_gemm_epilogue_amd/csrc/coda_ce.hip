@@ -3,6 +3,7 @@
 // merge into lse and the loss.
 #include "coda_abi.hpp"
 #include "coda_ce.hpp"
+#include "coda_launch.hpp"
 
 using namespace coda;
 
@@ -122,6 +123,36 @@ int launch_lse(const float* P, const int32_t* labels, int M, int nb, int V, floa
   return launch_status();
 }
 
+int gemm_ce(const uint16_t* x, const uint16_t* w, const int32_t* labels, int M, int K, int V, float* tile_lse,
+            float* target, float* lse, float* loss, bool split, void* workspace, long long workspace_bytes,
+            hipStream_t st) {
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(K));
+  CODA_TRY(check_depth_or_width(V));
+  if (split && workspace_bytes < 0) return CODA_ERR_ARG;
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(x);
+  CODA_NONNULL(w);
+  CODA_NONNULL(tile_lse);
+  CODA_ALIGN16(x);
+  CODA_ALIGN16(w);
+  if (!aligned(tile_lse, 4)) return CODA_ERR_ALIGN;
+  const int nb = (V + kBN - 1) / kBN;
+  CODA_TRY(check_ce_outputs(labels, target, lse, loss));
+  CODA_TRY(check_disjoint({f32_span(tile_lse, M, nb), f32_span(target, M), f32_span(lse, M), f32_span(loss, M)},
+                          {bf16_span(x, M, K), bf16_span(w, K, V), Span{labels, (uint64_t)M * 4u}}));
+  const GemmProblem p{x, w, M, V, K};
+  const EpiCrossEntropy::Args ea{labels, tile_lse, target, nb};
+  SplitPlan sp{1, 0};
+  if (split)
+    CODA_TRY(split_for_call(M, V, K, workspace, workspace_bytes,
+                            {f32_span(tile_lse, M, nb), f32_span(target, M), f32_span(lse, M), f32_span(loss, M),
+                             bf16_span(x, M, K), bf16_span(w, K, V), Span{labels, (uint64_t)M * 4u}},
+                            &sp));
+  CODA_TRY((launch_gemm_split<true, EpiCrossEntropy>(p, ea, sp, static_cast<float*>(workspace), st)));
+  return launch_lse(tile_lse, labels, M, nb, V, target, lse, loss, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -143,31 +174,14 @@ int coda_lse_reduce(const float* tile_lse, const int32_t* labels, int M, int nb,
 
 int coda_gemm_cross_entropy(const uint16_t* x, const uint16_t* w, const int32_t* labels, int M, int K, int V,
                             float* tile_lse, float* target, float* lse, float* loss, void* stream) {
-  CODA_TRY(check_rows(M));
-  CODA_TRY(check_depth_or_width(K));
-  CODA_TRY(check_depth_or_width(V));
-  if (M == 0) return CODA_OK;
-  CODA_NONNULL(x);
-  CODA_NONNULL(w);
-  CODA_NONNULL(tile_lse);
-  CODA_ALIGN16(x);
-  CODA_ALIGN16(w);
-  if (!aligned(tile_lse, 4)) return CODA_ERR_ALIGN;
-  const int nb = (V + kBN - 1) / kBN;
-  CODA_TRY(check_ce_outputs(labels, target, lse, loss));
-  CODA_TRY(check_disjoint({f32_span(tile_lse, M, nb), f32_span(target, M), f32_span(lse, M), f32_span(loss, M)},
-                          {bf16_span(x, M, K), bf16_span(w, K, V), Span{labels, (uint64_t)M * 4u}}));
-  const hipStream_t st = as_stream(stream);
-  const GemmProblem p{x, w, M, V, K};
-  const EpiCrossEntropy::Args ea{labels, tile_lse, target, nb};
-  if (kn_one_descriptor_fits(K, V))
-    hipLaunchKernelGGL((gemm_epilogue_kernel<true, EpiCrossEntropy, true>), dim3(gemm_grid(M, V)), dim3(kThreads), 0,
-                       st, p, ea);
-  else
-    hipLaunchKernelGGL((gemm_epilogue_kernel<true, EpiCrossEntropy>), dim3(gemm_grid(M, V)), dim3(kThreads), 0, st,
-                       p, ea);
-  CODA_TRY(launch_status());
-  return launch_lse(tile_lse, labels, M, nb, V, target, lse, loss, st);
+  return gemm_ce(x, w, labels, M, K, V, tile_lse, target, lse, loss, false, nullptr, 0, as_stream(stream));
+}
+
+int coda_gemm_cross_entropy_ws(const uint16_t* x, const uint16_t* w, const int32_t* labels, int M, int K, int V,
+                               float* tile_lse, float* target, float* lse, float* loss, void* workspace,
+                               long long workspace_bytes, void* stream) {
+  return gemm_ce(x, w, labels, M, K, V, tile_lse, target, lse, loss, true, workspace, workspace_bytes,
+                 as_stream(stream));
 }
 
 }  // extern "C"

@@ -3,7 +3,7 @@
 
 #include "coda_abi.hpp"
 #include "coda_gemm.hpp"
-#include "coda_splitk.hpp"
+#include "coda_launch.hpp"
 
 using namespace coda;
 
@@ -11,64 +11,6 @@ int coda_rowstat_reduce_impl(const float* partials, int M, int nb, int d, float 
                              float* out, hipStream_t stream);
 
 namespace {
-
-template <bool kWKN, class Epi>
-int launch_gemm(const GemmProblem& p, const typename Epi::Args& ea, hipStream_t stream) {
-  const int grid = gemm_grid(p.M, p.N);
-  if constexpr (kWKN) {
-    if (kn_one_descriptor_fits(p.K, p.N)) {
-      hipLaunchKernelGGL((gemm_epilogue_kernel<true, Epi, true>), dim3(grid), dim3(kThreads), 0, stream, p, ea);
-      return launch_status();
-    }
-  }
-  hipLaunchKernelGGL((gemm_epilogue_kernel<kWKN, Epi>), dim3(grid), dim3(kThreads), 0, stream, p, ea);
-  return launch_status();
-}
-
-// Compute units of the current device.
-int device_cus(int* cus) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                               hipSuccess || *cus < 1)
-    return CODA_ERR_HIP;
-  return CODA_OK;
-}
-
-// Split-depth schedule (coda_splitk.hpp) when the plan has more than one slice: the
-// slices' main loops, then the tiles' epilogues on the summed partials (two launches);
-// otherwise the one-kernel schedule. ws holds split_workspace_floats(M, N, sp) floats.
-template <bool kWKN, class Epi>
-int launch_gemm_split(const GemmProblem& p, const typename Epi::Args& ea, const SplitPlan& sp, float* ws,
-                      hipStream_t stream) {
-  if (sp.S <= 1) return launch_gemm<kWKN, Epi>(p, ea, stream);
-  const int T = gemm_grid(p.M, p.N);
-  const dim3 units((unsigned)(((T + 7) / 8) * 8 * sp.S));
-  f32x4_t* w4 = reinterpret_cast<f32x4_t*>(ws);
-  if (kWKN && kn_one_descriptor_fits(p.K, p.N))
-    hipLaunchKernelGGL((gemm_split_kernel<kWKN, kWKN>), units, dim3(kThreads), 0, stream, p, sp.S, sp.steps, w4);
-  else
-    hipLaunchKernelGGL((gemm_split_kernel<kWKN, false>), units, dim3(kThreads), 0, stream, p, sp.S, sp.steps, w4);
-  CODA_TRY(launch_status());
-  hipLaunchKernelGGL((split_epilogue_kernel<Epi>), dim3(T), dim3(kThreads), 0, stream, p, ea, sp.S,
-                     (const f32x4_t*)w4);
-  return launch_status();
-}
-
-// The split plan of one GEMM on the current device and its workspace checks: enough bytes,
-// 16-byte aligned, overlapping none of the call's other buffers (`others`).
-int split_for_call(int M, int N, int K, void* workspace, long long workspace_bytes, std::initializer_list<Span> others,
-                   SplitPlan* sp) {
-  if (workspace_bytes < 0) return CODA_ERR_ARG;
-  int cus = 0;
-  CODA_TRY(device_cus(&cus));
-  *sp = split_plan(M, N, K, cus);
-  const long long need = 4 * split_workspace_floats(M, N, *sp);
-  if (need == 0) return CODA_OK;
-  CODA_NONNULL(workspace);
-  CODA_ALIGN16(workspace);
-  if (workspace_bytes < need) return CODA_ERR_WORKSPACE;
-  return check_disjoint({Span{workspace, (uint64_t)need}}, others);
-}
 
 // Persistent schedule: min(tiles, CUs of the current device) workgroups walk the tiles
 // (one workgroup fills a CU's LDS); below the minimum depth the per-tile kernel runs
@@ -174,7 +116,7 @@ const char* coda_status_string(int status) {
   }
 }
 
-int coda_abi_version(void) { return 101; }
+int coda_abi_version(void) { return 102; }
 
 #ifndef CODA_SOURCE_HASH
 #define CODA_SOURCE_HASH "unknown"
@@ -382,6 +324,44 @@ int gemm_swiglu(const uint16_t* x, const uint16_t* w, int M, int K, int F, uint1
                           {bf16_span(out, M, F), bf16_span(x, M, K), bf16_span(w, K, 2LL * F)}, &sp));
   return launch_gemm_split<true, EpiSwiGLU>(p, ea, sp, static_cast<float*>(workspace), stream);
 }
+int gemm_bwd_stats(const uint16_t* dy, const uint16_t* w1, const uint16_t* h2, int M, int D, int N, uint16_t* dh2,
+                   float* partials, float* s, bool split, void* workspace, long long workspace_bytes,
+                   hipStream_t st) {
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(D));
+  CODA_TRY(check_depth_or_width(N));
+  if (split && workspace_bytes < 0) return CODA_ERR_ARG;
+  if (M == 0) return CODA_OK;
+  CODA_NONNULL(dy);
+  CODA_NONNULL(w1);
+  CODA_NONNULL(h2);
+  CODA_NONNULL(dh2);
+  CODA_NONNULL(partials);
+  CODA_NONNULL(s);
+  CODA_ALIGN16(dy);
+  CODA_ALIGN16(w1);
+  CODA_ALIGN16(h2);
+  CODA_ALIGN16(dh2);
+  if (!aligned(partials, 4) || !aligned(s, 4)) return CODA_ERR_ALIGN;
+  const int nb = (D + kBN - 1) / kBN;
+  CODA_TRY(check_disjoint({bf16_span(dh2, M, D), f32_span(partials, M, nb), f32_span(s, M)},
+                          {bf16_span(dy, M, N), bf16_span(w1, D, N), bf16_span(h2, M, D)}));
+  // dy [M, N] times W1^T: depth = N, output width = D, W1 [D, N] is the NK layout.
+  const GemmProblem p{dy, w1, M, D, N};
+  const EpiDotRowPartials::Args ea{h2, dh2, partials, nb};
+  if (split) {
+    SplitPlan sp;
+    CODA_TRY(split_for_call(M, D, N, workspace, workspace_bytes,
+                            {bf16_span(dh2, M, D), f32_span(partials, M, nb), f32_span(s, M), bf16_span(dy, M, N),
+                             bf16_span(w1, D, N), bf16_span(h2, M, D)},
+                            &sp));
+    CODA_TRY((launch_gemm_split<false, EpiDotRowPartials>(p, ea, sp, static_cast<float*>(workspace), st)));
+  } else {
+    CODA_TRY((launch_gemm<false, EpiDotRowPartials>(p, ea, st)));
+  }
+  return coda_rowstat_reduce_impl(partials, M, nb, D, 0.0f, CODA_ROWSTAT_MEAN, s, st);
+}
+
 }  // namespace
 
 int coda_gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K,
@@ -412,6 +392,13 @@ int coda_gemm_rope_bwd(const uint16_t* x, const uint16_t* w, const float* cos_t,
                    Schedule::kPerTile, as_stream(stream));
 }
 
+int coda_gemm_rope_bwd_ws(const uint16_t* x, const uint16_t* w, const float* cos_t, const float* sin_t, int M, int K,
+                          int n_q, int n_k, int n_v, int head_dim, int seq_len, int pos_offset, uint16_t* out,
+                          void* workspace, long long workspace_bytes, void* stream) {
+  return gemm_rope(x, w, cos_t, sin_t, M, K, n_q, n_k, n_v, head_dim, seq_len, pos_offset, out, 1, Schedule::kSplit,
+                   as_stream(stream), workspace, workspace_bytes);
+}
+
 int coda_gemm_swiglu(const uint16_t* x, const uint16_t* w, int M, int K, int F, uint16_t* out, void* stream) {
   return gemm_swiglu(x, w, M, K, F, out, false, nullptr, 0, as_stream(stream));
 }
@@ -436,30 +423,13 @@ int coda_split_workspace_bytes(int M, int N, int K, long long* bytes) {
 
 int coda_gemm_rmsnorm_bwd_stats(const uint16_t* dy, const uint16_t* w1, const uint16_t* h2, int M, int D, int N,
                                 uint16_t* dh2, float* partials, float* s, void* stream) {
-  CODA_TRY(check_rows(M));
-  CODA_TRY(check_depth_or_width(D));
-  CODA_TRY(check_depth_or_width(N));
-  if (M == 0) return CODA_OK;
-  CODA_NONNULL(dy);
-  CODA_NONNULL(w1);
-  CODA_NONNULL(h2);
-  CODA_NONNULL(dh2);
-  CODA_NONNULL(partials);
-  CODA_NONNULL(s);
-  CODA_ALIGN16(dy);
-  CODA_ALIGN16(w1);
-  CODA_ALIGN16(h2);
-  CODA_ALIGN16(dh2);
-  if (!aligned(partials, 4) || !aligned(s, 4)) return CODA_ERR_ALIGN;
-  const int nb = (D + kBN - 1) / kBN;
-  CODA_TRY(check_disjoint({bf16_span(dh2, M, D), f32_span(partials, M, nb), f32_span(s, M)},
-                          {bf16_span(dy, M, N), bf16_span(w1, D, N), bf16_span(h2, M, D)}));
-  const hipStream_t st = as_stream(stream);
-  // dy [M, N] times W1^T: depth = N, output width = D, W1 [D, N] is the NK layout.
-  const GemmProblem p{dy, w1, M, D, N};
-  const EpiDotRowPartials::Args ea{h2, dh2, partials, nb};
-  CODA_TRY((launch_gemm<false, EpiDotRowPartials>(p, ea, st)));
-  return coda_rowstat_reduce_impl(partials, M, nb, D, 0.0f, CODA_ROWSTAT_MEAN, s, st);
+  return gemm_bwd_stats(dy, w1, h2, M, D, N, dh2, partials, s, false, nullptr, 0, as_stream(stream));
+}
+
+int coda_gemm_rmsnorm_bwd_stats_ws(const uint16_t* dy, const uint16_t* w1, const uint16_t* h2, int M, int D, int N,
+                                   uint16_t* dh2, float* partials, float* s, void* workspace,
+                                   long long workspace_bytes, void* stream) {
+  return gemm_bwd_stats(dy, w1, h2, M, D, N, dh2, partials, s, true, workspace, workspace_bytes, as_stream(stream));
 }
 
 int coda_baseline_gemm(const uint16_t* a, const uint16_t* b, int M, int K, int N, int b_kn, uint16_t* c,
