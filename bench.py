@@ -294,6 +294,25 @@ def shard_share(coda, torch, b, reps):
     return out
 
 
+def token_shares(torch, reps, M, flops_per_row, one, split, need, G_list=(4, 8)):
+    """One GPU's share (M/G rows) of a row-independent GEMM under token sharding, through
+    the one-kernel entry point `one(m, ws)` and the split-depth one `split(m, ws)`, timed
+    interleaved; `need(m)` is the split workspace in bytes (allocated before timing)."""
+    ws = torch.empty((max([need(M // G) for G in G_list] + [16]),), dtype=torch.uint8, device="cuda")
+    fns = {}
+    for G in G_list:
+        m = M // G
+        fns[(G, "one_kernel")] = lambda m=m: one(m, ws)
+        fns[(G, "split_depth")] = lambda m=m: split(m, ws)
+    res = {}
+    for (G, how), ms in time_interleaved(fns, reps).items():
+        m = M // G
+        rec = res.setdefault(f"G{G}", dict(rows=m, workspace_bytes=need(m)))
+        rec[how] = dict(ms=round(ms, 4), tflops=round(flops_per_row * m / (ms * 1e-3) / 1e12, 1))
+    del ws
+    return res
+
+
 # ------------------------------------------------------------------ other fused paths
 def path_record(t, fl):
     rec = dict(fused_us=round(t["fused"] * 1e3, 1), tflops=round(fl / (t["fused"] * 1e-3) / 1e12, 1),
@@ -388,6 +407,12 @@ def other_paths(coda, torch, reps):
         "hipblaslt": lambda: torch.matmul(dy, w1t)}, reps)
     fl = 2.0 * M * N * D
     out["gemm_rmsnorm_bwd_stats_8192x4096x6144"] = path_record(t, fl)
+    out["gemm_rmsnorm_bwd_stats_8192x4096x6144"]["one_gpu_share_of_token_shards"] = token_shares(
+        torch, reps, M, 2.0 * N * D,
+        lambda m, ws: coda.coda_gemm_rmsnorm_bwd_stats(dy[:m], w1, h2[:m], dh2=dh2[:m], partials=part[:m], s=sv[:m]),
+        lambda m, ws: coda.coda_gemm_rmsnorm_bwd_stats_ws(dy[:m], w1, h2[:m], dh2=dh2[:m], partials=part[:m],
+                                                          s=sv[:m], workspace=ws),
+        lambda m: coda.coda_split_workspace_bytes(m, D, N))
     del dy, w1, h2, dh2, part, sv, w1t
     torch.cuda.empty_cache()
     # rest of the RMSNorm backward (dh1 with the residual-stream gradient, dgamma)
@@ -421,6 +446,15 @@ def other_paths(coda, torch, reps):
         "unfused": unfused,
         "hipblaslt": lambda: torch.matmul(dy, w1t)}, reps)
     out["rmsnorm_bwd_dx_dgamma_8192x4096x6144"] = path_record(t, fl)
+    # the grad GEMM with the dh1 / dgamma-partial epilogue alone, on one GPU's share
+    out["rmsnorm_bwd_dx_dgamma_8192x4096x6144"]["one_gpu_share_of_token_shards"] = token_shares(
+        torch, reps, M, 2.0 * N * D,
+        lambda m, ws: coda.coda_gemm_rmsnorm_bwd_dx(dy[:m], w1, h1[:m], g, r[:m], sv[:m], g_res=gres[:m],
+                                                    dh1=dh1[:m], dgamma_partials=pg[:(m + 255) // 256]),
+        lambda m, ws: coda.coda_gemm_rmsnorm_bwd_dx_ws(dy[:m], w1, h1[:m], g, r[:m], sv[:m], g_res=gres[:m],
+                                                       dh1=dh1[:m], dgamma_partials=pg[:(m + 255) // 256],
+                                                       workspace=ws),
+        lambda m: coda.coda_split_workspace_bytes(m, D, N))
     del dy, w1, h1, g, gres, hf, r, y, sv, dh1, pg, dg, dO, w1t
     torch.cuda.empty_cache()
     # SwiGLU backward on the down projection's grad GEMM
@@ -443,6 +477,11 @@ def other_paths(coda, torch, reps):
         "unfused": swiglu_bwd_unfused,
         "hipblaslt": lambda: torch.matmul(dy, wdt)}, reps)
     out["gemm_swiglu_bwd_8192x8192x4096"] = path_record(t, 2.0 * M * Dm * F)
+    out["gemm_swiglu_bwd_8192x8192x4096"]["one_gpu_share_of_token_shards"] = token_shares(
+        torch, reps, M, 2.0 * Dm * F,
+        lambda m, ws: coda.coda_gemm_swiglu_bwd(dy[:m], wd, h[:m], dh=dh[:m]),
+        lambda m, ws: coda.coda_gemm_swiglu_bwd_ws(dy[:m], wd, h[:m], dh=dh[:m], workspace=ws),
+        lambda m: coda.coda_split_workspace_bytes(m, F, Dm))
     del dy, wd, h, dh, dout, wdt
     torch.cuda.empty_cache()
     # RoPE backward (inverse rotation) in the epilogue of the GEMM producing dQKV
@@ -460,6 +499,11 @@ def other_paths(coda, torch, reps):
         "unfused": lambda: (coda.coda_baseline_gemm(x, w, c=hh), coda.coda_baseline_rope(hh, c, sneg, *args, out=q)),
         "hipblaslt": lambda: torch.matmul(x, w)}, reps)
     out["gemm_rope_bwd_4096x12288x4096"] = path_record(t, 2.0 * M * K * N)
+    out["gemm_rope_bwd_4096x12288x4096"]["one_gpu_share_of_token_shards"] = token_shares(
+        torch, reps, M, 2.0 * K * N,
+        lambda m, ws: coda.coda_gemm_rope_bwd(x[M - m:], w, c, sn, *args[:-1], M - m, out=q[:m]),
+        lambda m, ws: coda.coda_gemm_rope_bwd_ws(x[M - m:], w, c, sn, *args[:-1], M - m, out=q[:m], workspace=ws),
+        lambda m: coda.coda_split_workspace_bytes(m, N, K))
     del x, w, c, sn, sneg, q, hh
     torch.cuda.empty_cache()
     # GEMM + cross-entropy at the pages' two shapes (M x vocab x K); logits never stored
