@@ -3,8 +3,8 @@ points), through the C ABI: each output has fewer 256 x 256 tiles than the GPU h
 each tile's depth is cut into slices whose fp32 partial tiles go to the caller's
 workspace, and the same epilogue runs on their sum in slice order. Parity with the fp64
 oracle on every element (ragged rows, features and depth; two and eight slices),
-determinism from call to call, and bit-identity with the one-kernel entry point when the
-output is large enough that nothing splits."""
+determinism from call to call, bit-identity with the one-kernel entry point when the
+output is large enough that nothing splits, and graph replays equal to the eager call."""
 import ctypes
 
 import numpy as np
@@ -188,3 +188,50 @@ def test_split_depth_backward_workspace_errors(coda):
     assert L.coda_gemm_cross_entropy_ws(*args, p(f[0]), need, None) == 6       # workspace on an output
     assert L.coda_gemm_cross_entropy_ws(*args, p(ws), need, None) == 0
     sync()
+
+
+def test_split_depth_replays_from_a_graph(coda):
+    """The split-depth forward and SwiGLU backward captured in a HIP graph (two kernels
+    per split GEMM, no memory set inside): each replay, with eager fills of the outputs
+    and the workspace between replays, equals the eager call bit for bit."""
+    import torch
+    M, K, D, N1 = 300, 1024, 1032, 264
+    wl = W.gemm_rmsnorm_fwd_inputs(105, M, K, D, N1, 1e-5)
+    x, w0, z, g, w1 = (to_dev_bf16(wl[k]) for k in ("x", "w0", "z", "gamma", "w1"))
+    outs = dict(h1=torch.empty((M, D), dtype=torch.bfloat16, device="cuda"),
+                h2=torch.empty((M, D), dtype=torch.bfloat16, device="cuda"),
+                partials=torch.empty((M, coda.num_partials(D)), dtype=torch.float32, device="cuda"),
+                r=torch.empty((M,), dtype=torch.float32, device="cuda"),
+                y=torch.empty((M, N1), dtype=torch.bfloat16, device="cuda"))
+    ws = torch.empty((coda.coda_gemm_rmsnorm_fwd_workspace_bytes(M, K, D, N1),), dtype=torch.uint8, device="cuda")
+    wb = W.swiglu_bwd(seed=106, M=333, Dm=1040, F=136)
+    dy, wd, h = (to_dev_bf16(wb[k]) for k in ("dy", "w_down", "h"))
+    dh = torch.empty((333, 272), dtype=torch.bfloat16, device="cuda")
+    ws2 = torch.empty((coda.coda_split_workspace_bytes(333, 136, 1040),), dtype=torch.uint8, device="cuda")
+
+    def run():
+        coda.coda_gemm_rmsnorm_fwd_ws(x, w0, z, g, w1, wl["eps"], workspace=ws, **outs)
+        coda.coda_gemm_swiglu_bwd_ws(dy, wd, h, dh=dh, workspace=ws2)
+
+    def snapshot():
+        return [bf16_bits(t) if t.dtype == torch.bfloat16 else t.cpu().numpy() for t in (*outs.values(), dh)]
+
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        run()
+    sync()
+    want = snapshot()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    sync()
+    for rep in range(3):
+        for t in (*outs.values(), dh):
+            t.fill_(0)
+        ws.fill_(7)
+        ws2.fill_(7)
+        sync()
+        graph.replay()
+        sync()
+        for a, b in zip(snapshot(), want):
+            assert np.array_equal(a, b), f"replay {rep} differs from the eager call"
