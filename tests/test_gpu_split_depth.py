@@ -48,6 +48,7 @@ def check(got, ref):
     (300, 1024, 1032, 264),   # both GEMMs split; GEMM2's slices are 18 and 15 steps, its last step ragged
     (513, 2048, 768, 1024),   # GEMM1 in 4 slices of 16 steps, GEMM2 one kernel
     (40, 4096, 520, 520),     # one token tile, ragged features
+    (300, 4128, 264, 264),    # GEMM1 in 8 slices of 18 steps but the last of 3 (129 steps)
 ])
 def test_split_depth_small_full_compare(coda, shape):
     import torch

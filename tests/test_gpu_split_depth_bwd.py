@@ -79,7 +79,8 @@ def test_rmsnorm_bwd_dx_split_depth(coda, shape):
 
 
 # ------------------------------------------------------------ SwiGLU backward
-@pytest.mark.parametrize("shape", [(333, 1040, 136), (300, 4096, 264)])
+@pytest.mark.parametrize("shape", [(333, 1040, 136), (300, 4096, 264),
+                                   (300, 4128, 264)])   # 8 slices of 18 steps, the last of 3
 def test_swiglu_bwd_split_depth(coda, shape):
     M, Dm, F = shape
     assert coda.coda_split_workspace_bytes(M, F, Dm) > 0

@@ -99,15 +99,21 @@ void split_epilogue_kernel(GemmProblem p, typename Epi::Args ea, int S, const f3
     for (int j = 0; j < kMJ; ++j) acc[i][j] = in[(size_t)(i * kMJ + j) * kThreads];
   for (int s = 1; s < S; ++s) {
     in += (size_t)(kNI * kMJ * kThreads);
-    // one feature block (8 loads) at a time: the next partial tile's 128 values in flight
-    // at once would not fit beside the accumulators in the register budget
+    // two feature blocks (16 loads, 64 registers) in flight at a time: the whole next
+    // partial tile (128 values) would not fit beside the accumulators in the register
+    // budget, and fewer loads in flight leave the sum bound by their latency
+    constexpr int kB = 2;
 #pragma unroll
-    for (int i = 0; i < kNI; ++i) {
-      f32x4_t v[kMJ];
+    for (int i0 = 0; i0 < kNI; i0 += kB) {
+      f32x4_t v[kB][kMJ];
 #pragma unroll
-      for (int j = 0; j < kMJ; ++j) v[j] = in[(size_t)(i * kMJ + j) * kThreads];
+      for (int b = 0; b < kB; ++b)
 #pragma unroll
-      for (int j = 0; j < kMJ; ++j) acc[i][j] += v[j];
+        for (int j = 0; j < kMJ; ++j) v[b][j] = in[(size_t)((i0 + b) * kMJ + j) * kThreads];
+#pragma unroll
+      for (int b = 0; b < kB; ++b)
+#pragma unroll
+        for (int j = 0; j < kMJ; ++j) acc[i0 + b][j] += v[b][j];
       __builtin_amdgcn_sched_barrier(0);
     }
   }
