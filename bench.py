@@ -711,7 +711,30 @@ def cpu_baseline(target_s: float):
         t = sum(run(n) for _ in range(passes))
     flops = passes * (2.0 * n * K * D + 2.0 * n * D * N1)
     what = f"{n} of {M} rows" if n < M else f"all {M} rows, {passes} passes"
+    # wall time of one oracle pass over each stated workload in full (inputs generated
+    # beforehand, not timed)
+    per = {}
+    if n == M:
+        per["llama3_8b_gemm_rmsnorm_gemm_fwd"] = round(t / passes, 3)
+    else:
+        per[f"llama3_8b_gemm_rmsnorm_gemm_fwd ({n} of {M} rows)"] = round(t, 3)
+    del wl
+    for name, make, call in (
+            ("tiny_gemm_rmsnorm_gemm_256", W.tiny_fwd,
+             lambda w: O.gemm_rmsnorm_fwd(w["x"], w["w0"], w["z"], w["gamma"], w["w1"], w["eps"])),
+            ("gemm_rope_qkv_4096x12288x4096", W.rope_qkv,
+             lambda w: O.gemm_rope(w["x"], w["w"], w["n_q"], w["n_k"], w["n_v"], w["head_dim"], w["seq_len"],
+                                   w["pos_offset"], w["theta"])),
+            ("gemm_swiglu_8192x8192x8192", W.swiglu, lambda w: O.gemm_swiglu(w["x"], w["w"])),
+            ("gemm_rmsnorm_bwd_stats_8192x4096x6144", W.bwd_stats,
+             lambda w: O.gemm_rmsnorm_bwd_stats(w["dy"], w["w1"], w["h2"]))):
+        w = make()
+        t0 = time.perf_counter()
+        call(w)
+        per[name] = round(time.perf_counter() - t0, 3)
+        del w
     return {"value": round(flops / t / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "wall_s_per_workload": per,
             "sample": f"{what} of the same workload (all five fp64 outputs per row, incl. "
                       f"weight decode), {t:.1f} s wall",
             "implementation": f"numpy fp64, matrix products through {blas} with {cores} threads",
