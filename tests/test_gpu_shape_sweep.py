@@ -4,6 +4,8 @@ and its split-depth variant against the fp64 oracle on shapes drawn at random (r
 row, feature and depth tiles, a single depth step, a single row and one to several
 depth slices all occur; the persistent RoPE schedule equals the per-tile one bit for bit. The shapes are fixed by the seed; each case prints its shape
 before it runs."""
+import os
+
 import numpy as np
 import pytest
 
@@ -27,7 +29,8 @@ def _shapes(seed, n):
     return out
 
 
-SHAPES = _shapes(2026, 12)
+# CODA_SWEEP_SEED and CODA_SWEEP_N draw another or a longer sweep (the default is the committed one)
+SHAPES = _shapes(int(os.environ.get("CODA_SWEEP_SEED", "2026")), int(os.environ.get("CODA_SWEEP_N", "12")))
 SPLIT = [False, True]
 
 
