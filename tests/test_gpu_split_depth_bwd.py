@@ -236,3 +236,41 @@ def test_split_depth_replays_from_a_graph(coda):
         sync()
         for a, b in zip(snapshot(), want):
             assert np.array_equal(a, b), f"replay {rep} differs from the eager call"
+
+
+def test_calls_on_two_streams_overlap_safely(coda):
+    """The library keeps no state between calls (each call's buffers are its own): the
+    split forward and the split SwiGLU backward issued on two streams at once, from two
+    host threads, equal the same calls made one after the other."""
+    import threading
+    import torch
+    wl = W.gemm_rmsnorm_fwd_inputs(107, 300, 1024, 1032, 264, 1e-5)
+    fwd_in = [to_dev_bf16(wl[k]) for k in ("x", "w0", "z", "gamma", "w1")]
+    wb = W.swiglu_bwd(seed=108, M=333, Dm=1040, F=136)
+    bwd_in = (to_dev_bf16(wb["dy"]), to_dev_bf16(wb["w_down"]), to_dev_bf16(wb["h"]))
+    want_f = [bf16_bits(t) if t.dtype == torch.bfloat16 else t.cpu().numpy()
+              for t in coda.coda_gemm_rmsnorm_fwd_ws(*fwd_in, wl["eps"])]
+    want_b = bf16_bits(coda.coda_gemm_swiglu_bwd_ws(*bwd_in))
+    sync()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = {}
+
+    def run(i):
+        with torch.cuda.stream(streams[i]):
+            for rep in range(5):
+                if i == 0:
+                    got[(i, rep)] = coda.coda_gemm_rmsnorm_fwd_ws(*fwd_in, wl["eps"])
+                else:
+                    got[(i, rep)] = coda.coda_gemm_swiglu_bwd_ws(*bwd_in)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    sync()
+    for rep in range(5):
+        f = [bf16_bits(t) if t.dtype == torch.bfloat16 else t.cpu().numpy() for t in got[(0, rep)]]
+        for a, b in zip(f, want_f):
+            assert np.array_equal(a, b)
+        assert np.array_equal(bf16_bits(got[(1, rep)]), want_b)
