@@ -647,7 +647,7 @@ def schedule_probe(coda, torch, steps=20000):
     kind; 1024 cycles per step is the nominal MFMA time (64 MFMAs of 16 cycles per SIMD
     at the published peak)."""
     kinds = {0: "reads_kn_mfma_barrier", 1: "reads_kn_mfma_no_barrier", 2: "reads_nk_mfma_barrier",
-             3: "reads_kn_only", 4: "mfma_only"}
+             3: "reads_kn_only", 4: "mfma_only", 5: "w_reads_only_kn_mfma_barrier", 6: "x_reads_only_mfma_barrier"}
     res = {}
     for grid in (1, 256):
         for kind, name in list(kinds.items()) + [(4, "mfma_only_constant_image"), (0, "reads_kn_mfma_barrier_constant_image")]:

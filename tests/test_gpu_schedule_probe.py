@@ -21,7 +21,7 @@ def coda():
     return c
 
 
-@pytest.mark.parametrize("kind", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("kind", [0, 1, 2, 3, 4, 5, 6])
 def test_schedule_probe_closed_form(coda, kind):
     import torch
     for steps, grid in ((1, 1), (7, 3), (23, 2)):
@@ -38,7 +38,7 @@ def test_schedule_probe_closed_form(coda, kind):
         assert bool((cycles > 0).all())
 
 
-@pytest.mark.parametrize("kind", [0, 2, 3, 4])
+@pytest.mark.parametrize("kind", [0, 2, 3, 4, 5, 6])
 def test_schedule_probe_hashed_image(coda, kind):
     import torch
     log(f"schedule probe hashed kind={kind}")

@@ -434,7 +434,9 @@ namespace {
 //   2  NK-W reads (one 16-byte read per W block), the per-step barrier
 //   3  the reads of kind 0 alone, no MFMAs: every 32-bit word read is added (mod 2^32)
 //   4  the MFMAs of kind 0 alone, on operands read once before the loop
-// out[thread]: kinds 0-2 and 4 the sum of the thread's 128 accumulator values; kind 3 the
+//   5  kind 0 with only the W reads (the X operands read once before the loop)
+//   6  kind 0 with only the X reads (the W operands read once before the loop)
+// out[thread]: kinds 0-2 and 4-6 the sum of the thread's 128 accumulator values; kind 3 the
 // bits of its word sum. Each wave records the core-clock cycles of its `steps` steps
 // (s_memtime) in cycles[].
 template <int kKind>
@@ -445,6 +447,8 @@ void schedule_probe_kernel(float fill, uint32_t seed, int steps, float* __restri
   constexpr bool kBarrier = kKind != 1 && kKind != 4;
   constexpr bool kMfma = kKind != 3;
   constexpr bool kReads = kKind != 4;
+  constexpr bool kReadX = kReads && kKind != 5;
+  constexpr bool kReadW = kReads && kKind != 6;
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kSlotBytes];
   const uint32_t fill2 = f32_to_bf16(fill) * 0x10001u;
   for (int i = threadIdx.x; i < kStages * kSlotBytes / 4; i += kThreads) {
@@ -473,7 +477,7 @@ void schedule_probe_kernel(float fill, uint32_t seed, int steps, float* __restri
 #pragma unroll
   for (int i = 0; i < kNI; ++i) a[i] = ml.read_w(lds.slot[0], i);
 #pragma unroll
-  for (int j = 0; j < (kReads ? kH : kMJ); ++j) b[j] = ml.read_x(lds.slot[0], j);
+  for (int j = 0; j < (kReadX ? kH : kMJ); ++j) b[j] = ml.read_x(lds.slot[0], j);
   auto use = [&](int i, int j) {
     if constexpr (kMfma)
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
@@ -489,7 +493,7 @@ void schedule_probe_kernel(float fill, uint32_t seed, int steps, float* __restri
   auto step = [&](const int S) {
 #pragma unroll
     for (int j = kH; j < kMJ; ++j) {
-      if constexpr (kReads) b[j] = ml.read_x(lds.slot[S], j);
+      if constexpr (kReadX) b[j] = ml.read_x(lds.slot[S], j);
       fold(b[j]);
     }
     __builtin_amdgcn_s_setprio(1);
@@ -509,12 +513,12 @@ void schedule_probe_kernel(float fill, uint32_t seed, int steps, float* __restri
       const int i = r / kH, j = kH + r % kH;
       use(i, j);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      if (kReads && r < kH) {
+      if (kReadX && r < kH) {
         b[r] = ml.read_x(next, r);
         fold(b[r]);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
       }
-      if (kReads && r % kH == kH - 1) {
+      if (kReadW && r % kH == kH - 1) {
         a[i] = ml.read_w(next, i);
         fold(a[i]);
         __builtin_amdgcn_sched_group_barrier(0x100, kKN ? 2 : 1, 1);
@@ -550,7 +554,7 @@ extern "C" {
 
 int coda_baseline_schedule_probe(int kind, int steps, int grid, float fill, uint32_t seed, float* out,
                                  long long* cycles, void* stream) {
-  if (kind < 0 || kind > 4 || steps < 1 || grid < 1 || grid > 65535) return CODA_ERR_SHAPE;
+  if (kind < 0 || kind > 6 || steps < 1 || grid < 1 || grid > 65535) return CODA_ERR_SHAPE;
   CODA_NONNULL(out);
   CODA_NONNULL(cycles);
   if (!aligned(out, 4) || !aligned(cycles, 8)) return CODA_ERR_ALIGN;
@@ -561,6 +565,8 @@ int coda_baseline_schedule_probe(int kind, int steps, int grid, float fill, uint
     case 1: hipLaunchKernelGGL(schedule_probe_kernel<1>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
     case 2: hipLaunchKernelGGL(schedule_probe_kernel<2>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
     case 3: hipLaunchKernelGGL(schedule_probe_kernel<3>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
+    case 5: hipLaunchKernelGGL(schedule_probe_kernel<5>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
+    case 6: hipLaunchKernelGGL(schedule_probe_kernel<6>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
     default: hipLaunchKernelGGL(schedule_probe_kernel<4>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
   }
   return launch_status();
