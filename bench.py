@@ -647,18 +647,20 @@ def schedule_probe(coda, torch, steps=20000):
     kind; 1024 cycles per step is the nominal MFMA time (64 MFMAs of 16 cycles per SIMD
     at the published peak)."""
     kinds = {0: "reads_kn_mfma_barrier", 1: "reads_kn_mfma_no_barrier", 2: "reads_nk_mfma_barrier",
-             3: "reads_kn_only", 4: "mfma_only", 5: "w_reads_only_kn_mfma_barrier", 6: "x_reads_only_mfma_barrier"}
+             3: "reads_kn_only", 4: "mfma_only", 5: "w_reads_only_kn_mfma_barrier", 6: "x_reads_only_mfma_barrier",
+             7: "reads_kn_mfma_barrier_zero_fill_dma"}
     res = {}
     for grid in (1, 256):
         for kind, name in list(kinds.items()) + [(4, "mfma_only_constant_image"), (0, "reads_kn_mfma_barrier_constant_image")]:
-            seed = 0 if name.endswith("constant_image") else 11
+            seed = 0 if name.endswith("constant_image") or kind == 7 else 11
+            fill = 0.0 if kind == 7 else 0.125   # the zero-filling DMA runs on the zero image only
             out = torch.empty((grid * 512,), dtype=torch.float32, device="cuda")
             cyc = torch.empty((grid * 8,), dtype=torch.int64, device="cuda")
-            coda.coda_baseline_schedule_probe(kind, 50, grid, seed=seed, out=out, cycles=cyc)  # warm-up
+            coda.coda_baseline_schedule_probe(kind, 50, grid, fill=fill, seed=seed, out=out, cycles=cyc)  # warm-up
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            coda.coda_baseline_schedule_probe(kind, steps, grid, seed=seed, out=out, cycles=cyc)
+            coda.coda_baseline_schedule_probe(kind, steps, grid, fill=fill, seed=seed, out=out, cycles=cyc)
             e1.record()
             torch.cuda.synchronize()
             # a workgroup's time is its slowest wave's (without the per-step barrier the

@@ -422,12 +422,15 @@ int coda_baseline_mfma_loop(const uint16_t* operands, int n_frag, int iters, int
  * reads of kind 0 alone, no MFMAs; 4: the MFMAs of kind 0 alone, on operands read once
  * before the loop, no barrier; 5: kind 0 with only the W reads (X operands read once
  * before the loop); 6: kind 0 with only the X reads (W operands read once before the
- * loop). out [grid * 512] fp32: kinds 0-2 and 4-6 each thread's
+ * loop); 7: kind 0 plus the GEMM's DMA issue (4 loads of 1 KiB per wave and step into
+ * the ring) through a descriptor of no bytes, so every load zero-fills LDS without a
+ * memory access; only with fill == 0 and seed == 0 (else CODA_ERR_ARG), whose image the
+ * fills leave unchanged. out [grid * 512] fp32: kinds 0-2 and 4-7 each thread's
  * accumulator sum (seed 0: = 128 * 32 * fill^2 * steps up to rounding; every workgroup
  * computes the same values); kind 3 the bit pattern of
  * the 32-bit wrapping sum of every word the thread read (48 words per step). cycles
  * [grid * 8] int64: each wave's core-clock cycles over the steps (s_memtime). Rules:
- * 0 <= kind <= 6, steps >= 1, 1 <= grid <= 65535; out 4-, cycles 8-byte aligned. */
+ * 0 <= kind <= 7, steps >= 1, 1 <= grid <= 65535; out 4-, cycles 8-byte aligned. */
 int coda_baseline_schedule_probe(int kind, int steps, int grid, float fill, uint32_t seed,
                                  float* out, long long* cycles, void* stream);
 

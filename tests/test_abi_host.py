@@ -334,7 +334,9 @@ def test_library_matches_its_sources(raw, tmp_path):
 def test_schedule_probe_validation(L, raw):
     f = ctypes.c_float(0.125)
     assert L.coda_baseline_schedule_probe(-1, 5, 1, f, 0, P, P + 16, None) == SHAPE
-    assert L.coda_baseline_schedule_probe(7, 5, 1, f, 0, P, P + 16, None) == SHAPE
+    assert L.coda_baseline_schedule_probe(8, 5, 1, f, 0, P, P + 16, None) == SHAPE
+    assert L.coda_baseline_schedule_probe(7, 5, 1, f, 0, P, P + 16, None) == ARG      # fill != 0
+    assert L.coda_baseline_schedule_probe(7, 5, 1, ctypes.c_float(0.0), 3, P, P + 16, None) == ARG  # seed != 0
     assert L.coda_baseline_schedule_probe(0, 0, 1, f, 0, P, P + 16, None) == SHAPE
     assert L.coda_baseline_schedule_probe(0, 5, 0, f, 0, P, P + 16, None) == SHAPE
     assert L.coda_baseline_schedule_probe(0, 5, 65536, f, 0, P, P + 16, None) == SHAPE

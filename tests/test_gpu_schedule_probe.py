@@ -3,7 +3,8 @@ element equal to one bf16 value c, each of a thread's 128 accumulator values gai
 32 c^2 per step, and the reads-only kind adds 48 words (two bf16 c each) per step; both
 sums are exact in their arithmetic for c = 1/8, so they are checked bit for bit. Step counts
 that are not a multiple of the ring's 5 slots exercise the remainder steps. With a hashed
-image every workgroup must still compute the same values, and a different seed others."""
+image every workgroup must still compute the same values, and a different seed others.
+The kind with the zero-filling DMA runs on the all-zero image only: its sums are exactly 0."""
 import numpy as np
 import pytest
 
@@ -52,3 +53,13 @@ def test_schedule_probe_hashed_image(coda, kind):
     if kind != 3:
         assert np.all(np.isfinite(a))
     assert bool((ca > 0).all())
+
+
+def test_schedule_probe_zero_fill_dma(coda):
+    import torch
+    for steps, grid in ((1, 1), (7, 3), (23, 2), (400, 256)):
+        log(f"schedule probe kind=7 steps={steps} grid={grid}")
+        out, cycles = coda.coda_baseline_schedule_probe(7, steps, grid, fill=0.0, seed=0)
+        torch.cuda.synchronize()
+        assert np.all(out.cpu().numpy() == 0.0)
+        assert bool((cycles > 0).all())

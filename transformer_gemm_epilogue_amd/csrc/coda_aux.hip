@@ -436,6 +436,12 @@ namespace {
 //   4  the MFMAs of kind 0 alone, on operands read once before the loop
 //   5  kind 0 with only the W reads (the X operands read once before the loop)
 //   6  kind 0 with only the X reads (the W operands read once before the loop)
+//   7  kind 0 plus the GEMM's DMA issue into the ring (per wave and step, two W loads
+//      after the first-half MFMAs and two X loads behind the second-half ones, into the
+//      slots three and four steps ahead) through a descriptor of no bytes: every load
+//      zero-fills its 1 KiB of LDS without touching memory. Only for the all-zero image
+//      (fill 0, seed 0), which the zero fills leave unchanged, so no step waits for them;
+//      they are all waited for after the timed loop, before the workgroup ends.
 // out[thread]: kinds 0-2 and 4-6 the sum of the thread's 128 accumulator values; kind 3 the
 // bits of its word sum. Each wave records the core-clock cycles of its `steps` steps
 // (s_memtime) in cycles[].
@@ -449,6 +455,7 @@ void schedule_probe_kernel(float fill, uint32_t seed, int steps, float* __restri
   constexpr bool kReads = kKind != 4;
   constexpr bool kReadX = kReads && kKind != 5;
   constexpr bool kReadW = kReads && kKind != 6;
+  constexpr bool kDma = kKind == 7;
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kSlotBytes];
   const uint32_t fill2 = f32_to_bf16(fill) * 0x10001u;
   for (int i = threadIdx.x; i < kStages * kSlotBytes / 4; i += kThreads) {
@@ -488,6 +495,8 @@ void schedule_probe_kernel(float fill, uint32_t seed, int steps, float* __restri
       rsum += (w.x + w.y) + (w.z + w.w);
     }
   };
+  const i32x4_t none = rsrc_words(out, 0u);  // no bytes: every load zero-fills
+  const uint32_t wave_off = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * (kXJ * 1024u);
   __syncthreads();
   const long long t0 = __builtin_amdgcn_s_memtime();
   auto step = [&](const int S) {
@@ -503,6 +512,11 @@ void schedule_probe_kernel(float fill, uint32_t seed, int steps, float* __restri
       for (int j = 0; j < kH; ++j) use(i, j);
     __builtin_amdgcn_sched_group_barrier(0x100, kH, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, kMfmaH, 0);
+    if constexpr (kDma) {
+      const uint32_t w3 = lds_addr(lds.slot[(S + 3) % kStages]) + (uint32_t)kTileBytes + wave_off;
+      dma16(none, w3, 0u);
+      dma16(none, w3 + 1024u, 0u);
+    }
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kBarrier) __builtin_amdgcn_s_barrier();
@@ -513,6 +527,10 @@ void schedule_probe_kernel(float fill, uint32_t seed, int steps, float* __restri
       const int i = r / kH, j = kH + r % kH;
       use(i, j);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if (kDma && (r == kMfmaH - 8 || r == kMfmaH - 4)) {
+        const int q = r == kMfmaH - 8 ? 3 : 4;
+        dma16(none, lds_addr(lds.slot[(S + q) % kStages]) + wave_off, 0u);
+      }
       if (kReadX && r < kH) {
         b[r] = ml.read_x(next, r);
         fold(b[r]);
@@ -539,6 +557,10 @@ void schedule_probe_kernel(float fill, uint32_t seed, int steps, float* __restri
   if (s + 2 < steps) step(2);
   if (s + 3 < steps) step(3);
   const long long t1 = __builtin_amdgcn_s_memtime();
+  if constexpr (kDma) {
+    wait_vmcnt<0>();  // every zero fill has landed before the workgroup's LDS is given back
+    __syncthreads();
+  }
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < kNI; ++i)
@@ -554,7 +576,8 @@ extern "C" {
 
 int coda_baseline_schedule_probe(int kind, int steps, int grid, float fill, uint32_t seed, float* out,
                                  long long* cycles, void* stream) {
-  if (kind < 0 || kind > 6 || steps < 1 || grid < 1 || grid > 65535) return CODA_ERR_SHAPE;
+  if (kind < 0 || kind > 7 || steps < 1 || grid < 1 || grid > 65535) return CODA_ERR_SHAPE;
+  if (kind == 7 && (fill != 0.0f || seed != 0u)) return CODA_ERR_ARG;  // the zero image only
   CODA_NONNULL(out);
   CODA_NONNULL(cycles);
   if (!aligned(out, 4) || !aligned(cycles, 8)) return CODA_ERR_ALIGN;
@@ -567,6 +590,7 @@ int coda_baseline_schedule_probe(int kind, int steps, int grid, float fill, uint
     case 3: hipLaunchKernelGGL(schedule_probe_kernel<3>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
     case 5: hipLaunchKernelGGL(schedule_probe_kernel<5>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
     case 6: hipLaunchKernelGGL(schedule_probe_kernel<6>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
+    case 7: hipLaunchKernelGGL(schedule_probe_kernel<7>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
     default: hipLaunchKernelGGL(schedule_probe_kernel<4>, dim3(grid), dim3(kThreads), 0, st, fill, seed, steps, out, cycles); break;
   }
   return launch_status();
