@@ -112,10 +112,13 @@ int coda_gemm_rmsnorm_fwd(const uint16_t* x, const uint16_t* w0, const uint16_t*
  * token-sharded batch). The same steps (1)-(3), where a GEMM with too few tiles cuts
  * each tile's depth into S equal slices, runs one workgroup per slice (fp32 partial
  * tiles into `workspace`) and then one per tile that sums the S partials in slice order
- * and runs the tile's epilogue, (1) or (3) above, on the sum. A GEMM with enough tiles
- * runs as in coda_gemm_rmsnorm_fwd. Results are deterministic for a given shape and
- * device; their fp32 rounding differs from coda_gemm_rmsnorm_fwd's by the order of the
- * depth sum, within the same tolerance against exact arithmetic.
+ * and runs the tile's epilogue, (1) or (3) above, on the sum. A GEMM with at most half
+ * as many tiles as CUs splits every tile. A larger one whose last wave of tiles (one per
+ * CU) is at most half full runs its full waves as coda_gemm_rmsnorm_fwd does and splits
+ * only the last wave's tiles. Any other GEMM runs as in coda_gemm_rmsnorm_fwd. Results
+ * are deterministic for a given shape and device; a split tile's fp32 rounding differs
+ * from coda_gemm_rmsnorm_fwd's by the order of the depth sum, within the same tolerance
+ * against exact arithmetic.
  * workspace: caller-owned device memory of workspace_bytes bytes, 16-byte aligned, at
  * least coda_gemm_rmsnorm_fwd_workspace_bytes(M, K, D, N1) (else CODA_ERR_WORKSPACE;
  * may be NULL when that is 0); read and written by the call, overlapping no other
@@ -128,7 +131,8 @@ int coda_gemm_rmsnorm_fwd_ws(const uint16_t* x, const uint16_t* w0, const uint16
                              float* r, uint16_t* y, void* workspace, long long workspace_bytes,
                              void* stream);
 /* Bytes of workspace coda_gemm_rmsnorm_fwd_ws needs on the current device (0 when no
- * GEMM of the shape is split): 256 KiB per slice of every tile of the larger split GEMM.
+ * GEMM of the shape is split): 256 KiB per slice of every split tile of the GEMM that
+ * needs more.
  * Shape rules as coda_gemm_rmsnorm_fwd; CODA_ERR_HIP if the device cannot be queried. */
 int coda_gemm_rmsnorm_fwd_workspace_bytes(int M, int K, int D, int N1, long long* bytes);
 
@@ -233,9 +237,10 @@ int coda_gemm_swiglu_ws(const uint16_t* x, const uint16_t* w, int M, int K, int 
                         void* stream);
 
 /* Bytes of split-depth workspace one GEMM with output [M, N] (N the GEMM's full output
- * width) and depth K needs on the current device: 256 KiB per slice of every output
- * tile, 0 when it does not split. Shape rules as the GEMMs; CODA_ERR_HIP if the device
- * cannot be queried. */
+ * width) and depth K needs on the current device: 256 KiB per slice of every split
+ * tile (every tile of an output of at most half as many tiles as CUs, or the tiles of
+ * an at most half-full last wave of a larger one), 0 when it does not split. Shape
+ * rules as the GEMMs; CODA_ERR_HIP if the device cannot be queried. */
 int coda_split_workspace_bytes(int M, int N, int K, long long* bytes);
 
 /* RoPE backward ([notes] key design 2; [pith] Fig. 7; the rotation is orthogonal, so its

@@ -274,3 +274,54 @@ def test_calls_on_two_streams_overlap_safely(coda):
         for a, b in zip(f, want_f):
             assert np.array_equal(a, b)
         assert np.array_equal(bf16_bits(got[(1, rep)]), want_b)
+
+
+# ------------------------------------------------- the partial last wave of a larger output
+def test_remainder_split_forward(coda):
+    """GEMM2 with 384 tiles on 256 CUs: its full wave runs the one-kernel schedule and the
+    128 tiles of the partial wave are split in 2 slices (64 steps each); every element
+    against the oracle."""
+    import torch
+    M, K, D, N1 = 4096, 1024, 4096, 6144
+    need = coda.coda_gemm_rmsnorm_fwd_workspace_bytes(M, K, D, N1)
+    assert need == 128 * 2 * 256 * 1024
+    log(f"remainder split fwd M={M} K={K} D={D} N1={N1}")
+    wl = W.gemm_rmsnorm_fwd_inputs(109, M, K, D, N1, 1e-5)
+    h1, h2, part, r, y = coda.coda_gemm_rmsnorm_fwd_ws(*(to_dev_bf16(wl[k]) for k in ("x", "w0", "z", "gamma", "w1")),
+                                                       wl["eps"])
+    sync()
+    ref = O.gemm_rmsnorm_fwd(wl["x"], wl["w0"], wl["z"], wl["gamma"], wl["w1"], wl["eps"])
+    assert_close_tiles("h1", dec(h1), ref["h1"])
+    assert_close_tiles("r", r.cpu().numpy(), ref["r"], rel_fro=TIGHT)
+    assert_close_tiles("y", dec(y), ref["y"])
+
+
+def test_remainder_split_cross_entropy_and_nk(coda):
+    """320 output tiles: 256 in the one-kernel schedule, the last 64 in 2 slices; a KN
+    GEMM with the cross-entropy epilogue and an NK one with the SwiGLU backward map."""
+    import torch
+    M, K, V = 4096, 2048, 5120
+    assert coda.coda_split_workspace_bytes(M, V, K) == 64 * 2 * 256 * 1024
+    log(f"remainder split cross_entropy M={M} K={K} V={V}")
+    wl = W.cross_entropy(seed=110, M=M, K=K, V=V, ignore_every=13)
+    loss, lse, target, tile = (t.cpu().numpy() for t in coda.coda_gemm_cross_entropy_ws(
+        to_dev_bf16(wl["x"]), to_dev_bf16(wl["w"]), torch.from_numpy(wl["labels"]).cuda()))
+    ref = O.gemm_cross_entropy(wl["x"], wl["w"], wl["labels"])
+    assert_close_tiles("tile_lse", tile, ref["tile_lse"], rel_fro=TIGHT, tile_n=1)
+    assert_close_tiles("loss", loss, ref["loss"], rel_fro=TIGHT)
+    assert np.all(loss[~ref["valid"]] == 0) and np.all(target[~ref["valid"]] == 0)
+    M, Dm, F = 4096, 2048, 5120
+    assert coda.coda_split_workspace_bytes(M, F, Dm) == 64 * 2 * 256 * 1024
+    log(f"remainder split swiglu_bwd M={M} Dm={Dm} F={F}")
+    wb = W.swiglu_bwd(seed=111, M=M, Dm=Dm, F=F)
+    args = (to_dev_bf16(wb["dy"]), to_dev_bf16(wb["w_down"]), to_dev_bf16(wb["h"]))
+    dh = coda.coda_gemm_swiglu_bwd_ws(*args)
+    one = coda.coda_gemm_swiglu_bwd(*args)
+    sync()
+    ref = O.gemm_swiglu_bwd(wb["dy"], wb["w_down"], wb["h"])["dh"]
+    got = dec(dh)
+    assert_close_tiles("dh", got, ref, tile_n=512)
+    # the 256 tiles of the full wave are the one-kernel schedule's, bit for bit: at least
+    # 256 / 320 of the elements (the split tiles' may also agree where the rounding does)
+    same = bf16_bits(dh) == bf16_bits(one)
+    assert same.mean() >= 256 / 320

@@ -11,9 +11,10 @@
 
 namespace coda {
 
+// The one-kernel schedule over tiles [0, tiles) of the tile order (all of them by default).
 template <bool kWKN, class Epi>
-int launch_gemm(const GemmProblem& p, const typename Epi::Args& ea, hipStream_t stream) {
-  const int grid = gemm_grid(p.M, p.N);
+int launch_gemm(const GemmProblem& p, const typename Epi::Args& ea, hipStream_t stream, int tiles = -1) {
+  const int grid = tiles < 0 ? gemm_grid(p.M, p.N) : tiles;
   if constexpr (kWKN) {
     if (kn_one_descriptor_fits(p.K, p.N)) {
       hipLaunchKernelGGL((gemm_epilogue_kernel<true, Epi, true>), dim3(grid), dim3(kThreads), 0, stream, p, ea);
@@ -34,21 +35,25 @@ inline int device_cus(int* cus) {
 }
 
 // Split-depth schedule (coda_splitk.hpp) when the plan has more than one slice: the
-// slices' main loops, then the tiles' epilogues on the summed partials (two launches);
-// otherwise the one-kernel schedule. ws holds split_workspace_floats(M, N, sp) floats.
+// one-kernel schedule over the tiles before sp.tile0 (if any), then the split tiles'
+// slices, then their epilogues on the summed partials; otherwise the one-kernel schedule.
+// ws holds split_workspace_floats(M, N, sp) floats.
 template <bool kWKN, class Epi>
 int launch_gemm_split(const GemmProblem& p, const typename Epi::Args& ea, const SplitPlan& sp, float* ws,
                       hipStream_t stream) {
   if (sp.S <= 1) return launch_gemm<kWKN, Epi>(p, ea, stream);
-  const int T = gemm_grid(p.M, p.N);
-  const dim3 units((unsigned)(((T + 7) / 8) * 8 * sp.S));
+  if (sp.tile0 > 0) CODA_TRY((launch_gemm<kWKN, Epi>(p, ea, stream, sp.tile0)));
+  const int Tq = gemm_grid(p.M, p.N) - sp.tile0;
+  const dim3 units((unsigned)(((Tq + 7) / 8) * 8 * sp.S));
   f32x4_t* w4 = reinterpret_cast<f32x4_t*>(ws);
   if (kWKN && kn_one_descriptor_fits(p.K, p.N))
-    hipLaunchKernelGGL((gemm_split_kernel<kWKN, kWKN>), units, dim3(kThreads), 0, stream, p, sp.S, sp.steps, w4);
+    hipLaunchKernelGGL((gemm_split_kernel<kWKN, kWKN>), units, dim3(kThreads), 0, stream, p, sp.S, sp.steps, sp.tile0,
+                       w4);
   else
-    hipLaunchKernelGGL((gemm_split_kernel<kWKN, false>), units, dim3(kThreads), 0, stream, p, sp.S, sp.steps, w4);
+    hipLaunchKernelGGL((gemm_split_kernel<kWKN, false>), units, dim3(kThreads), 0, stream, p, sp.S, sp.steps,
+                       sp.tile0, w4);
   CODA_TRY(launch_status());
-  hipLaunchKernelGGL((split_epilogue_kernel<Epi>), dim3(T), dim3(kThreads), 0, stream, p, ea, sp.S,
+  hipLaunchKernelGGL((split_epilogue_kernel<Epi>), dim3(Tq), dim3(kThreads), 0, stream, p, ea, sp.S, sp.tile0,
                      (const f32x4_t*)w4);
   return launch_status();
 }
