@@ -201,8 +201,9 @@ int coda_gemm_rope(const uint16_t* x, const uint16_t* w, const float* cos_t,
                    const float* sin_t, int M, int K, int n_q, int n_k, int n_v, int head_dim,
                    int seq_len, int pos_offset, uint16_t* out, void* stream);
 
-/* coda_gemm_rope with the split-depth schedule of coda_gemm_rmsnorm_fwd_ws for outputs
- * with fewer 256 x 256 tiles than the current device has CUs: `workspace` holds at least
+/* coda_gemm_rope with the split-depth schedule of coda_gemm_rmsnorm_fwd_ws (outputs of
+ * at most half as many 256 x 256 tiles as the current device has CUs split every tile;
+ * a larger output's at most half-full last wave splits its tiles): `workspace` holds at least
  * coda_split_workspace_bytes(M, n_q + n_k + n_v, K) bytes (16-byte aligned; NULL when
  * that is 0; overlapping no other argument), else CODA_ERR_WORKSPACE. Same outputs up to
  * the fp32 order of the depth sum; a negative workspace_bytes is CODA_ERR_ARG. */
