@@ -17,20 +17,24 @@ pytestmark = pytest.mark.gpu
 TIGHT = 1e-4
 
 
-def _shapes(seed, n):
+def _shapes(seed, n, max_rows=1300, max_width=1400, max_depth=2104):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
-        M = int(rng.integers(1, 1301))
-        K = 8 * int(rng.integers(1, 264))     # 8 .. 2104: 1 .. 66 depth steps
-        N = 8 * int(rng.integers(1, 176))     # 8 .. 1400
+        M = int(rng.integers(1, max_rows + 1))
+        K = 8 * int(rng.integers(1, max_depth // 8 + 1))  # 8 .. 2104 (1 .. 66 depth steps) by default
+        N = 8 * int(rng.integers(1, max_width // 8 + 1))  # 8 .. 1400 by default
         out.append((M, K, N))
-    out[0] = (1, 8, 8)                        # one row, one depth step, one ragged tile
+    out[0] = (1, 8, 8)                                 # one row, one depth step, one ragged tile
     return out
 
 
-# CODA_SWEEP_SEED and CODA_SWEEP_N draw another or a longer sweep (the default is the committed one)
-SHAPES = _shapes(int(os.environ.get("CODA_SWEEP_SEED", "2026")), int(os.environ.get("CODA_SWEEP_N", "12")))
+# CODA_SWEEP_SEED, CODA_SWEEP_N and CODA_SWEEP_MAX_{ROWS,WIDTH,DEPTH} draw another, longer or
+# larger sweep (the default is the committed one)
+_env = os.environ.get
+SHAPES = _shapes(int(_env("CODA_SWEEP_SEED", "2026")), int(_env("CODA_SWEEP_N", "12")),
+                 int(_env("CODA_SWEEP_MAX_ROWS", "1300")), int(_env("CODA_SWEEP_MAX_WIDTH", "1400")),
+                 int(_env("CODA_SWEEP_MAX_DEPTH", "2104")))
 SPLIT = [False, True]
 
 
