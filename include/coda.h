@@ -69,7 +69,7 @@ const char* coda_status_string(int status);
 
 /* ABI version of this header (major * 100 + minor): 101 adds the split-depth forward
  * and the schedule probe to 100; 102 adds the split-depth backward and cross-entropy
- * entry points. */
+ * entry points; 103 adds coda_split_plan. */
 int coda_abi_version(void);
 
 /* SHA-256 (64 hex digits, static string) of the sources and compile flags this library
@@ -243,6 +243,14 @@ int coda_gemm_swiglu_ws(const uint16_t* x, const uint16_t* w, int M, int K, int 
  * an at most half-full last wave of a larger one), 0 when it does not split. Shape
  * rules as the GEMMs; CODA_ERR_HIP if the device cannot be queried. */
 int coda_split_workspace_bytes(int M, int N, int K, long long* bytes);
+/* The split-depth plan of one GEMM (output [M, N], depth K) on a device of `cus` compute
+ * units, computed on the host alone (no device is queried): *slices per split tile (1:
+ * the one-kernel schedule for every tile), *steps of 32 depth per slice (the last may be
+ * shorter), *first_split_tile (tiles before it in the tile order run the one-kernel
+ * schedule) and the workspace *bytes, as the _ws entry points plan it on such a device.
+ * CODA_ERR_NULL, CODA_ERR_SHAPE as the GEMMs, CODA_ERR_ARG if cus < 1. */
+int coda_split_plan(int M, int N, int K, int cus, int* slices, int* steps, int* first_split_tile,
+                    long long* bytes);
 
 /* RoPE backward ([notes] key design 2; [pith] Fig. 7; the rotation is orthogonal, so its
  * gradient is the rotation by the negated angle): same arguments, layouts and rules as

@@ -26,6 +26,7 @@ const any_fn coda_entry_points[] = {
     (any_fn)&coda_gemm_swiglu,
     (any_fn)&coda_gemm_swiglu_ws,
     (any_fn)&coda_split_workspace_bytes,
+    (any_fn)&coda_split_plan,
     (any_fn)&coda_gemm_rope_bwd,
     (any_fn)&coda_gemm_rope_bwd_ws,
     (any_fn)&coda_gemm_swiglu_bwd,

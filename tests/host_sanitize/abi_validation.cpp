@@ -235,6 +235,17 @@ int main() {
     });
   }
   {
+    int sl = 0, st = 0, t0 = 0;
+    long long bytes = 0;
+    sweep("coda_split_plan", {256, 256, 256, 256}, [&](const std::vector<int>& a) {
+      return coda_split_plan(a[0], a[1], a[2], a[3], &sl, &st, &t0, &bytes);
+    });
+    EXPECT(coda_split_plan(1 << 24, 1 << 22, 1 << 22, INT_MAX, &sl, &st, &t0, &bytes) == CODA_OK && sl == 1,
+           "largest grid, most CUs");
+    EXPECT(coda_split_plan(8, 8, 8, 256, nullptr, &st, &t0, &bytes) == CODA_ERR_NULL, "slices NULL");
+    EXPECT(coda_split_plan(8, 8, 8, 0, &sl, &st, &t0, &bytes) == CODA_ERR_ARG, "no CUs");
+  }
+  {
     long long bytes = 0;
     sweep("coda_gemm_rmsnorm_fwd_workspace_bytes", {256, 256, 256, 256}, [&](const std::vector<int>& a) {
       return coda_gemm_rmsnorm_fwd_workspace_bytes(a[0], a[1], a[2], a[3], &bytes);

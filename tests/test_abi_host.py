@@ -87,7 +87,7 @@ def test_binding_exports_every_public_wrapper():
 def test_status_strings(L):
     for st in range(7):
         assert L.coda_status_string(st)
-    assert L.coda_abi_version() == 102
+    assert L.coda_abi_version() == 103
 
 
 def test_num_partials(L):
@@ -403,3 +403,35 @@ def test_split_backward_and_cross_entropy_validation(L):
     assert L.coda_gemm_rope_bwd_ws(*rope, P, -1, None) == ARG
     assert L.coda_gemm_rope_bwd_ws(None, *rope[1:], P, 0, None) == NULL
     assert L.coda_gemm_rope_bwd_ws(P, P, P, P, 0, 8, 8, 8, 8, 8, 8, 0, P, None, 0, None) == OK
+
+
+def test_split_plan_rules(L):
+    """The split-depth plan, on the host for a given CU count (no device needed)."""
+    plan = coda.coda_split_plan
+    tile = 256 * 1024                      # bytes of one fp32 partial tile
+    # at most half as many tiles as CUs: every tile split, S <= CUs / T, <= 8, >= 16 steps
+    assert plan(1024, 4096, 14336, 256) == (4, 112, 0, 64 * 4 * tile)      # 64 tiles, 448 steps
+    assert plan(1024, 6144, 4096, 256) == (2, 64, 0, 96 * 2 * tile)        # 96 tiles: 2, not 3
+    assert plan(300, 264, 4128, 256) == (8, 18, 0, 4 * 8 * tile)           # 129 steps: 8 x 18, last 3
+    assert plan(300, 264, 992, 256) == (1, 31, 0, 0)                       # 31 steps: no 2 x 16
+    assert plan(300, 264, 1000, 256) == (2, 16, 0, 4 * 2 * tile)           # 32 steps, the last ragged
+    assert plan(40, 8, 8, 256) == (1, 1, 0, 0)                             # one step
+    # more than half: a partial last wave of r <= CUs / 2 tiles is split, slices >= 32 steps
+    assert plan(4096, 6144, 4096, 256) == (2, 64, 256, 128 * 2 * tile)     # 384 tiles: 256 + 128
+    assert plan(4096, 4608, 8192, 256) == (8, 32, 256, 32 * 8 * tile)      # 288 tiles: 256 + 32
+    assert plan(4096, 5120, 2048, 256) == (2, 32, 256, 64 * 2 * tile)
+    assert plan(4096, 5120, 1024, 256) == (1, 32, 0, 0)                    # 32 steps: no 2 x 32
+    assert plan(8192, 4096, 14336, 256) == (1, 448, 0, 0)                  # 512 tiles: full waves
+    assert plan(4096, 12288, 4096, 256) == (1, 128, 0, 0)                  # 768 tiles
+    assert plan(1024, 12288, 4096, 256) == (1, 128, 0, 0)                  # 192 tiles: 3/4 of the CUs
+    # the plan follows the CU count
+    assert plan(1024, 4096, 14336, 304) == (4, 112, 0, 64 * 4 * tile)
+    assert plan(1024, 4096, 14336, 128) == (2, 224, 0, 64 * 2 * tile)
+    assert plan(0, 4096, 14336, 256)[3] == 0
+    out = ctypes.c_int(0)
+    i64 = ctypes.c_int64(0)
+    assert L.coda_split_plan(8, 8, 8, 0, ctypes.byref(out), ctypes.byref(out), ctypes.byref(out),
+                             ctypes.byref(i64)) == ARG
+    assert L.coda_split_plan(8, 12, 8, 256, ctypes.byref(out), ctypes.byref(out), ctypes.byref(out),
+                             ctypes.byref(i64)) == SHAPE
+    assert L.coda_split_plan(8, 8, 8, 256, None, ctypes.byref(out), ctypes.byref(out), ctypes.byref(i64)) == NULL

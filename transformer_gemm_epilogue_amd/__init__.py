@@ -39,6 +39,7 @@ __all__ = [
     "coda_gemm_swiglu_ws",
     "coda_gemm_rope_ws",
     "coda_split_workspace_bytes",
+    "coda_split_plan",
     "coda_gemm_rmsnorm_bwd_stats",
     "coda_gemm_rmsnorm_bwd_stats_ws",
     "num_row_tiles",
@@ -93,6 +94,8 @@ SIGNATURES = {
     "coda_gemm_swiglu": [_P, _P, _I, _I, _I, _P, _P],
     "coda_gemm_swiglu_ws": [_P, _P, _I, _I, _I, _P, _P, _I64, _P],
     "coda_split_workspace_bytes": [_I, _I, _I, ctypes.POINTER(_I64)],
+    "coda_split_plan": [_I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I), ctypes.POINTER(_I),
+                        ctypes.POINTER(_I64)],
     "coda_gemm_rope_bwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P],
     "coda_gemm_rope_bwd_ws": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I64, _P],
     "coda_gemm_swiglu_bwd": [_P, _P, _P, _I, _I, _I, _P, _P],
@@ -360,6 +363,15 @@ def coda_split_workspace_bytes(M, N, K):
     out = ctypes.c_int64(0)
     _call("coda_split_workspace_bytes", int(M), int(N), int(K), ctypes.byref(out))
     return out.value
+
+
+def coda_split_plan(M, N, K, cus):
+    """The split-depth plan of one GEMM on a device of `cus` CUs (host only): (slices per
+    split tile, depth steps per slice, first split tile, workspace bytes)."""
+    s, st, t0, b = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int64(0)
+    _call("coda_split_plan", int(M), int(N), int(K), int(cus), ctypes.byref(s), ctypes.byref(st), ctypes.byref(t0),
+          ctypes.byref(b))
+    return s.value, st.value, t0.value, b.value
 
 
 def _workspace(need, like, workspace):

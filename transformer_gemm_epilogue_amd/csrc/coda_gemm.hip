@@ -116,7 +116,7 @@ const char* coda_status_string(int status) {
   }
 }
 
-int coda_abi_version(void) { return 102; }
+int coda_abi_version(void) { return 103; }
 
 #ifndef CODA_SOURCE_HASH
 #define CODA_SOURCE_HASH "unknown"
@@ -406,6 +406,24 @@ int coda_gemm_swiglu(const uint16_t* x, const uint16_t* w, int M, int K, int F, 
 int coda_gemm_swiglu_ws(const uint16_t* x, const uint16_t* w, int M, int K, int F, uint16_t* out, void* workspace,
                         long long workspace_bytes, void* stream) {
   return gemm_swiglu(x, w, M, K, F, out, true, workspace, workspace_bytes, as_stream(stream));
+}
+
+int coda_split_plan(int M, int N, int K, int cus, int* slices, int* steps, int* first_split_tile,
+                    long long* bytes) {
+  CODA_NONNULL(slices);
+  CODA_NONNULL(steps);
+  CODA_NONNULL(first_split_tile);
+  CODA_NONNULL(bytes);
+  CODA_TRY(check_rows(M));
+  CODA_TRY(check_depth_or_width(N));
+  CODA_TRY(check_depth_or_width(K));
+  if (cus < 1) return CODA_ERR_ARG;
+  const SplitPlan sp = M == 0 ? SplitPlan{1, (K + kBK - 1) / kBK, 0} : split_plan(M, N, K, cus);
+  *slices = sp.S;
+  *steps = sp.steps;
+  *first_split_tile = sp.tile0;
+  *bytes = M == 0 ? 0 : 4 * split_workspace_floats(M, N, sp);
+  return CODA_OK;
 }
 
 int coda_split_workspace_bytes(int M, int N, int K, long long* bytes) {

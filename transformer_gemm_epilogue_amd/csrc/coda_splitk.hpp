@@ -50,9 +50,9 @@ __host__ inline SplitPlan split_slices(int Tp, int KT, int cus, int min_steps, i
 // otherwise leave at least half of the CUs idle for a whole tile.
 __host__ inline SplitPlan split_plan(int M, int N, int K, int cus) {
   const int T = gemm_grid(M, N), KT = (K + kBK - 1) / kBK;
-  if (2 * T <= cus) return split_slices(T, KT, cus, kSplitMinSteps, 0);
+  if (T <= cus / 2) return split_slices(T, KT, cus, kSplitMinSteps, 0);  // 2T <= cus, without overflow
   const int r = T % cus;
-  if (r > 0 && 2 * r <= cus) return split_slices(r, KT, cus, kRemainderMinSteps, T - r);
+  if (r > 0 && r <= cus / 2) return split_slices(r, KT, cus, kRemainderMinSteps, T - r);
   return SplitPlan{1, KT, 0};
 }
 
