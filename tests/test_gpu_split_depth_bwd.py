@@ -327,3 +327,16 @@ def test_remainder_split_cross_entropy_and_nk(coda):
     # 256 / 320 of the elements (the split tiles' may also agree where the rounding does)
     same = bf16_bits(dh) == bf16_bits(one)
     assert not cus256 or same.mean() >= 256 / 320
+
+
+def test_split_plan_matches_the_device(coda):
+    """The host-side plan at the device's CU count asks for the workspace that the calls
+    on this device ask for, all-split, remainder-split and one-kernel shapes alike."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for M, N, K in [(300, 264, 4096), (517, 392, 1064), (4096, 5120, 2048), (4096, 4096, 1024),
+                    (8192, 4096, 14336), (1, 8, 8), (0, 256, 256), (40, 1 << 22, 8)]:
+        s, steps, tile0, nbytes = coda.coda_split_plan(M, N, K, cus)
+        log(f"split plan M={M} N={N} K={K} cus={cus}: S={s} steps={steps} tile0={tile0} bytes={nbytes}")
+        assert nbytes == coda.coda_split_workspace_bytes(M, N, K)
+        assert s >= 1 and (s == 1) == (nbytes == 0)
